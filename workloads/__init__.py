@@ -1,0 +1,190 @@
+"""Seeded synthetic inputs for the fused GEMM-epilogue workloads.
+
+This module is shared by the HIP path's tests/bench and by the CPU oracle.  It
+holds the workload *definitions* (shapes, host scalars, the epilogue chain as
+plain data) and the random-number recipe, and nothing of the method's
+arithmetic: no GEMM, no epilogue op, no encoder.  Every tensor is returned as
+raw bits (bf16 as ``uint16``) or ``float32`` so both sides read identical
+bytes.
+
+Recipe (one independent stream per tensor):
+  ``numpy.random.Generator(PCG64(SeedSequence([config_id, tensor_id])))``,
+  tensor ids A=0, B=1, B2=2, bias=3, R=4, g=5, base W (RMS fold)=6.
+  ``N(0, v)`` means variance ``v``; normals are drawn as float32 standard
+  normals, multiplied by ``sqrt(v)`` in float32 and cast to bf16 with
+  round-to-nearest-even (torch's float32 -> bfloat16 cast).
+
+The RMS workload folds a per-channel gain ``g[k]`` into the weight before
+anything runs: ``W'[k, n] = bf16(g[k] * W[k, n])`` with the product taken in
+float32 (a row scaling over the contraction axis, the only fold for which
+``rmsnorm(X) * g @ W == s * (X @ W')``).  That is input preparation: both sides
+receive ``W'``.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+
+# Tensor ids of the seeded streams.
+T_A, T_B, T_B2, T_BIAS, T_R, T_G, T_W = 0, 1, 2, 3, 4, 5, 6
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One fused GEMM-epilogue problem.
+
+    ``chain`` lists the epilogue ops in their canonical order as plain tuples:
+    ``("scale",)``, ``("row_rms", eps)``, ``("bias",)``, ``("act", name)``,
+    ``("pairwise", act_name)``, ``("residual",)``, ``("amax",)``,
+    ``("quant_fp8",)``.  Activation names: ``none``, ``relu``, ``gelu_tanh``,
+    ``silu``.
+    """
+
+    name: str
+    config_id: int
+    batch: int
+    M: int
+    N: int
+    K: int
+    chain: Tuple[tuple, ...]
+    alpha: float = 1.0
+    quant_scale: float = 1.0
+    a_var: str = "1/K"          # "1/K" or "1"
+    b_var: str = "1/K"
+    bias_var: float = 1.0
+    out: str = "bf16"           # "bf16" or "fp8_e4m3"
+    description: str = ""
+
+    @property
+    def pairwise(self) -> bool:
+        return any(op[0] == "pairwise" for op in self.chain)
+
+    def has(self, kind: str) -> bool:
+        return any(op[0] == kind for op in self.chain)
+
+    def op(self, kind: str) -> Optional[tuple]:
+        for op in self.chain:
+            if op[0] == kind:
+                return op
+        return None
+
+    def flops(self) -> float:
+        """2*M*N*K per GEMM, times batch, times two for the pairwise (gate, up) pair."""
+        return 2.0 * self.batch * self.M * self.N * self.K * (2 if self.pairwise else 1)
+
+    def algorithmic_bytes(self) -> int:
+        """Each operand read once, the output written once, plus the 4-byte AMAX."""
+        b = self.batch
+        nbytes = 2 * b * self.M * self.K + 2 * b * self.K * self.N
+        if self.pairwise:
+            nbytes += 2 * b * self.K * self.N
+        if self.has("bias"):
+            nbytes += 2 * self.N
+        if self.has("residual"):
+            nbytes += 2 * b * self.M * self.N
+        nbytes += (1 if self.out == "fp8_e4m3" else 2) * b * self.M * self.N
+        if self.has("amax"):
+            nbytes += 4
+        return nbytes
+
+    def with_shape(self, batch=None, M=None, N=None, K=None) -> "Workload":
+        return dataclasses.replace(
+            self,
+            batch=self.batch if batch is None else batch,
+            M=self.M if M is None else M,
+            N=self.N if N is None else N,
+            K=self.K if K is None else K,
+        )
+
+
+WORKLOADS: Dict[str, Workload] = {
+    "c1": Workload(
+        name="c1", config_id=1, batch=1, M=256, N=256, K=256,
+        chain=(("scale",), ("bias",), ("act", "gelu_tanh"), ("amax",)),
+        alpha=0.5, bias_var=1.0,
+        description="Y = GELU_tanh(0.5*A@B + bias), AMAX=max|Y|; M=N=K=256; A,B N(0,1/K); bias N(0,1)"),
+    "c2": Workload(
+        name="c2", config_id=2, batch=16, M=1024, N=1024, K=1024,
+        chain=(("scale",), ("bias",), ("act", "relu"), ("amax",)),
+        alpha=1.25, bias_var=0.1,
+        description="batch 16 x 1024^3, alpha=1.25, per-column bias N(0,0.1), ReLU, AMAX over all outputs"),
+    "c3": Workload(
+        name="c3", config_id=3, batch=1, M=8192, N=11008, K=4096,
+        chain=(("pairwise", "silu"),),
+        a_var="1", b_var="1/K",
+        description="SwiGLU up-projection: SiLU(X@Wg)*(X@Wu), X[8192x4096] N(0,1), W[4096x11008] N(0,1/4096)"),
+    "c4": Workload(
+        name="c4", config_id=4, batch=1, M=8192, N=4096, K=4096,
+        chain=(("row_rms", 1e-6), ("residual",)),
+        a_var="1", b_var="1/K",
+        description="RMS row scale of X[8192x4096] (gain U(0.5,1.5) folded into W), plus residual R N(0,1)"),
+    "c5": Workload(
+        name="c5", config_id=5, batch=1, M=8192, N=8192, K=8192,
+        chain=(("bias",), ("act", "gelu_tanh"), ("amax",), ("quant_fp8",)),
+        quant_scale=448.0 / 4.0, bias_var=0.1, out="fp8_e4m3",
+        description="M=N=K=8192, bias N(0,0.1), GELU_tanh, fp8 e4m3 output with scale 112 and fp32 AMAX"),
+}
+
+CONFIG_ORDER: List[str] = ["c1", "c2", "c3", "c4", "c5"]
+
+
+def _rng(config_id: int, tensor_id: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([config_id, tensor_id])))
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit pattern, round-to-nearest-even (torch's cast)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _normal_bf16(config_id: int, tensor_id: int, shape, var: float) -> np.ndarray:
+    z = _rng(config_id, tensor_id).standard_normal(size=shape, dtype=np.float32)
+    z *= np.float32(math.sqrt(var))
+    return f32_to_bf16_bits(z)
+
+
+def _var(spec: str, K: int) -> float:
+    return 1.0 / K if spec == "1/K" else float(spec)
+
+
+def generate(w: Workload, sensitive: bool = False, seed_offset: int = 0) -> Dict[str, np.ndarray]:
+    """Seeded inputs for workload ``w``.
+
+    Returns bf16 tensors as uint16 bit arrays (A: [batch, M, K]; B, B2:
+    [batch, K, N]; bias: [N]; R: [batch, M, N]) and float32 arrays for the
+    gain ``g`` (RMS workload only).  ``sensitive=True`` draws A from N(0, 1)
+    and sets the bias to zero, so the GEMM term dominates the output.
+    ``seed_offset`` shifts the config id of every stream (extra seeds for the
+    parity sweeps).
+    """
+    cid = w.config_id + 100 * seed_offset
+    b, M, N, K = w.batch, w.M, w.N, w.K
+    out: Dict[str, np.ndarray] = {}
+    a_var = 1.0 if sensitive else _var(w.a_var, K)
+    out["A"] = _normal_bf16(cid, T_A, (b, M, K), a_var)
+    if w.has("row_rms"):
+        # gain g[k] ~ U(0.5, 1.5) folded into the base weight along the contraction axis
+        g = _rng(cid, T_G).uniform(0.5, 1.5, size=K).astype(np.float32)
+        w_base = _normal_bf16(cid, T_W, (b, K, N), _var(w.b_var, K))
+        w_f32 = (w_base.astype(np.uint32) << 16).view(np.float32)
+        out["g"] = g
+        out["W_base"] = w_base
+        out["B"] = f32_to_bf16_bits(w_f32 * g[None, :, None])
+    else:
+        out["B"] = _normal_bf16(cid, T_B, (b, K, N), _var(w.b_var, K))
+    if w.pairwise:
+        out["B2"] = _normal_bf16(cid, T_B2, (b, K, N), _var(w.b_var, K))
+    if w.has("bias"):
+        if sensitive:
+            out["bias"] = np.zeros(N, dtype=np.uint16)
+        else:
+            out["bias"] = _normal_bf16(cid, T_BIAS, (N,), w.bias_var)
+    if w.has("residual"):
+        out["R"] = _normal_bf16(cid, T_R, (b, M, N), 1.0)
+    return out
