@@ -1,0 +1,293 @@
+// C-ABI of the fused GEMM-epilogue library: validate / create / run / destroy.
+//
+// The split follows the cuDNN Graph API tutorial's build-then-execute model
+// (opening paragraph): a descriptor is checked and turned into a plan once
+// (validate, support check, kernel choice), then executed many times against a
+// pack of device pointers with host scalars (batched-matmul paragraph: alpha is
+// a host scalar).  The op set is the CODA news item's epilogue primitive set
+// ("How CODA works").  The handle holds host memory only.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "../../include/gemm_epilogue.h"
+#include "ge_internal.h"
+
+struct ge_plan {
+  ge_desc_t desc;
+  ge::TileKind tile;
+  int act;            // ge::Act
+  bool fp8_out;
+  uint32_t flags;     // ge::F_*
+  float eps;
+  int64_t tiles_m, tiles_n;
+};
+
+namespace {
+
+constexpr int64_t kMaxExtent = 0x7FFFFFF0;   // buffer extents are 31-bit byte counts
+
+int op_rank(int kind) {
+  switch (kind) {
+    case GE_OP_SCALE: return 0;
+    case GE_OP_ROW_RMS:
+    case GE_OP_ROW_SCALE: return 1;
+    case GE_OP_BIAS_COL: return 2;
+    case GE_OP_ACT:
+    case GE_OP_PAIRWISE_ACT_MUL: return 3;
+    case GE_OP_RESIDUAL: return 4;
+    case GE_OP_AMAX: return 5;
+    case GE_OP_QUANT_FP8: return 6;
+    default: return -1;
+  }
+}
+
+bool has_op(const ge_desc_t* d, int kind) {
+  for (int i = 0; i < d->n_ops; ++i)
+    if (d->ops[i].kind == kind) return true;
+  return false;
+}
+
+const ge_op_t* find_op(const ge_desc_t* d, int kind) {
+  for (int i = 0; i < d->n_ops; ++i)
+    if (d->ops[i].kind == kind) return &d->ops[i];
+  return nullptr;
+}
+
+// Bytes from a matrix's base to one past its last element: (rows-1)*ld + cols.
+int64_t extent_elems(int64_t rows, int64_t cols, int64_t ld) {
+  if (rows <= 0 || cols <= 0) return 0;
+  return (rows - 1) * ld + cols;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+ge::TileKind pick_tile(const ge_desc_t* d, bool pair) {
+  const char* force = std::getenv("GE_FORCE_TILE");
+  if (force && *force) {
+    const int k = std::atoi(force);
+    if (k >= 0 && k < ge::TILE_KIND_COUNT && ge::tile_info((ge::TileKind)k).pair == pair)
+      return (ge::TileKind)k;
+  }
+  auto tiles = [&](int bm, int bn) { return ceil_div(d->M, bm) * ceil_div(d->N, bn) * d->batch; };
+  if (pair) return tiles(256, 128) >= 256 ? ge::TILE_256x128_PAIR : ge::TILE_128x128_PAIR;
+  if (tiles(256, 256) >= 256) return ge::TILE_256x256;
+  if (tiles(128, 128) >= 128) return ge::TILE_128x128;
+  return ge::TILE_64x64;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+ge_status_t gemm_epilogue_validate(const ge_desc_t* d) {
+  if (!d) return GE_ERR_INVALID_ARG;
+  if (d->batch < 0 || d->M < 0 || d->N < 0 || d->K < 0) return GE_ERR_INVALID_ARG;
+  if (d->n_ops < 0 || d->n_ops > GE_MAX_OPS) return GE_ERR_INVALID_ARG;
+  if (d->lda < 0 || d->ldb < 0 || d->ldy < 0 || d->ldr < 0) return GE_ERR_INVALID_ARG;
+  if (d->stride_a < 0 || d->stride_b < 0 || d->stride_y < 0 || d->stride_r < 0) return GE_ERR_INVALID_ARG;
+
+  // op chain: known kinds, canonical order, each at most once, exclusive pairs
+  int last_rank = -1;
+  for (int i = 0; i < d->n_ops; ++i) {
+    const ge_op_t& op = d->ops[i];
+    const int r = op_rank(op.kind);
+    if (r < 0) return GE_ERR_INVALID_ARG;
+    if (r <= last_rank) return GE_ERR_INVALID_ARG;
+    last_rank = r;
+    if (op.kind == GE_OP_ACT || op.kind == GE_OP_PAIRWISE_ACT_MUL) {
+      if (op.act < GE_ACT_NONE || op.act > GE_ACT_SILU) return GE_ERR_INVALID_ARG;
+    }
+    if (op.kind == GE_OP_ROW_RMS) {
+      if (!std::isfinite(op.eps) || op.eps < 0.0f) return GE_ERR_INVALID_ARG;
+    }
+  }
+  const bool pair = has_op(d, GE_OP_PAIRWISE_ACT_MUL);
+  const bool quant = has_op(d, GE_OP_QUANT_FP8);
+  if (has_op(d, GE_OP_ROW_RMS) && d->K < 1) return GE_ERR_INVALID_ARG;
+
+  // dtypes
+  if (d->a_type != GE_DT_BF16 || d->b_type != GE_DT_BF16) return GE_ERR_UNSUPPORTED;
+  if (d->y_type == GE_DT_FP8_E4M3) {
+    if (!quant) return GE_ERR_INVALID_ARG;
+  } else if (d->y_type == GE_DT_BF16) {
+    if (quant) return GE_ERR_INVALID_ARG;
+  } else if (d->y_type == GE_DT_FP32) {
+    return GE_ERR_UNSUPPORTED;
+  } else {
+    return GE_ERR_INVALID_ARG;
+  }
+  if (pair && has_op(d, GE_OP_BIAS_COL)) return GE_ERR_UNSUPPORTED;
+
+  // layout
+  const bool res = has_op(d, GE_OP_RESIDUAL);
+  if (d->M > 1 && d->lda < d->K) return GE_ERR_INVALID_ARG;
+  if (d->K > 1 && d->ldb < d->N) return GE_ERR_INVALID_ARG;
+  if (d->M > 1 && d->ldy < d->N) return GE_ERR_INVALID_ARG;
+  if (res && d->M > 1 && d->ldr < d->N) return GE_ERR_INVALID_ARG;
+  if (d->batch > 1 && d->stride_y == 0 && d->M > 0 && d->N > 0) return GE_ERR_INVALID_ARG;  // batches would race
+
+  // supported set: 16-byte vector access everywhere
+  if (d->N % 8 || d->K % 8) return GE_ERR_UNSUPPORTED;
+  if (d->lda % 8 || d->ldb % 8 || d->ldy % 8 || (res && d->ldr % 8)) return GE_ERR_UNSUPPORTED;
+  if (d->stride_a % 8 || d->stride_b % 8 || d->stride_y % 8 || (res && d->stride_r % 8))
+    return GE_ERR_UNSUPPORTED;
+  if (d->M > INT32_MAX || d->N > INT32_MAX || d->K > INT32_MAX || d->batch > INT32_MAX)
+    return GE_ERR_UNSUPPORTED;
+  const int64_t esize = d->y_type == GE_DT_FP8_E4M3 ? 1 : 2;
+  if (extent_elems(d->M, d->K, d->lda) * 2 > kMaxExtent) return GE_ERR_UNSUPPORTED;
+  if (extent_elems(d->K, d->N, d->ldb) * 2 > kMaxExtent) return GE_ERR_UNSUPPORTED;
+  if (extent_elems(d->M, d->N, d->ldy) * esize > kMaxExtent) return GE_ERR_UNSUPPORTED;
+  if (res && extent_elems(d->M, d->N, d->ldr) * 2 > kMaxExtent) return GE_ERR_UNSUPPORTED;
+  // grid: one workgroup per 64x64 tile at most
+  if (ceil_div(d->M, 64) * ceil_div(d->N, 64) * d->batch > INT32_MAX) return GE_ERR_UNSUPPORTED;
+  return GE_OK;
+}
+
+ge_status_t gemm_epilogue_create(const ge_desc_t* desc, ge_handle_t* out) {
+  if (!out) return GE_ERR_INVALID_ARG;
+  *out = nullptr;
+  const ge_status_t st = gemm_epilogue_validate(desc);
+  if (st != GE_OK) return st;
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return GE_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return GE_ERR_DEVICE;
+  }
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GE_ERR_DEVICE;
+
+  ge_plan* p = new (std::nothrow) ge_plan();
+  if (!p) return GE_ERR_HIP;
+  p->desc = *desc;
+  const bool pair = has_op(desc, GE_OP_PAIRWISE_ACT_MUL);
+  p->tile = pick_tile(desc, pair);
+  p->fp8_out = desc->y_type == GE_DT_FP8_E4M3;
+  p->act = ge::ACT_NONE;
+  if (const ge_op_t* a = find_op(desc, GE_OP_ACT)) p->act = a->act;
+  if (const ge_op_t* a = find_op(desc, GE_OP_PAIRWISE_ACT_MUL)) p->act = a->act;
+  p->flags = 0;
+  if (has_op(desc, GE_OP_SCALE)) p->flags |= ge::F_SCALE;
+  if (has_op(desc, GE_OP_ROW_SCALE)) p->flags |= ge::F_ROW_SCALE;
+  if (const ge_op_t* r = find_op(desc, GE_OP_ROW_RMS)) {
+    p->flags |= ge::F_ROW_RMS;
+    p->eps = r->eps;
+  } else {
+    p->eps = 0.0f;
+  }
+  if (has_op(desc, GE_OP_BIAS_COL)) p->flags |= ge::F_BIAS;
+  if (has_op(desc, GE_OP_RESIDUAL)) p->flags |= ge::F_RESIDUAL;
+  if (has_op(desc, GE_OP_AMAX)) p->flags |= ge::F_AMAX;
+  const ge::TileInfo ti = ge::tile_info(p->tile);
+  p->tiles_m = ceil_div(desc->M, ti.bm);
+  p->tiles_n = ceil_div(desc->N, ti.bn);
+  *out = p;
+  return GE_OK;
+}
+
+ge_status_t gemm_epilogue_workspace_size(ge_handle_t h, size_t* bytes) {
+  if (!h || !bytes) return GE_ERR_INVALID_ARG;
+  *bytes = (h->flags & ge::F_AMAX) ? ge::kAmaxWorkspaceBytes : 0;
+  return GE_OK;
+}
+
+ge_status_t gemm_epilogue_run(ge_handle_t h, const ge_args_t* a, void* stream) {
+  if (!h || !a) return GE_ERR_INVALID_ARG;
+  const ge_desc_t& d = h->desc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool empty = d.batch == 0 || d.M == 0 || d.N == 0;
+  const uint32_t f = h->flags;
+
+  if (f & ge::F_AMAX) {
+    if (!a->amax || !aligned(a->amax, 4)) return GE_ERR_INVALID_ARG;
+    if (!empty && (!a->workspace || !aligned(a->workspace, 16) ||
+                   a->workspace_bytes < ge::kAmaxWorkspaceBytes))
+      return GE_ERR_INVALID_ARG;
+  }
+  if (!empty) {
+    if (!a->Y || !aligned(a->Y, 16)) return GE_ERR_INVALID_ARG;
+    if (d.K > 0) {
+      if (!a->A || !a->B || !aligned(a->A, 16) || !aligned(a->B, 16)) return GE_ERR_INVALID_ARG;
+      if (h->tile == ge::TILE_256x128_PAIR || h->tile == ge::TILE_128x128_PAIR) {
+        if (!a->B2 || !aligned(a->B2, 16)) return GE_ERR_INVALID_ARG;
+      }
+    }
+    if ((f & ge::F_BIAS) && (!a->bias || !aligned(a->bias, 16))) return GE_ERR_INVALID_ARG;
+    if ((f & ge::F_ROW_SCALE) && (!a->row_scale || !aligned(a->row_scale, 4))) return GE_ERR_INVALID_ARG;
+    if ((f & ge::F_RESIDUAL) && (!a->residual || !aligned(a->residual, 16))) return GE_ERR_INVALID_ARG;
+  }
+
+  if (empty) {
+    // nothing to reduce: AMAX of no outputs is 0
+    if ((f & ge::F_AMAX) && ge::launch_amax_zero(reinterpret_cast<uint32_t*>(a->amax), s) != hipSuccess)
+      return GE_ERR_HIP;
+    return GE_OK;
+  }
+
+  ge::Params p;
+  p.A = static_cast<const uint16_t*>(a->A);
+  p.B = static_cast<const uint16_t*>(a->B);
+  p.B2 = static_cast<const uint16_t*>(a->B2);
+  p.bias = static_cast<const uint16_t*>(a->bias);
+  p.row_scale = a->row_scale;
+  p.R = static_cast<const uint16_t*>(a->residual);
+  p.Y = a->Y;
+  p.amax = reinterpret_cast<uint32_t*>(a->amax);
+  p.ws = static_cast<uint32_t*>(a->workspace);
+  p.lda = d.lda;
+  p.ldb = d.ldb;
+  p.ldy = d.ldy;
+  p.ldr = d.ldr;
+  p.sa = d.stride_a;
+  p.sb = d.stride_b;
+  p.sy = d.stride_y;
+  p.sr = d.stride_r;
+  p.M = (int32_t)d.M;
+  p.N = (int32_t)d.N;
+  p.K = (int32_t)d.K;
+  p.batch = (int32_t)d.batch;
+  p.tiles_m = (int32_t)h->tiles_m;
+  p.tiles_n = (int32_t)h->tiles_n;
+  p.alpha = a->alpha;
+  p.qscale = a->quant_scale;
+  p.eps = h->eps;
+  p.flags = f;
+  if (ge::launch_fused(h->tile, h->act, h->fp8_out, p, s) != hipSuccess) return GE_ERR_HIP;
+  return GE_OK;
+}
+
+void gemm_epilogue_destroy(ge_handle_t h) { delete h; }
+
+const char* gemm_epilogue_status_string(ge_status_t s) {
+  switch (s) {
+    case GE_OK: return "GE_OK";
+    case GE_ERR_INVALID_ARG: return "GE_ERR_INVALID_ARG: malformed descriptor or argument";
+    case GE_ERR_UNSUPPORTED: return "GE_ERR_UNSUPPORTED: outside the supported set";
+    case GE_ERR_DEVICE: return "GE_ERR_DEVICE: no gfx950 device is current";
+    case GE_ERR_HIP: return "GE_ERR_HIP: a HIP call or kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+ge_status_t gemm_epilogue_describe(ge_handle_t h, char* buf, size_t len) {
+  if (!h || !buf || len == 0) return GE_ERR_INVALID_ARG;
+  const ge::TileInfo ti = ge::tile_info(h->tile);
+  std::snprintf(buf, len, "tile=%dx%dx64 pair=%d threads=%d lds=%d grid=%lld act=%d fp8=%d flags=0x%x",
+                ti.bm, ti.bn, ti.pair ? 1 : 0, ti.threads, ti.lds_bytes,
+                (long long)(h->tiles_m * h->tiles_n * h->desc.batch), h->act, h->fp8_out ? 1 : 0,
+                (unsigned)h->flags);
+  return GE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+"""Marshalling between seeded workloads and the C-ABI (no arithmetic here).
+
+Turns a workload's host bit arrays into device tensors, builds the descriptor
+for its epilogue chain, and enqueues ``gemm_epilogue_run`` on the current
+torch stream.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+from . import (GE_DT_BF16, GE_DT_FP8_E4M3, Plan, make_args, make_desc, make_ops)
+
+
+def to_device_bf16(bits: np.ndarray, device) -> torch.Tensor:
+    """uint16 bf16 bit array -> torch.bfloat16 tensor on ``device``."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+@dataclasses.dataclass
+class DeviceProblem:
+    workload: object
+    plan: Plan
+    tensors: Dict[str, torch.Tensor]
+    Y: torch.Tensor
+    amax: Optional[torch.Tensor]
+    args: object
+
+    def run(self, stream: Optional[int] = None) -> None:
+        self.plan.run(self.args, stream)
+
+    def y_host_bits(self) -> np.ndarray:
+        y = self.Y.cpu()
+        if self.workload.out == "fp8_e4m3":
+            return y.view(torch.uint8).numpy()
+        return y.view(torch.int16).numpy().view(np.uint16)
+
+    def amax_host(self) -> Optional[float]:
+        return None if self.amax is None else float(self.amax.item())
+
+
+def prepare(w, inputs: Dict[str, np.ndarray], device="cuda", y_fill: Optional[int] = None) -> DeviceProblem:
+    """Uploads inputs, allocates Y (and AMAX), creates the plan for workload ``w``."""
+    t = {k: to_device_bf16(v, device) for k, v in inputs.items()
+         if k in ("A", "B", "B2", "bias", "R")}
+    if "row_scale" in inputs:
+        t["row_scale"] = torch.from_numpy(np.ascontiguousarray(inputs["row_scale"], dtype=np.float32)).to(device)
+    fp8 = w.out == "fp8_e4m3"
+    shape = (w.batch, w.M, w.N)
+    if fp8:
+        Y = torch.empty(shape, dtype=torch.uint8, device=device)
+    else:
+        Y = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    if y_fill is not None:
+        Y.view(torch.uint8).fill_(y_fill)
+    amax = torch.full((1,), -1.0, dtype=torch.float32, device=device) if w.has("amax") else None
+    desc = make_desc(w.batch, w.M, w.N, w.K, make_ops(w.chain),
+                     y_type=GE_DT_FP8_E4M3 if fp8 else GE_DT_BF16)
+    plan = Plan(desc)
+    args = make_args(A=t.get("A"), B=t.get("B"), B2=t.get("B2"), bias=t.get("bias"), residual=t.get("R"),
+                     row_scale=t.get("row_scale"), Y=Y, amax=amax, alpha=w.alpha, quant_scale=w.quant_scale)
+    return DeviceProblem(w, plan, t, Y, amax, args)

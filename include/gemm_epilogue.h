@@ -1,0 +1,177 @@
+/*
+ * gemm_epilogue.h -- fused GEMM + epilogue for AMD Instinct MI355X (gfx950).
+ *
+ * One operation:  Y = epilogue(A @ B [, A @ B2])  with bf16 operands, fp32
+ * accumulation, and an epilogue that runs on the fp32 output tile while it is
+ * still in registers, followed by the only store of Y to HBM.
+ *
+ * Where the operation is defined (pages as titled):
+ *   - The tiled GEMM with the output tile kept in register fragments and the
+ *     bias + GELU epilogue applied before the final write: "Optimising GPU
+ *     kernels with TileLang: from GEMM to FlashAttention", tiled-matmul and
+ *     fused-epilogue paragraphs; "Lean4-TileLang Tensor Program
+ *     Superoptimizer" write-up, section 8 (Matmul): W is laid out [d, N].
+ *   - The epilogue primitive set (scaling, reductions, pairwise transforms,
+ *     accumulation) running while the GEMM output tile is on chip: "CODA:
+ *     GEMM-epilogue for Transformer blocks", section "How CODA works".
+ *   - Host-scalar alpha, bias, activation and an AMAX reduction on the result
+ *     in the same kernel, feeding the next fp8 quantisation: "NVIDIA cuDNN
+ *     Graph API" tutorial, batched-matmul paragraph; build-then-execute over
+ *     a pack of device pointers: same tutorial, opening paragraph.
+ *   - The pairwise SwiGLU epilogue out = silu(X@W_gate) * (X@W_up):
+ *     superoptimizer write-up, section 7 (SwiGLU).
+ *   - The per-row RMS scale 1/sqrt(mean(x^2) + eps) applied after the GEMM via
+ *     (X*S)@W == (X@W)*S: superoptimizer write-up, section 9 (RMSNorm).
+ *
+ * Layout (all row-major, leading dimensions and batch strides in ELEMENTS):
+ *   A  [batch][M][K] bf16, element (b,m,k) at A + b*stride_a + m*lda + k
+ *   B  [batch][K][N] bf16, element (b,k,n) at B + b*stride_b + k*ldb + n
+ *   B2 same layout, leading dimension and batch stride as B (pairwise only)
+ *   Y  [batch][M][N] bf16 or fp8-e4m3 (OCP "e4m3fn"), at Y + b*stride_y + m*ldy + n
+ *   R  [batch][M][N] bf16 residual, at R + b*stride_r + m*ldr + n
+ *   bias [N] bf16, shared by every row and batch
+ *   row_scale [batch][M] fp32, at row_scale + b*M + m
+ *   amax: one fp32 in device memory
+ *   A batch stride of 0 broadcasts that operand over the batch.
+ *
+ * Epilogue chain (descriptor order must be this canonical order; each op at
+ * most once):
+ *   SCALE            t = alpha * acc                      (alpha: host scalar)
+ *   ROW_RMS(eps)     t = t / sqrt(mean_k A[b,m,k]^2 + eps) (statistic gathered in the mainloop)
+ *   ROW_SCALE        t = t * row_scale[b,m]               (exclusive with ROW_RMS)
+ *   BIAS_COL         t = t + bias[n]                      (not with PAIRWISE_ACT_MUL)
+ *   ACT(act)         y = act(t)
+ *   PAIRWISE_ACT_MUL(act)  y = act(t_gate) * t_up, gate from B, up from B2; the
+ *                    linear ops above apply to both accumulators (exclusive with ACT)
+ *   RESIDUAL         y = y + R[b,m,n]
+ *   AMAX             *amax = max |y| over all outputs, before any rounding (needs the workspace)
+ *   QUANT_FP8        Y = e4m3(clamp(y * quant_scale, -448, 448)), round to
+ *                    nearest even; requires y_type == GE_DT_FP8_E4M3 and must be last
+ *   Without QUANT_FP8, Y = bf16(y), round to nearest even (y_type == GE_DT_BF16).
+ *   Activations: RELU max(t,0); GELU_TANH 0.5 t (1 + tanh(sqrt(2/pi)(t + 0.044715 t^3)));
+ *   SILU t / (1 + e^-t).
+ *
+ * Supported shapes: batch >= 0, M >= 0, N >= 0, K >= 0 (K >= 1 with ROW_RMS);
+ * N, K, lda, ldb, ldy (and ldr) multiples of 8; lda >= K, ldb >= N, ldy >= N,
+ * ldr >= N; every device pointer 16-byte aligned.  Ragged M, N and K tails
+ * (not multiples of the tile) are handled inside the kernels.
+ *
+ * Ownership: the caller owns every device buffer and the stream.  The
+ * library borrows the pointers until the work enqueued by gemm_epilogue_run
+ * has completed.  A handle owns host memory only; the library never
+ * allocates or frees device memory and never synchronises the stream.
+ *
+ * Errors: every call returns a status; nothing aborts and there is no global
+ * error state.  Calls on one handle are safe from several threads because
+ * run() reads the handle only.
+ */
+#ifndef GEMM_EPILOGUE_H
+#define GEMM_EPILOGUE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GE_MAX_OPS 8
+
+typedef enum {
+  GE_OK = 0,
+  GE_ERR_INVALID_ARG = 1,   /* null pointer, negative size, bad stride, bad op order */
+  GE_ERR_UNSUPPORTED = 2,   /* well-formed but outside the supported set */
+  GE_ERR_DEVICE = 3,        /* no HIP device, or the current device is not gfx950 */
+  GE_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} ge_status_t;
+
+typedef enum { GE_DT_BF16 = 0, GE_DT_FP8_E4M3 = 1, GE_DT_FP32 = 2 } ge_dtype_t;
+
+typedef enum { GE_ACT_NONE = 0, GE_ACT_RELU = 1, GE_ACT_GELU_TANH = 2, GE_ACT_SILU = 3 } ge_act_t;
+
+typedef enum {
+  GE_OP_SCALE = 0,
+  GE_OP_ROW_RMS = 1,
+  GE_OP_ROW_SCALE = 2,
+  GE_OP_BIAS_COL = 3,
+  GE_OP_ACT = 4,
+  GE_OP_PAIRWISE_ACT_MUL = 5,
+  GE_OP_RESIDUAL = 6,
+  GE_OP_AMAX = 7,
+  GE_OP_QUANT_FP8 = 8
+} ge_op_kind_t;
+
+typedef struct {
+  int32_t kind;     /* ge_op_kind_t */
+  int32_t act;      /* ge_act_t, for ACT and PAIRWISE_ACT_MUL; else 0 */
+  float eps;        /* for ROW_RMS; else 0 */
+} ge_op_t;
+
+typedef struct {
+  int64_t batch, M, N, K;
+  int64_t lda, ldb, ldy, ldr;                   /* leading dimensions, elements */
+  int64_t stride_a, stride_b, stride_y, stride_r; /* batch strides, elements (0 = broadcast) */
+  int32_t a_type, b_type, y_type;               /* ge_dtype_t: bf16, bf16, bf16 | fp8_e4m3 */
+  int32_t n_ops;
+  ge_op_t ops[GE_MAX_OPS];
+} ge_desc_t;
+
+/* The per-execution "variant pack": borrowed device pointers plus host scalars.
+ * Pointers an op does not use may be NULL. */
+typedef struct {
+  const void* A;
+  const void* B;
+  const void* B2;          /* PAIRWISE_ACT_MUL: the "up" weight */
+  const void* bias;        /* BIAS_COL */
+  const float* row_scale;  /* ROW_SCALE */
+  const void* residual;    /* RESIDUAL */
+  void* Y;
+  float* amax;             /* AMAX: overwritten with max|y| */
+  void* workspace;         /* AMAX only: device scratch of gemm_epilogue_workspace_size bytes,
+                              16-byte aligned, ZERO-FILLED before its first use; each run leaves
+                              it zeroed again when it completes.  Runs that share a workspace
+                              must not overlap (order them on one stream). */
+  size_t workspace_bytes;
+  float alpha;             /* SCALE */
+  float quant_scale;       /* QUANT_FP8 */
+} ge_args_t;
+
+typedef struct ge_plan* ge_handle_t;
+
+/* Checks a descriptor without touching any device.  Returns GE_OK,
+ * GE_ERR_INVALID_ARG (malformed) or GE_ERR_UNSUPPORTED (outside the supported set). */
+ge_status_t gemm_epilogue_validate(const ge_desc_t* desc);
+
+/* Validates, checks that the current HIP device is gfx950, and picks a kernel
+ * instance (tile shape) for the descriptor.  On success *out owns a host-side
+ * plan; on failure *out is set to NULL.  Launches nothing. */
+ge_status_t gemm_epilogue_create(const ge_desc_t* desc, ge_handle_t* out);
+
+/* Device scratch the plan needs from the caller, in bytes: 256 when the chain
+ * has AMAX (a running maximum and a finished-workgroup counter), else 0. */
+ge_status_t gemm_epilogue_workspace_size(ge_handle_t handle, size_t* bytes);
+
+/* Enqueues the fused GEMM + epilogue on `stream` (a hipStream_t; NULL = the
+ * null stream) as ONE kernel launch and returns without waiting.  With AMAX
+ * in the chain, *amax is overwritten with max|y| when the kernel completes
+ * (the last workgroup to finish publishes it).  Returns GE_ERR_INVALID_ARG for
+ * a pointer an op needs that is NULL or misaligned (or a too-small AMAX
+ * workspace), GE_ERR_HIP if the launch fails.  An empty problem (batch, M or
+ * N zero) launches only a one-thread kernel that writes *amax = 0. */
+ge_status_t gemm_epilogue_run(ge_handle_t handle, const ge_args_t* args, void* stream);
+
+/* Frees the plan.  NULL is a no-op. */
+void gemm_epilogue_destroy(ge_handle_t handle);
+
+/* Static description of a status code. */
+const char* gemm_epilogue_status_string(ge_status_t status);
+
+/* Writes a one-line description of the plan's kernel instance (tile shape,
+ * waves, grid) into buf (NUL-terminated, truncated to len). */
+ge_status_t gemm_epilogue_describe(ge_handle_t handle, char* buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_EPILOGUE_H */

@@ -1,0 +1,70 @@
+"""Tolerances of the parity tests (HIP path vs the float64 oracle).
+
+* bf16 outputs: floored relative error
+      err_i = |y_i - r_i| / max(|r_i|, 1e-3 * max_j |r_j|)  <=  1e-2,
+  with r the unrounded float64 oracle value.  The floor keeps values that
+  cancel to near zero from dominating a pure relative error; bf16 rounding
+  alone contributes up to 2**-8 = 3.9e-3.
+* fp8 outputs: each code within one step of the oracle's code along the
+  monotone order of E4M3 values (+0 and -0 count as the same point).
+* AMAX: relative error <= 2e-3 against the oracle's max |y| taken before
+  rounding.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+BF16_TOL = 1e-2
+AMAX_TOL = 2e-3
+FLOOR = 1e-3
+
+
+def bf16_errors(y_bits: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    y = oracle.decode_bf16(y_bits)
+    r = np.asarray(ref, dtype=np.float64)
+    if r.size == 0:
+        return np.zeros(0)
+    floor = FLOOR * np.max(np.abs(r))
+    denom = np.maximum(np.abs(r), floor)
+    denom = np.where(denom == 0, 1.0, denom)
+    return np.abs(y - r) / denom
+
+
+def check_bf16(y_bits: np.ndarray, ref: np.ndarray, what: str = "") -> float:
+    assert y_bits.shape == ref.shape, (y_bits.shape, ref.shape)
+    err = bf16_errors(y_bits, ref)
+    worst = float(err.max()) if err.size else 0.0
+    if not worst <= BF16_TOL:
+        idx = np.unravel_index(int(np.argmax(err)), err.shape)
+        raise AssertionError(f"{what}: max floored rel err {worst:.3e} at {idx}: "
+                             f"gpu={oracle.decode_bf16(y_bits[idx])} ref={ref[idx]}; "
+                             f"{int((err > BF16_TOL).sum())} of {err.size} over tolerance")
+    return worst
+
+
+def e4m3_index(codes: np.ndarray) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.int64)
+    mag = c & 0x7F
+    return np.where(c & 0x80, -mag, mag)
+
+
+def check_fp8(codes: np.ndarray, ref_codes: np.ndarray, what: str = "") -> int:
+    assert codes.shape == ref_codes.shape
+    d = np.abs(e4m3_index(codes) - e4m3_index(ref_codes))
+    worst = int(d.max()) if d.size else 0
+    if worst > 1:
+        idx = np.unravel_index(int(np.argmax(d)), d.shape)
+        raise AssertionError(f"{what}: fp8 code distance {worst} at {idx}: gpu={codes[idx]:#04x} "
+                             f"ref={ref_codes[idx]:#04x}; {int((d > 1).sum())} codes off by more than one")
+    return worst
+
+
+def check_amax(got: float, ref: float, what: str = "") -> float:
+    if ref == 0.0:
+        assert got == 0.0, f"{what}: amax {got} vs 0"
+        return 0.0
+    rel = abs(got - ref) / abs(ref)
+    assert rel <= AMAX_TOL, f"{what}: amax {got} vs {ref} (rel {rel:.3e})"
+    return rel

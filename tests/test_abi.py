@@ -1,0 +1,127 @@
+"""The C-ABI library on the host: it loads, exports every symbol the header
+declares, and its HIP-free descriptor validation returns the documented codes.
+No compute is launched here."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import gemm_epilogue_transformer_tiled_amd as ge
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    names = set()
+    for path in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"\b(gemm_epilogue_\w+)\s*\(", text))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_symbols()
+    assert len(names) >= 7
+    lib = ctypes.CDLL(ge.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(ge.EXPORTED)
+
+
+def _desc(**kw):
+    base = dict(batch=1, M=64, N=64, K=64, ops=ge.make_ops([("scale",), ("bias",), ("act", "gelu_tanh"), ("amax",)]))
+    base.update(kw)
+    return ge.make_desc(**base)
+
+
+def test_validate_accepts_every_workload_chain():
+    import workloads
+    for w in workloads.WORKLOADS.values():
+        d = ge.make_desc(w.batch, w.M, w.N, w.K, ge.make_ops(w.chain),
+                         y_type=ge.GE_DT_FP8_E4M3 if w.out == "fp8_e4m3" else ge.GE_DT_BF16)
+        assert ge.gemm_epilogue_validate(d) == ge.GE_OK, w.name
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(M=-1), ge.GE_ERR_INVALID_ARG),
+    (dict(K=-8), ge.GE_ERR_INVALID_ARG),
+    (dict(N=12), ge.GE_ERR_UNSUPPORTED),                  # N not a multiple of 8
+    (dict(K=20), ge.GE_ERR_UNSUPPORTED),
+    (dict(lda=32), ge.GE_ERR_INVALID_ARG),                # lda < K
+    (dict(ldb=72, ldy=72), ge.GE_OK),
+    (dict(ldb=68), ge.GE_ERR_UNSUPPORTED),                # ld not a multiple of 8
+    (dict(a_type=ge.GE_DT_FP8_E4M3), ge.GE_ERR_UNSUPPORTED),
+    (dict(y_type=ge.GE_DT_FP32), ge.GE_ERR_UNSUPPORTED),
+    (dict(y_type=ge.GE_DT_FP8_E4M3), ge.GE_ERR_INVALID_ARG),  # fp8 output without QUANT_FP8
+    (dict(batch=2, stride_y=0), ge.GE_ERR_INVALID_ARG),   # batches would overwrite each other
+    (dict(batch=2, stride_b=0), ge.GE_OK),                # broadcast B
+    (dict(M=0), ge.GE_OK),
+    (dict(batch=0), ge.GE_OK),
+    (dict(K=0), ge.GE_OK),
+    (dict(M=1 << 20, K=1 << 12), ge.GE_ERR_UNSUPPORTED),  # A extent beyond 2 GiB
+])
+def test_validate_status_codes(kw, want):
+    assert ge.gemm_epilogue_validate(_desc(**kw)) == want
+
+
+@pytest.mark.parametrize("chain,want", [
+    ([("bias",), ("scale",)], ge.GE_ERR_INVALID_ARG),                 # out of canonical order
+    ([("scale",), ("scale",)], ge.GE_ERR_INVALID_ARG),                # duplicate
+    ([("act", "relu"), ("pairwise", "silu")], ge.GE_ERR_INVALID_ARG),  # exclusive
+    ([("row_rms", 1e-6), ("row_scale",)], ge.GE_ERR_INVALID_ARG),      # exclusive
+    ([("bias",), ("pairwise", "silu")], ge.GE_ERR_UNSUPPORTED),       # bias with pairwise
+    ([("row_rms", -1.0)], ge.GE_ERR_INVALID_ARG),
+    ([("row_rms", 1e-6), ("pairwise", "none")], ge.GE_OK),            # RMSNorm-MLP shape of chain
+    ([("scale",), ("row_scale",), ("bias",), ("act", "silu"), ("residual",), ("amax",)], ge.GE_OK),
+])
+def test_validate_chain_rules(chain, want):
+    assert ge.gemm_epilogue_validate(_desc(ops=ge.make_ops(chain))) == want
+
+
+def test_bad_op_kind_and_act():
+    d = _desc()
+    d.ops[0].kind = 42
+    assert ge.gemm_epilogue_validate(d) == ge.GE_ERR_INVALID_ARG
+    d = _desc()
+    d.ops[2].act = 9
+    assert ge.gemm_epilogue_validate(d) == ge.GE_ERR_INVALID_ARG
+    d = _desc()
+    d.n_ops = 9
+    assert ge.gemm_epilogue_validate(d) == ge.GE_ERR_INVALID_ARG
+
+
+def test_rms_needs_k():
+    d = _desc(K=0, ops=ge.make_ops([("row_rms", 1e-6)]))
+    assert ge.gemm_epilogue_validate(d) == ge.GE_ERR_INVALID_ARG
+
+
+def test_quant_requires_fp8_output_and_is_last():
+    ok = _desc(ops=ge.make_ops([("bias",), ("act", "gelu_tanh"), ("amax",), ("quant_fp8",)]),
+               y_type=ge.GE_DT_FP8_E4M3)
+    assert ge.gemm_epilogue_validate(ok) == ge.GE_OK
+    bf16_out = _desc(ops=ge.make_ops([("bias",), ("quant_fp8",)]))
+    assert ge.gemm_epilogue_validate(bf16_out) == ge.GE_ERR_INVALID_ARG
+
+
+def test_null_arguments_and_status_strings():
+    assert ge.lib.gemm_epilogue_validate(None) == ge.GE_ERR_INVALID_ARG
+    assert ge.lib.gemm_epilogue_create(None, None) == ge.GE_ERR_INVALID_ARG
+    assert ge.lib.gemm_epilogue_run(None, None, None) == ge.GE_ERR_INVALID_ARG
+    ge.gemm_epilogue_destroy(None)
+    for s in range(5):
+        assert ge.gemm_epilogue_status_string(s).startswith("GE_")
+    assert "unknown" in ge.gemm_epilogue_status_string(77)
+
+
+def test_create_without_a_gfx950_device_reports_device_error():
+    """On a host with no GPU, create() must fail cleanly with GE_ERR_DEVICE (and set no handle)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    h = ge.ge_handle_t(1234)
+    st = ge.lib.gemm_epilogue_create(ctypes.byref(_desc()), ctypes.byref(h))
+    assert st == ge.GE_ERR_DEVICE
+    assert not h.value

@@ -1,0 +1,276 @@
+"""GPU parity: the HIP path (through the C-ABI) against the float64 oracle.
+
+Small ragged shapes on every kernel instance, the K / empty / stride edge
+cases, the fp8 writer over every bf16 value in range, and each of the five
+workloads at full size in the launch configuration the benchmark uses.
+"""
+import contextlib
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.parity import check_amax, check_bf16, check_fp8
+
+pytestmark = pytest.mark.gpu
+
+ge = pytest.importorskip("gemm_epilogue_transformer_tiled_amd")
+from gemm_epilogue_transformer_tiled_amd import runner  # noqa: E402
+
+TILE_NAMES = {0: "256x256", 1: "256x128p", 2: "128x128", 3: "64x64", 4: "128x128p"}
+SINGLE_TILES = [0, 2, 3]
+PAIR_TILES = [1, 4]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    name = torch.cuda.get_device_properties(0).gcnArchName
+    assert name.startswith("gfx950"), name
+    yield
+    torch.cuda.synchronize()
+
+
+@contextlib.contextmanager
+def forced_tile(kind):
+    old = os.environ.get("GE_FORCE_TILE")
+    if kind is not None:
+        os.environ["GE_FORCE_TILE"] = str(kind)
+    try:
+        yield
+    finally:
+        if old is None:
+            os.environ.pop("GE_FORCE_TILE", None)
+        else:
+            os.environ["GE_FORCE_TILE"] = old
+
+
+def gpu_run(w, inp, tile=None, y_fill=None):
+    with forced_tile(tile):
+        prob = runner.prepare(w, inp, y_fill=y_fill)
+    prob.run()
+    torch.cuda.synchronize()
+    return prob
+
+
+def compare(w, inp, prob, what, rows=None):
+    ref = oracle.run_workload(w, inp, rows=rows)
+    y = prob.y_host_bits()
+    if rows is not None:
+        y = y[:, rows, :]
+    if w.out == "fp8_e4m3":
+        check_fp8(y, ref.codes, what)
+    else:
+        check_bf16(y, ref.y, what)
+    if w.has("amax") and rows is None:
+        check_amax(prob.amax_host(), ref.amax, what)
+    return ref
+
+
+RAGGED = dict(batch=2, M=300, N=264, K=200)
+
+
+@pytest.mark.parametrize("tile", SINGLE_TILES, ids=[TILE_NAMES[t] for t in SINGLE_TILES])
+@pytest.mark.parametrize("name", ["c1", "c2", "c4", "c5"])
+def test_ragged_every_tile(name, tile):
+    w = workloads.WORKLOADS[name].with_shape(**RAGGED)
+    inp = workloads.generate(w)
+    prob = gpu_run(w, inp, tile)
+    bm, bn = TILE_NAMES[tile].rstrip("p").split("x")
+    assert f"tile={bm}x{bn}x64" in prob.plan.describe()
+    compare(w, inp, prob, f"{name} ragged tile {TILE_NAMES[tile]}")
+
+
+@pytest.mark.parametrize("tile", PAIR_TILES, ids=[TILE_NAMES[t] for t in PAIR_TILES])
+def test_ragged_pairwise_tiles(tile):
+    w = workloads.WORKLOADS["c3"].with_shape(**RAGGED)
+    inp = workloads.generate(w)
+    compare(w, inp, gpu_run(w, inp, tile), f"c3 ragged tile {TILE_NAMES[tile]}")
+
+
+@pytest.mark.parametrize("tile", SINGLE_TILES, ids=[TILE_NAMES[t] for t in SINGLE_TILES])
+@pytest.mark.parametrize("name", ["c1", "c2", "c5"])
+def test_sensitive_inputs_every_tile(name, tile):
+    """bias = 0 and A ~ N(0, 1): the GEMM term dominates, so a wrong GEMM cannot hide behind the bias."""
+    w = workloads.WORKLOADS[name].with_shape(batch=2, M=264, N=136, K=520)
+    inp = workloads.generate(w, sensitive=True)
+    compare(w, inp, gpu_run(w, inp, tile), f"{name} sensitive tile {TILE_NAMES[tile]}")
+
+
+@pytest.mark.parametrize("K", [0, 8, 56, 64, 72, 128, 136, 1032])
+@pytest.mark.parametrize("tile", [0, 3], ids=["256x256", "64x64"])
+def test_k_edges(K, tile):
+    w = workloads.WORKLOADS["c2"].with_shape(batch=1, M=136, N=72, K=K)
+    inp = workloads.generate(w, sensitive=True)
+    compare(w, inp, gpu_run(w, inp, tile), f"K={K}")
+
+
+@pytest.mark.parametrize("K", [8, 64, 72, 200])
+@pytest.mark.parametrize("tile", PAIR_TILES, ids=[TILE_NAMES[t] for t in PAIR_TILES])
+def test_k_edges_pairwise(K, tile):
+    w = workloads.WORKLOADS["c3"].with_shape(batch=1, M=72, N=136, K=K)
+    inp = workloads.generate(w)
+    compare(w, inp, gpu_run(w, inp, tile), f"pairwise K={K}")
+
+
+@pytest.mark.parametrize("shape", [dict(M=0), dict(N=0), dict(batch=0)], ids=["M0", "N0", "batch0"])
+def test_empty_problem_zeroes_amax_and_writes_nothing(shape):
+    base = dict(batch=1, M=64, N=64, K=64)
+    base.update(shape)
+    w = workloads.WORKLOADS["c1"].with_shape(**base)
+    inp = workloads.generate(w)
+    prob = gpu_run(w, inp, y_fill=0x5A)
+    assert prob.amax_host() == 0.0
+    assert bool((prob.Y.view(torch.uint8) == 0x5A).all())
+
+
+def test_single_row_and_narrow_columns():
+    w = workloads.WORKLOADS["c1"].with_shape(batch=1, M=1, N=8, K=64)
+    inp = workloads.generate(w, sensitive=True)
+    compare(w, inp, gpu_run(w, inp), "1x8")
+
+
+def test_outputs_outside_the_problem_are_untouched():
+    """Y is written exactly once inside [M, N]; padding columns of a wider ldy keep their bytes."""
+    w = workloads.WORKLOADS["c2"].with_shape(batch=2, M=100, N=40, K=64)
+    inp = workloads.generate(w)
+    dev = "cuda"
+    t = {k: runner.to_device_bf16(v, dev) for k, v in inp.items()}
+    ldy = 56
+    Y = torch.full((2, 100, ldy), 7.0, dtype=torch.bfloat16, device=dev)
+    amax = torch.zeros(1, dtype=torch.float32, device=dev)
+    desc = ge.make_desc(2, 100, 40, 64, ge.make_ops(w.chain), ldy=ldy)
+    plan = ge.Plan(desc)
+    plan.run(ge.make_args(A=t["A"], B=t["B"], bias=t["bias"], Y=Y, amax=amax, alpha=w.alpha))
+    torch.cuda.synchronize()
+    ref = oracle.run_workload(w, inp)
+    ybits = Y.cpu().view(torch.int16).numpy().view(np.uint16)
+    check_bf16(np.ascontiguousarray(ybits[:, :, :40]), ref.y, "ldy=56")
+    assert np.all(oracle.decode_bf16(ybits[:, :, 40:]) == 7.0)
+    check_amax(float(amax.item()), ref.amax, "ldy=56")
+
+
+def test_strided_operands_and_broadcast_b():
+    """lda > K, ldb > N and a batch stride of 0 on B (one weight shared by every batch)."""
+    batch, M, N, K = 3, 96, 48, 80
+    lda, ldb = 96, 64
+    w = workloads.WORKLOADS["c2"].with_shape(batch=batch, M=M, N=N, K=K)
+    inp = workloads.generate(w, sensitive=True)
+    A_pad = np.zeros((batch, M, lda), dtype=np.uint16)
+    A_pad[:, :, :K] = inp["A"]
+    B_pad = np.zeros((1, K, ldb), dtype=np.uint16)
+    B_pad[0, :, :N] = inp["B"][0]
+    dev = "cuda"
+    A = runner.to_device_bf16(A_pad, dev)
+    B = runner.to_device_bf16(B_pad, dev)
+    bias = runner.to_device_bf16(inp["bias"], dev)
+    Y = torch.empty((batch, M, N), dtype=torch.bfloat16, device=dev)
+    amax = torch.zeros(1, dtype=torch.float32, device=dev)
+    desc = ge.make_desc(batch, M, N, K, ge.make_ops(w.chain), lda=lda, ldb=ldb, stride_b=0)
+    plan = ge.Plan(desc)
+    plan.run(ge.make_args(A=A, B=B, bias=bias, Y=Y, amax=amax, alpha=w.alpha))
+    torch.cuda.synchronize()
+    B_bcast = np.repeat(inp["B"][:1], batch, axis=0)
+    ref = oracle.run_chain(w.chain, inp["A"], B_bcast, bias=inp["bias"], alpha=w.alpha)
+    check_bf16(Y.cpu().view(torch.int16).numpy().view(np.uint16), ref.y, "strided")
+    check_amax(float(amax.item()), ref.amax, "strided")
+
+
+def test_external_row_scale_and_signed_amax():
+    """ROW_SCALE from a caller vector, no activation, and an output whose largest magnitude is negative."""
+    batch, M, N, K = 2, 130, 72, 96
+    chain = (("scale",), ("row_scale",), ("bias",), ("residual",), ("amax",))
+    w = workloads.Workload(name="rs", config_id=9, batch=batch, M=M, N=N, K=K, chain=chain, alpha=0.75)
+    inp = workloads.generate(w)
+    rng = np.random.default_rng(5)
+    inp["row_scale"] = rng.uniform(0.5, 2.0, size=(batch, M)).astype(np.float32)
+    inp["bias"][5] = 0xC2C8      # bf16 -100.0: the largest |y| sits in column 5 and is negative
+    prob = gpu_run(w, inp)
+    ref = oracle.run_workload(w, inp)
+    check_bf16(prob.y_host_bits(), ref.y, "row_scale")
+    assert ref.y.min() < -90
+    check_amax(prob.amax_host(), ref.amax, "row_scale")
+
+
+def test_rmsnorm_mlp_chain():
+    """ROW_RMS with a pairwise product and no activation (the RMSNorm-MLP graph): s^2 * (X@Wu)(X@Wg)."""
+    chain = (("row_rms", 1e-6), ("pairwise", "none"))
+    w = workloads.Workload(name="rmsmlp", config_id=10, batch=1, M=272, N=136, K=256, chain=chain,
+                           a_var="1", b_var="1/K")
+    inp = workloads.generate(w)
+    for tile in PAIR_TILES:
+        compare(w, inp, gpu_run(w, inp, tile), f"rms-mlp tile {TILE_NAMES[tile]}")
+
+
+def test_fp8_writer_over_every_bf16_value_in_range():
+    """A = 0, so y = bias[n]: the E4M3 writer sees every bf16 value in [-512, 512] once, scale 1 and 1.37."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = oracle.decode_bf16(bits)
+    sel = bits[np.isfinite(vals) & (np.abs(vals) <= 512)]
+    N = ((len(sel) + 7) // 8) * 8
+    bias = np.zeros(N, dtype=np.uint16)
+    bias[:len(sel)] = sel
+    for qs in (1.0, 1.37):
+        w = workloads.Workload(name="fp8", config_id=11, batch=1, M=4, N=N, K=8,
+                               chain=(("bias",), ("amax",), ("quant_fp8",)), quant_scale=qs, out="fp8_e4m3")
+        inp = {"A": np.zeros((1, 4, 8), dtype=np.uint16), "B": np.zeros((1, 8, N), dtype=np.uint16), "bias": bias}
+        prob = gpu_run(w, inp)
+        ref = oracle.run_workload(w, inp)
+        codes = prob.y_host_bits()
+        check_fp8(codes, ref.codes, f"fp8 writer qs={qs}")
+        if qs == 1.0:
+            # y*1 is exact in fp32, so the writer's rounding alone decides the code: it must be RNE exactly
+            mism = int((codes != ref.codes).sum())
+            assert mism == 0, f"{mism} codes differ from round-to-nearest-even"
+        check_amax(prob.amax_host(), ref.amax, "fp8 amax")
+
+
+# ---------------------------------------------------------------------------------------------
+# The five workloads at full size, in the benchmark's launch configuration.
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", workloads.CONFIG_ORDER)
+def test_full_workload(name):
+    w = workloads.WORKLOADS[name]
+    inp = workloads.generate(w)
+    prob = gpu_run(w, inp)
+    print(f"\n{name}: {prob.plan.describe()}", flush=True)
+    compare(w, inp, prob, f"{name} full")
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c5"])
+def test_full_workload_sensitive(name):
+    w = workloads.WORKLOADS[name]
+    inp = workloads.generate(w, sensitive=True)
+    compare(w, inp, gpu_run(w, inp), f"{name} full sensitive")
+
+
+def test_amax_workspace_is_left_zeroed_and_checked():
+    w = workloads.WORKLOADS["c2"].with_shape(batch=2, M=512, N=512, K=256)
+    inp = workloads.generate(w)
+    prob = gpu_run(w, inp)
+    assert prob.plan.workspace is not None
+    assert int(prob.plan.workspace.count_nonzero()) == 0
+    ref = oracle.run_workload(w, inp)
+    check_amax(prob.amax_host(), ref.amax, "first run")
+    # a workspace smaller than gemm_epilogue_workspace_size is rejected before any launch
+    args = ge.make_args(A=prob.tensors["A"], B=prob.tensors["B"], bias=prob.tensors["bias"], Y=prob.Y,
+                        amax=prob.amax, alpha=w.alpha, workspace=prob.plan.workspace[:8])
+    st = ge.gemm_epilogue_run(prob.plan.handle, args, torch.cuda.current_stream().cuda_stream)
+    assert st == ge.GE_ERR_INVALID_ARG
+
+
+def test_repeated_runs_are_identical_and_amax_is_overwritten():
+    w = workloads.WORKLOADS["c2"]
+    inp = workloads.generate(w)
+    prob = gpu_run(w, inp)
+    y1, a1 = prob.Y.clone(), prob.amax_host()
+    for _ in range(3):
+        prob.run()
+    torch.cuda.synchronize()
+    assert torch.equal(prob.Y, y1)
+    assert prob.amax_host() == a1

@@ -150,7 +150,7 @@ def _normal_bf16(config_id: int, tensor_id: int, shape, var: float) -> np.ndarra
 
 
 def _var(spec: str, K: int) -> float:
-    return 1.0 / K if spec == "1/K" else float(spec)
+    return 1.0 / max(K, 1) if spec == "1/K" else float(spec)
 
 
 def generate(w: Workload, sensitive: bool = False, seed_offset: int = 0) -> Dict[str, np.ndarray]:
