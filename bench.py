@@ -44,7 +44,22 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle timing sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bare", action="store_true", help="skip the bare-GEMM comparison")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark: run a plain device copy of MIB MiB ten times (the "
+                         "reference kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def calibrate_copy(mib):
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": n * 4, "copy_bytes_written_per_launch": n * 4, "launches": 10}))
 
 
 def time_launches(prob, steps, warmup):
@@ -119,6 +134,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import workloads
     from gemm_epilogue_transformer_tiled_amd import runner

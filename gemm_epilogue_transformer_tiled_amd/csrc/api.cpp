@@ -127,10 +127,10 @@ ge_status_t gemm_epilogue_validate(const ge_desc_t* d) {
 
   // layout
   const bool res = has_op(d, GE_OP_RESIDUAL);
-  if (d->M > 1 && d->lda < d->K) return GE_ERR_INVALID_ARG;
-  if (d->K > 1 && d->ldb < d->N) return GE_ERR_INVALID_ARG;
-  if (d->M > 1 && d->ldy < d->N) return GE_ERR_INVALID_ARG;
-  if (res && d->M > 1 && d->ldr < d->N) return GE_ERR_INVALID_ARG;
+  if (d->M > 0 && d->lda < d->K) return GE_ERR_INVALID_ARG;
+  if (d->K > 0 && d->ldb < d->N) return GE_ERR_INVALID_ARG;
+  if (d->M > 0 && d->ldy < d->N) return GE_ERR_INVALID_ARG;
+  if (res && d->M > 0 && d->ldr < d->N) return GE_ERR_INVALID_ARG;
   if (d->batch > 1 && d->stride_y == 0 && d->M > 0 && d->N > 0) return GE_ERR_INVALID_ARG;  // batches would race
 
   // supported set: 16-byte vector access everywhere
@@ -141,10 +141,13 @@ ge_status_t gemm_epilogue_validate(const ge_desc_t* d) {
   if (d->M > INT32_MAX || d->N > INT32_MAX || d->K > INT32_MAX || d->batch > INT32_MAX)
     return GE_ERR_UNSUPPORTED;
   const int64_t esize = d->y_type == GE_DT_FP8_E4M3 ? 1 : 2;
-  if (extent_elems(d->M, d->K, d->lda) * 2 > kMaxExtent) return GE_ERR_UNSUPPORTED;
-  if (extent_elems(d->K, d->N, d->ldb) * 2 > kMaxExtent) return GE_ERR_UNSUPPORTED;
-  if (extent_elems(d->M, d->N, d->ldy) * esize > kMaxExtent) return GE_ERR_UNSUPPORTED;
-  if (res && extent_elems(d->M, d->N, d->ldr) * 2 > kMaxExtent) return GE_ERR_UNSUPPORTED;
+  // Kernels address each operand with 32-bit byte offsets from a per-tile base and mark
+  // masked accesses with an offset of 2^31; every offset a tile can form (one tile and one
+  // K step past the end included) must therefore stay below 2^31.
+  if (extent_elems(d->M + 256, d->K + 64, d->lda) * 2 > kMaxExtent) return GE_ERR_UNSUPPORTED;
+  if (extent_elems(d->K + 128, d->N, d->ldb) * 2 > kMaxExtent) return GE_ERR_UNSUPPORTED;
+  if (extent_elems(d->M + 256, d->N, d->ldy) * esize > kMaxExtent) return GE_ERR_UNSUPPORTED;
+  if (res && extent_elems(d->M + 256, d->N, d->ldr) * 2 > kMaxExtent) return GE_ERR_UNSUPPORTED;
   // grid: one workgroup per 64x64 tile at most
   if (ceil_div(d->M, 64) * ceil_div(d->N, 64) * d->batch > INT32_MAX) return GE_ERR_UNSUPPORTED;
   return GE_OK;

@@ -31,6 +31,8 @@
 //     and stores Y with 8-byte (bf16) or 4-byte (fp8) vector accesses.
 //   * Workgroup ids are remapped so each XCD (own L2) receives a contiguous run
 //     of tiles, which are then walked in groups of 8 tile-rows for L2 reuse.
+#include <type_traits>
+
 #include "ge_internal.h"
 
 namespace ge {
@@ -41,12 +43,16 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 v4bf16_t __attribute__((ext_vector_type(4)));
 
 constexpr int kBK = 64;                   // K depth of one LDS stage
 constexpr int kRowBytes = kBK * 2;        // one staged row: 128 bytes
 constexpr uint32_t kOOB = 0x80000000u;    // offset past every buffer extent
 constexpr int kXCDs = 8;                  // MI355X: 8 accelerator dies, each with its own L2
 constexpr int kGroupM = 8;                // tile-rows walked together for L2 reuse
+// s_waitcnt immediate for "vector memory count 0" with the other counters left free
+// (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]).
+constexpr int kVmcnt0 = 0x0F70;
 constexpr float kLog2e = 1.4426950408889634f;
 // GELU tanh form as t * sigmoid(2u), u = sqrt(2/pi) (t + 0.044715 t^3):
 // sigmoid(2u) = 1 / (1 + 2^(-2 log2(e) u)).
@@ -62,15 +68,22 @@ struct Tile {
   static constexpr int WM = BM / 2, WN = BN / 2;     // per-wave output tile
   static constexpr int FM = WM / 32, FN = WN / 32;   // 32x32 MFMA blocks per wave
   static constexpr int NB = PAIR ? 2 : 1;            // B operands
-  static constexpr int A_CHUNKS = BM * 8 / NT;       // 16-byte chunks of A per thread per stage
-  static constexpr int B_UNITS_TOTAL = BN * NB;      // 8x8 transpose units per stage
-  static constexpr int B_UNITS = (B_UNITS_TOTAL + NT - 1) / NT;
+  // One LDS stage: A as [BM][64] (128-byte rows), then each B operand as [64][BN].
   static constexpr int A_BYTES = BM * kRowBytes;
-  static constexpr int B_BYTES = BN * kRowBytes;
+  static constexpr int B_ROWB = BN * 2;              // bytes per staged B row
+  static constexpr int B_CHUNKS = B_ROWB / 16;       // 16-byte chunks per B row
+  static constexpr int B_BYTES = kBK * B_ROWB;       // one B operand
   static constexpr int STAGE = A_BYTES + NB * B_BYTES;
   static constexpr int LDS = 2 * STAGE;
+  // Direct global->LDS loads: one instruction moves 1 KB (64 lanes x 16 bytes).
+  static constexpr int A_LOADS = A_BYTES / 1024 / WAVES;          // per wave per stage
+  static constexpr int B_ROWS_PER_LOAD = 1024 / B_ROWB;
+  static constexpr int B_LOADS_PER_OP = kBK / B_ROWS_PER_LOAD;    // per operand per stage
+  static constexpr int B_LOADS = NB * B_LOADS_PER_OP / WAVES;     // per wave per stage
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile must split into 2x2 waves of 32x32 blocks");
-  static_assert(A_CHUNKS >= 1 && BM * 8 % NT == 0, "A staging must divide evenly");
+  static_assert(A_LOADS >= 1 && A_BYTES % (1024 * WAVES) == 0, "A loads must divide over the waves");
+  static_assert(B_LOADS >= 1 && (NB * B_LOADS_PER_OP) % WAVES == 0, "B loads must divide over the waves");
+  static_assert(B_LOADS_PER_OP % B_LOADS == 0 || B_LOADS % B_LOADS_PER_OP == 0, "one operand per load");
 };
 
 using T256 = Tile<256, 256, false, 1>;
@@ -84,10 +97,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ uint32_t swz(uint32_t row) { return (row ^ (row >> 3)) & 7u; }
+// A rows are 128 bytes (eight 16-byte chunks).  Chunk c of row r lives at chunk
+// c ^ swz_a(r); the swizzle uses only r mod 32, so it is the same for every 32-row
+// MFMA block, and 16 consecutive rows read at one logical chunk hit 16 distinct
+// (row parity, chunk) bank groups.
+__device__ __forceinline__ uint32_t swz_a32(uint32_t row) { return ((row & 7u) ^ ((row >> 3) & 3u)); }
 
-__device__ __forceinline__ uint32_t lds_off(uint32_t row, uint32_t chunk) {
-  return row * kRowBytes + ((chunk ^ swz(row)) << 4);
+// B rows ([k][n], 2*BN bytes).  Chunk c of row k lives at chunk c ^ swz_b(k).  A
+// 16-lane transpose read touches rows k..k+3 (k % 4 == 0) and one pair of chunks;
+// the XOR pattern {0, 4, 10, 14} sends those four pairs to four different pairs of
+// every aligned group of four (distinct banks for 128-byte LDS cycles) and the two
+// 16-lane groups of a half-wave to complementary halves (256-byte cycles).
+template <int CHUNKS>
+__device__ __forceinline__ uint32_t swz_b(uint32_t k) {
+  const uint32_t q = k & 3u;
+  return ((q << 2) | ((q >> 1) << 1)) & (uint32_t)(CHUNKS - 1);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -139,13 +163,16 @@ __device__ __forceinline__ void tile_coords(int wg, const Params& p, int& b, int
 template <class T, int ACT, bool FP8, bool ROWSTAT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(T::WPE, T::WPE)))
 void fused_gemm_epilogue(Params p) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[T::LDS];
+  // Two LDS stages as two distinct arrays, so the compiler can tell that the direct
+  // loads filling one stage never alias the fragment reads of the other.
+  __shared__ __attribute__((aligned(1024))) unsigned char stage0[T::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage1[T::STAGE];
   __shared__ float row_ss[ROWSTAT ? T::BM : 1];
   __shared__ uint32_t wave_amax[T::WAVES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wave_m = wave & 1, wave_n = wave >> 1;
 
   int b, tm, tn;
@@ -153,92 +180,84 @@ void fused_gemm_epilogue(Params p) {
   const int m0 = tm * T::BM, n0 = tn * T::BN;
   const int M = p.M, N = p.N, K = p.K;
 
-  // ---- buffer resources (extent = last byte this tile may touch, so a bad offset reads 0) ----
+  // ---- buffer resources (extent = last byte this tile may touch; an offset past it reads 0) ----
   const uint16_t* a_base = p.A + b * p.sa + (int64_t)m0 * p.lda;
   const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(a_base, ((int64_t)(M - 1 - m0) * p.lda + K) * 2);
-  const uint16_t* b_base = p.B + b * p.sb + n0;
   const int64_t b_ext = K > 0 ? ((int64_t)(K - 1) * p.ldb + (N - n0)) * 2 : 0;
-  const __amdgpu_buffer_rsrc_t b_rs = make_rsrc(b_base, b_ext);
+  const __amdgpu_buffer_rsrc_t b_rs = make_rsrc(p.B + b * p.sb + n0, b_ext);
   __amdgpu_buffer_rsrc_t b2_rs = b_rs;
   if constexpr (T::PAIR) b2_rs = make_rsrc(p.B2 + b * p.sb + n0, b_ext);
 
-  // ---- per-thread staging assignment ----
-  // A: chunk q = tid + i*NT -> row q/8, 16-byte K-chunk q%8
-  // B: unit u = tid + i*NT -> operand u/BN, column block (u%BN)%(BN/8), K group (u%BN)/(BN/8)
-  u32x4_t a_stage[T::A_CHUNKS];
-  u32x4_t b_stage[T::B_UNITS][8];
-  float ss_part[ROWSTAT ? T::A_CHUNKS : 1];
-  if constexpr (ROWSTAT) {
+  // ---- direct global->LDS loads: per-lane source offsets, fixed for the whole K loop ----
+  // A load t of this wave fills 8 staged rows (1 KB): lane -> row 8*blk + lane/8, physical
+  // chunk lane%8, so it fetches logical chunk (lane%8) ^ swz_a32(row).  Rows past M fall
+  // outside the resource extent (lda >= K); K-tail chunks get the out-of-range offset.
+  const uint32_t ldb2 = (uint32_t)p.ldb * 2u;
+  uint32_t a_voff[T::A_LOADS], a_kcol[T::A_LOADS];
 #pragma unroll
-    for (int i = 0; i < T::A_CHUNKS; ++i) ss_part[i] = 0.0f;
+  for (int t = 0; t < T::A_LOADS; ++t) {
+    const uint32_t row = (uint32_t)(wave * T::A_LOADS + t) * 8u + (uint32_t)(lane >> 3);
+    const uint32_t lchunk = (uint32_t)(lane & 7) ^ swz_a32(row);
+    a_voff[t] = row * (uint32_t)p.lda * 2u + lchunk * 16u;
+    a_kcol[t] = lchunk * 8u;
+  }
+  // B load t fills B_ROWS_PER_LOAD rows of one operand: lane -> row lane/B_CHUNKS (within
+  // the load), physical chunk lane%B_CHUNKS, logical chunk ^ swz_b(row).  Rows past K fall
+  // outside the extent; a column block past N gets the out-of-range offset.
+  uint32_t b_voff[T::B_LOADS];
+#pragma unroll
+  for (int t = 0; t < T::B_LOADS; ++t) {
+    const int blk = (wave * T::B_LOADS + t) % T::B_LOADS_PER_OP;
+    const uint32_t row = (uint32_t)blk * T::B_ROWS_PER_LOAD + (uint32_t)(lane / T::B_CHUNKS);
+    const uint32_t lchunk = (uint32_t)(lane % T::B_CHUNKS) ^ swz_b<T::B_CHUNKS>(row);
+    b_voff[t] = (n0 + (int)lchunk * 8 < N) ? row * ldb2 + lchunk * 16u : kOOB;
   }
 
-  auto load_stage = [&](int k0) {
+  auto issue_loads = [&](int k0, unsigned char* stage) {
 #pragma unroll
-    for (int i = 0; i < T::A_CHUNKS; ++i) {
-      const int q = tid + i * T::NT;
-      const int r = q >> 3, c = q & 7;
-      const bool ok = (m0 + r < M) && (k0 + c * 8 < K);
-      const uint32_t off = ok ? (uint32_t)(((int64_t)r * p.lda + k0 + c * 8) * 2) : kOOB;
-      a_stage[i] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, off, 0, 0);
+    for (int t = 0; t < T::A_LOADS; ++t) {
+      const uint32_t off = (k0 + (int)a_kcol[t] < K) ? a_voff[t] + (uint32_t)k0 * 2u : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          a_rs, (__attribute__((address_space(3))) void*)(stage + (wave * T::A_LOADS + t) * 1024), 16, off, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < T::B_UNITS; ++i) {
-      const int u = tid + i * T::NT;
-      if (T::B_UNITS_TOTAL % T::NT == 0 || u < T::B_UNITS_TOTAL) {
-        const int op = u / T::BN, uu = u % T::BN;
-        const int nb = uu % (T::BN / 8), kg = uu / (T::BN / 8);
-        const bool col_ok = n0 + nb * 8 < N;
-        const __amdgpu_buffer_rsrc_t rs = (T::PAIR && op == 1) ? b2_rs : b_rs;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int k = k0 + kg * 8 + j;
-          const bool ok = col_ok && k < K;
-          const uint32_t off = ok ? (uint32_t)(((int64_t)k * p.ldb + nb * 8) * 2) : kOOB;
-          b_stage[i][j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-        }
-      }
+    for (int t = 0; t < T::B_LOADS; ++t) {
+      const int gblk = wave * T::B_LOADS + t;           // wave-uniform
+      const int op = gblk / T::B_LOADS_PER_OP;
+      const int blk = gblk % T::B_LOADS_PER_OP;
+      const uint32_t off = b_voff[t] + (uint32_t)k0 * ldb2;
+      unsigned char* dst = stage + T::A_BYTES + op * T::B_BYTES + blk * 1024;
+      if (T::PAIR && op == 1)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(b2_rs, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rs, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
     }
   };
 
-  auto store_stage = [&](unsigned char* stage) {
+  // ---- fragment addressing ----
+  // A (second MFMA source): lane reads row wm0 + 32j + lane%32, logical chunk 2ks + lane/32
+  // (eight consecutive K); the swizzle depends on lane%32 only, so j is an immediate offset.
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int wm0 = wave_m * T::WM, wn0 = wave_n * T::WN;
+  uint32_t a_frag[kBK / 16];
 #pragma unroll
-    for (int i = 0; i < T::A_CHUNKS; ++i) {
-      const int q = tid + i * T::NT;
-      const int r = q >> 3, c = q & 7;
-      *(u32x4_t*)(stage + lds_off(r, c)) = a_stage[i];
-      if constexpr (ROWSTAT) {
-        float s = ss_part[i];
+  for (int ks = 0; ks < kBK / 16; ++ks)
+    a_frag[ks] = (uint32_t)(wm0 + lrow) * kRowBytes + (((uint32_t)(2 * ks + lhalf) ^ swz_a32(lrow)) << 4);
+  // B (first MFMA source) through 16-lane transpose reads: in each group of 16 lanes, lane s
+  // points at row k0 + s/4 and columns nb + 4(s%4) .. +3, and receives column nb + s of rows
+  // k0 .. k0+3.  Two reads (rows +0..3, +4..7) give the eight K values of A's lane layout.
+  const int grp = lane >> 4, sl = lane & 15;
+  const uint32_t kl = (uint32_t)(8 * (grp >> 1) + (sl >> 2));            // row within the 16-K slice
+  uint32_t b_frag[T::NB][T::FN];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float lo = bf16_lo(a_stage[i][w]), hi = bf16_hi(a_stage[i][w]);
-          s = fmaf(lo, lo, s);
-          s = fmaf(hi, hi, s);
-        }
-        ss_part[i] = s;
-      }
+  for (int op = 0; op < T::NB; ++op)
+#pragma unroll
+    for (int i = 0; i < T::FN; ++i) {
+      const uint32_t ncol = (uint32_t)(wn0 + 32 * i + 16 * (grp & 1) + 4 * (sl & 3));
+      const uint32_t lchunk = ncol >> 3;
+      b_frag[op][i] = (uint32_t)(T::A_BYTES + op * T::B_BYTES) + kl * T::B_ROWB +
+                      ((lchunk ^ swz_b<T::B_CHUNKS>(kl)) << 4) + (ncol & 7u) * 2u;
     }
-#pragma unroll
-    for (int i = 0; i < T::B_UNITS; ++i) {
-      const int u = tid + i * T::NT;
-      if (T::B_UNITS_TOTAL % T::NT == 0 || u < T::B_UNITS_TOTAL) {
-        const int op = u / T::BN, uu = u % T::BN;
-        const int nb = uu % (T::BN / 8), kg = uu / (T::BN / 8);
-        unsigned char* bs = stage + T::A_BYTES + op * T::B_BYTES;
-        // 8x8 bf16 transpose: out[c] = column n = nb*8+c, K = kg*8 .. kg*8+7
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-          u32x4_t o;
-#pragma unroll
-          for (int pr = 0; pr < 4; ++pr) {
-            o[pr] = __builtin_amdgcn_perm(b_stage[i][2 * pr + 1][c >> 1], b_stage[i][2 * pr][c >> 1], sel);
-          }
-          *(u32x4_t*)(bs + lds_off(nb * 8 + c, kg)) = o;
-        }
-      }
-    }
-  };
 
   f32x16_t acc[T::FN][T::FM];
   f32x16_t acc2[T::PAIR ? T::FN : 1][T::PAIR ? T::FM : 1];
@@ -249,56 +268,123 @@ void fused_gemm_epilogue(Params p) {
       acc[i][j] = f32x16_t{};
       if constexpr (T::PAIR) acc2[i][j] = f32x16_t{};
     }
-
-  const int nk = (K + kBK - 1) / kBK;
-  const int lrow = lane & 31, lhalf = lane >> 5;
-  const int wm0 = wave_m * T::WM, wn0 = wave_n * T::WN;
-
-  if (nk > 0) {
-    load_stage(0);
-    store_stage(smem);
-    __syncthreads();
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    unsigned char* cur = smem + (kt & 1) * T::STAGE;
-    const bool more = kt + 1 < nk;
-    if (more) load_stage((kt + 1) * kBK);
+  // RMS statistic from the A fragments: waves with wave_n == 0 own the first half of the
+  // wave's 32-row blocks, wave_n == 1 the second half (all of them when FM == 1 and wave_n == 0).
+  constexpr int SS_J = T::FM > 1 ? T::FM / 2 : 1;
+  float ss[SS_J];
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int chunk = 2 * ks + lhalf;
-      bf16x8_t af[T::FM], bfr[T::FN], bfr2[T::PAIR ? T::FN : 1];
+  for (int j = 0; j < SS_J; ++j) ss[j] = 0.0f;
+  const bool ss_owner = T::FM > 1 || wave_n == 0;
+  const int ss_j0 = T::FM > 1 ? wave_n * SS_J : 0;
+
+  struct Frags {
+    bf16x8_t a[T::FM];
+    bf16x8_t b[T::NB][T::FN];
+  };
+  typedef __attribute__((address_space(3))) v4bf16_t lds_v4bf16;
+  auto read_frags = [&](const unsigned char* st, int ks, Frags& f) {
 #pragma unroll
-      for (int j = 0; j < T::FM; ++j)
-        af[j] = *(const bf16x8_t*)(cur + lds_off(wm0 + 32 * j + lrow, chunk));
+    for (int j = 0; j < T::FM; ++j)
+      f.a[j] = *(const bf16x8_t*)(st + a_frag[ks] + j * 32 * kRowBytes);
+#pragma unroll
+    for (int op = 0; op < T::NB; ++op)
 #pragma unroll
       for (int i = 0; i < T::FN; ++i) {
-        bfr[i] = *(const bf16x8_t*)(cur + T::A_BYTES + lds_off(wn0 + 32 * i + lrow, chunk));
-        if constexpr (T::PAIR)
-          bfr2[i] = *(const bf16x8_t*)(cur + T::A_BYTES + T::B_BYTES + lds_off(wn0 + 32 * i + lrow, chunk));
+        const unsigned char* q = st + b_frag[op][i] + 16 * ks * T::B_ROWB;
+        const v4bf16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf16*)(q));
+        const v4bf16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf16*)(q + 4 * T::B_ROWB));
+        f.b[op][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
+  };
+  auto mfmas = [&](const Frags& f) {
 #pragma unroll
-      for (int i = 0; i < T::FN; ++i)
+    for (int i = 0; i < T::FN; ++i)
 #pragma unroll
-        for (int j = 0; j < T::FM; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[i], af[j], acc[i][j], 0, 0, 0);
-          if constexpr (T::PAIR)
-            acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr2[i], af[j], acc2[i][j], 0, 0, 0);
+      for (int j = 0; j < T::FM; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[0][i], f.a[j], acc[i][j], 0, 0, 0);
+        if constexpr (T::PAIR)
+          acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[T::NB - 1][i], f.a[j], acc2[i][j], 0, 0, 0);
+      }
+    if constexpr (ROWSTAT) {
+      if (ss_owner) {
+#pragma unroll
+        for (int j = 0; j < SS_J; ++j) {
+          const bf16x8_t v = (T::FM > 1 && wave_n == 1) ? f.a[(T::FM > 1 ? SS_J : 0) + j] : f.a[j];
+          const bf16x2_t p0 = __builtin_shufflevector(v, v, 0, 1), p1 = __builtin_shufflevector(v, v, 2, 3);
+          const bf16x2_t p2 = __builtin_shufflevector(v, v, 4, 5), p3 = __builtin_shufflevector(v, v, 6, 7);
+          ss[j] = __builtin_amdgcn_fdot2_f32_bf16(p0, p0, ss[j], false);
+          ss[j] = __builtin_amdgcn_fdot2_f32_bf16(p1, p1, ss[j], false);
+          ss[j] = __builtin_amdgcn_fdot2_f32_bf16(p2, p2, ss[j], false);
+          ss[j] = __builtin_amdgcn_fdot2_f32_bf16(p3, p3, ss[j], false);
         }
+      }
     }
-    if (more) store_stage(smem + ((kt + 1) & 1) * T::STAGE);
+  };
+  // Interleave the fragment reads of the next 16-deep group with this group's MFMAs
+  // (DS read = 0x100, MFMA = 0x008 in the scheduling-group masks).
+  constexpr int READS_PER_GROUP = T::FM + 2 * T::NB * T::FN;
+  constexpr int MFMAS_PER_GROUP = T::FM * T::FN * T::NB;
+  // The first group of a K step also carries the direct loads of the next tile (VMEM =
+  // 0x010), spread over its first MFMAs so they are in flight as early as possible.
+  constexpr int LOADS_PER_STEP = T::A_LOADS + T::B_LOADS;
+  static_assert(LOADS_PER_STEP % 2 == 0, "loads are slotted in pairs");
+  constexpr bool LOAD_PAIRS = LOADS_PER_STEP / 2 <= MFMAS_PER_GROUP;
+  auto interleave = [&](bool with_loads) {
+#pragma unroll
+    for (int m = 0; m < MFMAS_PER_GROUP; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (LOAD_PAIRS) {
+        if (with_loads && m < LOADS_PER_STEP / 2) __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);
+      } else {
+        if (with_loads && m == 0) __builtin_amdgcn_sched_group_barrier(0x010, LOADS_PER_STEP, 0);
+      }
+      if (m < READS_PER_GROUP) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  // One K step on stage `cur`, entered with the fragments of its first 16-deep group in f0:
+  // start the direct loads of the next tile into `nxt`, run groups 0..2 with the following
+  // group's fragments in flight, read group 3's fragments, wait for this wave's loads and
+  // meet the other waves at the barrier.  Then group 3 runs while the first fragments of
+  // `nxt` are read, so the matrix cores stay busy across the barrier.  The loads are issued
+  // even past the last tile: every such offset is out of range, so they only write zeros
+  // into a stage whose reads are discarded (no branch in the loop body).
+  Frags f0, f1;
+  auto k_step = [&](const unsigned char* cur, unsigned char* nxt, int kt) {
+    issue_loads((kt + 1) * kBK, nxt);
+    read_frags(cur, 1, f1);
+    mfmas(f0);
+    interleave(true);
+    read_frags(cur, 2, f0);
+    mfmas(f1);
+    interleave(false);
+    read_frags(cur, 3, f1);
+    mfmas(f0);
+    interleave(false);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
-  }
+    read_frags(nxt, 0, f0);
+    mfmas(f1);
+    interleave(false);
+  };
 
-  // ---- RMS row statistic: reduce the 8 lanes that share a row, park it in LDS ----
+  const int nk = (K + kBK - 1) / kBK;
+  issue_loads(0, stage0);
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  __syncthreads();
+  read_frags(stage0, 0, f0);
+  int kt = 0;
+  for (; kt + 2 <= nk; kt += 2) {
+    k_step(stage0, stage1, kt);
+    k_step(stage1, stage0, kt + 1);
+  }
+  if (kt < nk) k_step(stage0, stage1, kt);
+
+  // ---- RMS row statistic: the two lane halves hold different K of the same rows ----
   if constexpr (ROWSTAT) {
 #pragma unroll
-    for (int i = 0; i < T::A_CHUNKS; ++i) {
-      float s = ss_part[i];
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 4);
-      const int q = tid + i * T::NT;
-      if ((q & 7) == 0) row_ss[q >> 3] = s;
+    for (int j = 0; j < SS_J; ++j) {
+      const float s = ss[j] + __shfl_xor(ss[j], 32);
+      if (ss_owner && lhalf == 0) row_ss[wm0 + 32 * (ss_j0 + j) + lrow] = s;
     }
     __syncthreads();
   }
