@@ -64,7 +64,7 @@ EXPORTED = ("gemm_epilogue_validate", "gemm_epilogue_create", "gemm_epilogue_wor
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m gemm_epilogue_transformer_tiled_amd.build` "
+            f"{LIB_PATH} is not built; run `python gemm_epilogue_transformer_tiled_amd/build.py` "
             "(there is no host fallback for this library)")
     # One HIP runtime per process: torch ships its own libamdhip64 (DT_NEEDED
     # "libamdhip64.so", soname "libamdhip64.so.7").  Loading torch first makes this

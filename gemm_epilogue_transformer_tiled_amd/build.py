@@ -1,6 +1,7 @@
 """Builds libgemm_epilogue.so in-tree with hipcc for gfx950.
 
-Usage: python -m gemm_epilogue_transformer_tiled_amd.build  (or build() from Python)
+Usage: python gemm_epilogue_transformer_tiled_amd/build.py  (runs by path: importing the
+package itself needs the library this script builds)
 """
 from __future__ import annotations
 

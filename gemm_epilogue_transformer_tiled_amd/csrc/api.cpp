@@ -201,7 +201,7 @@ ge_status_t gemm_epilogue_create(const ge_desc_t* desc, ge_handle_t* out) {
 
 ge_status_t gemm_epilogue_workspace_size(ge_handle_t h, size_t* bytes) {
   if (!h || !bytes) return GE_ERR_INVALID_ARG;
-  *bytes = (h->flags & ge::F_AMAX) ? ge::kAmaxWorkspaceBytes : 0;
+  *bytes = (h->flags & ge::F_AMAX) ? ge::amax_workspace_bytes(h->tiles_m * h->tiles_n * h->desc.batch) : 0;
   return GE_OK;
 }
 
@@ -215,7 +215,7 @@ ge_status_t gemm_epilogue_run(ge_handle_t h, const ge_args_t* a, void* stream) {
   if (f & ge::F_AMAX) {
     if (!a->amax || !aligned(a->amax, 4)) return GE_ERR_INVALID_ARG;
     if (!empty && (!a->workspace || !aligned(a->workspace, 16) ||
-                   a->workspace_bytes < ge::kAmaxWorkspaceBytes))
+                   a->workspace_bytes < ge::amax_workspace_bytes(h->tiles_m * h->tiles_n * d.batch)))
       return GE_ERR_INVALID_ARG;
   }
   if (!empty) {

@@ -37,7 +37,7 @@ struct Params {
   const uint16_t* R;
   void* Y;
   uint32_t* amax;          // fp32 AMAX viewed as its bit pattern
-  uint32_t* ws;            // AMAX workspace: [0] running max bits, [1] finished-workgroup count; zero between runs
+  uint32_t* ws;            // AMAX workspace (layout below); counters are zero between runs
   int64_t lda, ldb, ldy, ldr;
   int64_t sa, sb, sy, sr;  // batch strides in elements
   int32_t M, N, K, batch;
@@ -60,7 +60,11 @@ hipError_t launch_fused(TileKind kind, int act, bool fp8_out, const Params& p, h
 // Enqueues a one-thread kernel that writes 0 to *amax (empty problems only).
 hipError_t launch_amax_zero(uint32_t* amax, hipStream_t stream);
 
-// Bytes of caller workspace the AMAX reduction needs.
-constexpr size_t kAmaxWorkspaceBytes = 256;
+// AMAX workspace layout (32-bit words): eight dispatch-group ticket counters and one top
+// counter, each on its own 256-byte line, then one partial-maximum slot per workgroup.
+constexpr uint32_t kAmaxGroups = 8;
+constexpr uint32_t kAmaxCounterStride = 64;
+constexpr uint32_t kAmaxSlot0 = 1024;
+inline size_t amax_workspace_bytes(int64_t workgroups) { return 4 * ((size_t)kAmaxSlot0 + (size_t)workgroups); }
 
 }  // namespace ge

@@ -44,15 +44,17 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 v4bf16_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kBK = 64;                   // K depth of one LDS stage
-constexpr int kRowBytes = kBK * 2;        // one staged row: 128 bytes
 constexpr uint32_t kOOB = 0x80000000u;    // offset past every buffer extent
 constexpr int kXCDs = 8;                  // MI355X: 8 accelerator dies, each with its own L2
 constexpr int kGroupM = 8;                // tile-rows walked together for L2 reuse
 // s_waitcnt immediate for "vector memory count 0" with the other counters left free
 // (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]).
-constexpr int kVmcnt0 = 0x0F70;
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+constexpr int kVmcnt0 = vmcnt_imm(0);
+// Same, with the LDS counter (lgkmcnt) also drained to zero.
+constexpr int vmcnt_lgkm0_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4); }
 constexpr float kLog2e = 1.4426950408889634f;
 // GELU tanh form as t * sigmoid(2u), u = sqrt(2/pi) (t + 0.044715 t^3):
 // sigmoid(2u) = 1 / (1 + 2^(-2 log2(e) u)).
@@ -68,22 +70,31 @@ struct Tile {
   static constexpr int WM = BM / 2, WN = BN / 2;     // per-wave output tile
   static constexpr int FM = WM / 32, FN = WN / 32;   // 32x32 MFMA blocks per wave
   static constexpr int NB = PAIR ? 2 : 1;            // B operands
-  // One LDS stage: A as [BM][64] (128-byte rows), then each B operand as [64][BN].
-  static constexpr int A_BYTES = BM * kRowBytes;
+  // Pipeline: K steps of BK, NS LDS stages in a ring, so the tile of step k+NS-1 is
+  // fetched while step k computes (three steps of latency cover for L2 misses).
+  static constexpr int BK = 32, NS = 4;
+  static constexpr int GROUPS = BK / 16;             // 16-deep MFMA groups per step
+  // One LDS stage: A as [BM][BK] (64-byte rows), then each B operand as [BK][BN].
+  static constexpr int A_ROWB = BK * 2;
+  static constexpr int A_CHUNKS = A_ROWB / 16;
+  static constexpr int A_BYTES = BM * A_ROWB;
   static constexpr int B_ROWB = BN * 2;              // bytes per staged B row
   static constexpr int B_CHUNKS = B_ROWB / 16;       // 16-byte chunks per B row
-  static constexpr int B_BYTES = kBK * B_ROWB;       // one B operand
+  static constexpr int B_BYTES = BK * B_ROWB;        // one B operand
   static constexpr int STAGE = A_BYTES + NB * B_BYTES;
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int LDS = NS * STAGE;
   // Direct global->LDS loads: one instruction moves 1 KB (64 lanes x 16 bytes).
-  static constexpr int A_LOADS = A_BYTES / 1024 / WAVES;          // per wave per stage
+  static constexpr int A_ROWS_PER_LOAD = 1024 / A_ROWB;
+  static constexpr int A_LOADS = A_BYTES / 1024 / WAVES;          // per wave per step
   static constexpr int B_ROWS_PER_LOAD = 1024 / B_ROWB;
-  static constexpr int B_LOADS_PER_OP = kBK / B_ROWS_PER_LOAD;    // per operand per stage
-  static constexpr int B_LOADS = NB * B_LOADS_PER_OP / WAVES;     // per wave per stage
+  static constexpr int B_LOADS_PER_OP = BK / B_ROWS_PER_LOAD;     // per operand per step
+  static constexpr int B_LOADS = NB * B_LOADS_PER_OP / WAVES;     // per wave per step
+  static constexpr int LOADS = A_LOADS + B_LOADS;                 // per wave per step
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile must split into 2x2 waves of 32x32 blocks");
   static_assert(A_LOADS >= 1 && A_BYTES % (1024 * WAVES) == 0, "A loads must divide over the waves");
   static_assert(B_LOADS >= 1 && (NB * B_LOADS_PER_OP) % WAVES == 0, "B loads must divide over the waves");
   static_assert(B_LOADS_PER_OP % B_LOADS == 0 || B_LOADS % B_LOADS_PER_OP == 0, "one operand per load");
+  static_assert((NS - 2) * LOADS < 64, "vmcnt range");
 };
 
 using T256 = Tile<256, 256, false, 1>;
@@ -97,11 +108,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// A rows are 128 bytes (eight 16-byte chunks).  Chunk c of row r lives at chunk
-// c ^ swz_a(r); the swizzle uses only r mod 32, so it is the same for every 32-row
-// MFMA block, and 16 consecutive rows read at one logical chunk hit 16 distinct
-// (row parity, chunk) bank groups.
-__device__ __forceinline__ uint32_t swz_a32(uint32_t row) { return ((row & 7u) ^ ((row >> 3) & 3u)); }
+// A rows are 2*BK bytes (CHUNKS 16-byte chunks).  Chunk c of row r lives at chunk
+// c ^ swz_a(r).  The swizzle uses only r mod 16, so it is the same for every 32-row MFMA
+// block; 32 consecutive rows read at one logical chunk land on distinct banks both for
+// 128-byte and 256-byte LDS cycles.
+template <int CHUNKS>
+__device__ __forceinline__ uint32_t swz_a(uint32_t row) {
+  if constexpr (CHUNKS == 4) {
+    return ((row >> 1) ^ (row >> 2)) & 3u;
+  } else {
+    return (row & 7u) ^ ((row >> 3) & 3u);
+  }
+}
 
 // B rows ([k][n], 2*BN bytes).  Chunk c of row k lives at chunk c ^ swz_b(k).  A
 // 16-lane transpose read touches rows k..k+3 (k % 4 == 0) and one pair of chunks;
@@ -163,12 +181,26 @@ __device__ __forceinline__ void tile_coords(int wg, const Params& p, int& b, int
 template <class T, int ACT, bool FP8, bool ROWSTAT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(T::WPE, T::WPE)))
 void fused_gemm_epilogue(Params p) {
-  // Two LDS stages as two distinct arrays, so the compiler can tell that the direct
-  // loads filling one stage never alias the fragment reads of the other.
+  // The LDS stages are distinct arrays, so the compiler can tell that the direct loads
+  // filling one stage never alias the fragment reads of another.
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[T::STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char stage1[T::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage2[T::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage3[T::STAGE];
   __shared__ float row_ss[ROWSTAT ? T::BM : 1];
   __shared__ uint32_t wave_amax[T::WAVES];
+  static_assert(T::NS == 4, "four stage arrays");
+  auto stage = [&](auto s_c) -> unsigned char* {
+    constexpr int S = decltype(s_c)::value % T::NS;
+    if constexpr (S == 0) return stage0;
+    else if constexpr (S == 1) return stage1;
+    else if constexpr (S == 2) return stage2;
+    else return stage3;
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -189,15 +221,16 @@ void fused_gemm_epilogue(Params p) {
   if constexpr (T::PAIR) b2_rs = make_rsrc(p.B2 + b * p.sb + n0, b_ext);
 
   // ---- direct global->LDS loads: per-lane source offsets, fixed for the whole K loop ----
-  // A load t of this wave fills 8 staged rows (1 KB): lane -> row 8*blk + lane/8, physical
-  // chunk lane%8, so it fetches logical chunk (lane%8) ^ swz_a32(row).  Rows past M fall
-  // outside the resource extent (lda >= K); K-tail chunks get the out-of-range offset.
+  // A load t of this wave fills A_ROWS_PER_LOAD staged rows (1 KB): lane -> row
+  // lane/A_CHUNKS of the load, physical chunk lane%A_CHUNKS, so it fetches logical chunk
+  // (lane%A_CHUNKS) ^ swz_a(row).  Rows past M fall outside the resource extent
+  // (lda >= K); K-tail chunks get the out-of-range offset.
   const uint32_t ldb2 = (uint32_t)p.ldb * 2u;
   uint32_t a_voff[T::A_LOADS], a_kcol[T::A_LOADS];
 #pragma unroll
   for (int t = 0; t < T::A_LOADS; ++t) {
-    const uint32_t row = (uint32_t)(wave * T::A_LOADS + t) * 8u + (uint32_t)(lane >> 3);
-    const uint32_t lchunk = (uint32_t)(lane & 7) ^ swz_a32(row);
+    const uint32_t row = (uint32_t)(wave * T::A_LOADS + t) * T::A_ROWS_PER_LOAD + (uint32_t)(lane / T::A_CHUNKS);
+    const uint32_t lchunk = (uint32_t)(lane % T::A_CHUNKS) ^ swz_a<T::A_CHUNKS>(row);
     a_voff[t] = row * (uint32_t)p.lda * 2u + lchunk * 16u;
     a_kcol[t] = lchunk * 8u;
   }
@@ -213,20 +246,21 @@ void fused_gemm_epilogue(Params p) {
     b_voff[t] = (n0 + (int)lchunk * 8 < N) ? row * ldb2 + lchunk * 16u : kOOB;
   }
 
-  auto issue_loads = [&](int k0, unsigned char* stage) {
+  auto issue_loads = [&](int k0, unsigned char* st) {
+    const bool live = k0 >= 0;     // k0 < 0: an all-zero leading tile
 #pragma unroll
     for (int t = 0; t < T::A_LOADS; ++t) {
-      const uint32_t off = (k0 + (int)a_kcol[t] < K) ? a_voff[t] + (uint32_t)k0 * 2u : kOOB;
+      const uint32_t off = (live & (k0 + (int)a_kcol[t] < K)) ? a_voff[t] + (uint32_t)k0 * 2u : kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          a_rs, (__attribute__((address_space(3))) void*)(stage + (wave * T::A_LOADS + t) * 1024), 16, off, 0, 0, 0);
+          a_rs, (__attribute__((address_space(3))) void*)(st + (wave * T::A_LOADS + t) * 1024), 16, off, 0, 0, 0);
     }
 #pragma unroll
     for (int t = 0; t < T::B_LOADS; ++t) {
       const int gblk = wave * T::B_LOADS + t;           // wave-uniform
       const int op = gblk / T::B_LOADS_PER_OP;
       const int blk = gblk % T::B_LOADS_PER_OP;
-      const uint32_t off = b_voff[t] + (uint32_t)k0 * ldb2;
-      unsigned char* dst = stage + T::A_BYTES + op * T::B_BYTES + blk * 1024;
+      const uint32_t off = live ? b_voff[t] + (uint32_t)k0 * ldb2 : kOOB;
+      unsigned char* dst = st + T::A_BYTES + op * T::B_BYTES + blk * 1024;
       if (T::PAIR && op == 1)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(b2_rs, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
       else
@@ -235,14 +269,14 @@ void fused_gemm_epilogue(Params p) {
   };
 
   // ---- fragment addressing ----
-  // A (second MFMA source): lane reads row wm0 + 32j + lane%32, logical chunk 2ks + lane/32
+  // A (second MFMA source): lane reads row wm0 + 32j + lane%32, logical chunk 2g + lane/32
   // (eight consecutive K); the swizzle depends on lane%32 only, so j is an immediate offset.
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int wm0 = wave_m * T::WM, wn0 = wave_n * T::WN;
-  uint32_t a_frag[kBK / 16];
+  uint32_t a_frag[T::GROUPS];
 #pragma unroll
-  for (int ks = 0; ks < kBK / 16; ++ks)
-    a_frag[ks] = (uint32_t)(wm0 + lrow) * kRowBytes + (((uint32_t)(2 * ks + lhalf) ^ swz_a32(lrow)) << 4);
+  for (int g = 0; g < T::GROUPS; ++g)
+    a_frag[g] = (uint32_t)(wm0 + lrow) * T::A_ROWB + (((uint32_t)(2 * g + lhalf) ^ swz_a<T::A_CHUNKS>(lrow)) << 4);
   // B (first MFMA source) through 16-lane transpose reads: in each group of 16 lanes, lane s
   // points at row k0 + s/4 and columns nb + 4(s%4) .. +3, and receives column nb + s of rows
   // k0 .. k0+3.  Two reads (rows +0..3, +4..7) give the eight K values of A's lane layout.
@@ -282,15 +316,15 @@ void fused_gemm_epilogue(Params p) {
     bf16x8_t b[T::NB][T::FN];
   };
   typedef __attribute__((address_space(3))) v4bf16_t lds_v4bf16;
-  auto read_frags = [&](const unsigned char* st, int ks, Frags& f) {
+  auto read_frags = [&](const unsigned char* st, int g, Frags& f) {
 #pragma unroll
     for (int j = 0; j < T::FM; ++j)
-      f.a[j] = *(const bf16x8_t*)(st + a_frag[ks] + j * 32 * kRowBytes);
+      f.a[j] = *(const bf16x8_t*)(st + a_frag[g] + j * 32 * T::A_ROWB);
 #pragma unroll
     for (int op = 0; op < T::NB; ++op)
 #pragma unroll
       for (int i = 0; i < T::FN; ++i) {
-        const unsigned char* q = st + b_frag[op][i] + 16 * ks * T::B_ROWB;
+        const unsigned char* q = st + b_frag[op][i] + 16 * g * T::B_ROWB;
         const v4bf16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf16*)(q));
         const v4bf16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf16*)(q + 4 * T::B_ROWB));
         f.b[op][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -321,63 +355,69 @@ void fused_gemm_epilogue(Params p) {
     }
   };
   // Interleave the fragment reads of the next 16-deep group with this group's MFMAs
-  // (DS read = 0x100, MFMA = 0x008 in the scheduling-group masks).
+  // (DS read = 0x100, MFMA = 0x008 in the scheduling-group masks).  The first group of a
+  // step also carries the step's direct loads (VMEM = 0x010), in pairs after its first MFMAs.
   constexpr int READS_PER_GROUP = T::FM + 2 * T::NB * T::FN;
   constexpr int MFMAS_PER_GROUP = T::FM * T::FN * T::NB;
-  // The first group of a K step also carries the direct loads of the next tile (VMEM =
-  // 0x010), spread over its first MFMAs so they are in flight as early as possible.
-  constexpr int LOADS_PER_STEP = T::A_LOADS + T::B_LOADS;
-  static_assert(LOADS_PER_STEP % 2 == 0, "loads are slotted in pairs");
-  constexpr bool LOAD_PAIRS = LOADS_PER_STEP / 2 <= MFMAS_PER_GROUP;
+  static_assert(T::LOADS % 2 == 0, "loads are slotted in pairs");
+  constexpr bool LOAD_PAIRS = T::LOADS / 2 <= MFMAS_PER_GROUP;
   auto interleave = [&](bool with_loads) {
 #pragma unroll
     for (int m = 0; m < MFMAS_PER_GROUP; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if constexpr (LOAD_PAIRS) {
-        if (with_loads && m < LOADS_PER_STEP / 2) __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);
+        if (with_loads && m < T::LOADS / 2) __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);
       } else {
-        if (with_loads && m == 0) __builtin_amdgcn_sched_group_barrier(0x010, LOADS_PER_STEP, 0);
+        if (with_loads && m == 0) __builtin_amdgcn_sched_group_barrier(0x010, T::LOADS, 0);
       }
       if (m < READS_PER_GROUP) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
-  // One K step on stage `cur`, entered with the fragments of its first 16-deep group in f0:
-  // start the direct loads of the next tile into `nxt`, run groups 0..2 with the following
-  // group's fragments in flight, read group 3's fragments, wait for this wave's loads and
-  // meet the other waves at the barrier.  Then group 3 runs while the first fragments of
-  // `nxt` are read, so the matrix cores stay busy across the barrier.  The loads are issued
-  // even past the last tile: every such offset is out of range, so they only write zeros
-  // into a stage whose reads are discarded (no branch in the loop body).
+  // One K step on stage S (tile kt), entered with the fragments of its first group in f0:
+  // start the direct loads of tile kt+NS-1 into the stage freed by the previous step, run
+  // the groups with the following group's fragments in flight, read the last group's
+  // fragments, wait until tile kt+1 has landed (later tiles stay in flight), meet the other
+  // waves at the barrier, then run the last group while the first fragments of tile kt+1
+  // are read -- the matrix cores stay busy across the barrier.  Loads are issued even past
+  // the last tile: those offsets are all out of range, so they only write zeros into stages
+  // whose reads are discarded (no branch in the loop body).
   Frags f0, f1;
-  auto k_step = [&](const unsigned char* cur, unsigned char* nxt, int kt) {
-    issue_loads((kt + 1) * kBK, nxt);
+  auto k_step = [&](auto s_c, int kt) {
+    constexpr int S = decltype(s_c)::value;
+    const unsigned char* cur = stage(std::integral_constant<int, S>{});
+    issue_loads((kt + T::NS - 1) * T::BK, stage(std::integral_constant<int, S + T::NS - 1>{}));
+    static_assert(T::GROUPS == 2, "two groups per step");
     read_frags(cur, 1, f1);
     mfmas(f0);
     interleave(true);
-    read_frags(cur, 2, f0);
-    mfmas(f1);
-    interleave(false);
-    read_frags(cur, 3, f1);
-    mfmas(f0);
-    interleave(false);
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
-    __syncthreads();
-    read_frags(nxt, 0, f0);
+    // Cross-wave facts the barrier publishes: this wave's direct loads of tile kt+1 have
+    // landed in LDS, and its fragment reads of this stage have returned (the stage is
+    // refilled one step later).  No memory fence: the later tiles stay in flight.
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((T::NS - 2) * T::LOADS));
+    __builtin_amdgcn_s_barrier();
+    read_frags(stage(std::integral_constant<int, S + 1>{}), 0, f0);
     mfmas(f1);
     interleave(false);
   };
 
-  const int nk = (K + kBK - 1) / kBK;
-  issue_loads(0, stage0);
-  __builtin_amdgcn_s_waitcnt(kVmcnt0);
-  __syncthreads();
-  read_frags(stage0, 0, f0);
-  int kt = 0;
-  for (; kt + 2 <= nk; kt += 2) {
-    k_step(stage0, stage1, kt);
-    k_step(stage1, stage0, kt + 1);
+  // Step count rounded up to a multiple of NS with leading all-zero tiles, so the loop
+  // always runs whole stage rings and the accumulators have one exit path.
+  const int nk = (K + T::BK - 1) / T::BK;
+  const int nsteps = (nk + T::NS - 1) / T::NS * T::NS;
+  int kt = nk - nsteps;
+  issue_loads((kt + 0) * T::BK, stage(S0{}));
+  issue_loads((kt + 1) * T::BK, stage(S1{}));
+  issue_loads((kt + 2) * T::BK, stage(S2{}));
+  __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((T::NS - 2) * T::LOADS));
+  __builtin_amdgcn_s_barrier();
+  read_frags(stage(S0{}), 0, f0);
+  for (; kt < nk; kt += T::NS) {
+    k_step(S0{}, kt);
+    k_step(S1{}, kt + 1);
+    k_step(S2{}, kt + 2);
+    k_step(S3{}, kt + 3);
   }
-  if (kt < nk) k_step(stage0, stage1, kt);
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);                 // trailing zero-tile loads into the stages
 
   // ---- RMS row statistic: the two lane halves hold different K of the same rows ----
   if constexpr (ROWSTAT) {
@@ -389,106 +429,151 @@ void fused_gemm_epilogue(Params p) {
     __syncthreads();
   }
 
-  // ---- epilogue on the register tile ----
+  // ---- epilogue, two phases per 32-row block of the wave's tile ----
+  // Phase 1 (registers -> LDS): the per-row linear part t = acc * alpha * s[m] (for the
+  // pairwise op the finished product act(t_gate) * t_up) goes to a wave-private fp32
+  // block in LDS, rows padded by 16 bytes so the 32 rows written at one column spread
+  // over all banks.  Phase 2 (LDS -> HBM): each lane takes 4 consecutive columns of a
+  // row, adds the column bias, applies the activation, adds the residual, folds |y|
+  // into AMAX (fp32, before rounding), converts and stores; one instruction covers whole
+  // rows, so residual loads and output stores are fully coalesced.
   const uint32_t flags = p.flags;
+  const bool has_bias = (flags & F_BIAS) != 0;
+  const bool has_res = (flags & F_RESIDUAL) != 0;
+  const bool has_rs = (flags & F_ROW_SCALE) != 0;
+  const bool has_rms = ROWSTAT && (flags & F_ROW_RMS) != 0;
   const float alpha = (flags & F_SCALE) ? p.alpha : 1.0f;
   const float inv_k = K > 0 ? 1.0f / (float)K : 0.0f;
 
-  // bias for this lane's columns: n = wn0 + 32i + 8g + 4*lhalf + e
-  float bias_v[T::FN][4][4];
-  if (flags & F_BIAS) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.bias + n0, (int64_t)(N - n0) * 2);
-#pragma unroll
-    for (int i = 0; i < T::FN; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int nl = wn0 + 32 * i + 8 * g + 4 * lhalf;
-        const uint32_t off = (n0 + nl < N) ? (uint32_t)(nl * 2) : kOOB;
-        const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
-        bias_v[i][g][0] = bf16_lo(w[0]);
-        bias_v[i][g][1] = bf16_hi(w[0]);
-        bias_v[i][g][2] = bf16_lo(w[1]);
-        bias_v[i][g][3] = bf16_hi(w[1]);
-      }
-  } else {
-#pragma unroll
-    for (int i = 0; i < T::FN; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) bias_v[i][g][e] = 0.0f;
-  }
+  constexpr int EP_LD = T::WN + 4;                      // floats per LDS row
+  constexpr int EP_WAVE_BYTES = 32 * EP_LD * 4;
+  static_assert(EP_WAVE_BYTES <= T::STAGE, "one wave's epilogue block per stage");
+  constexpr int LPR = T::WN / 4;                        // phase-2 lanes per row
+  constexpr int RPP = 64 / LPR;                         // rows per phase-2 pass
+  constexpr int PASSES = 32 / RPP;
+  __syncthreads();                                      // every wave is done with the stages
+  float* ep = (float*)(wave == 0 ? stage0 : wave == 1 ? stage1 : wave == 2 ? stage2 : stage3);
 
+  const int p2_row = lane / LPR, p2_col = 4 * (lane % LPR);
+  const int gcol = n0 + wn0 + p2_col;
+  const bool col_ok = gcol < N;
+  float bias4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (has_bias) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.bias + n0, (int64_t)(N - n0) * 2);
+    const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(rs, col_ok ? (uint32_t)(gcol - n0) * 2u : kOOB, 0, 0);
+    bias4[0] = bf16_lo(w[0]);
+    bias4[1] = bf16_hi(w[0]);
+    bias4[2] = bf16_lo(w[1]);
+    bias4[3] = bf16_hi(w[1]);
+  }
   const int esize = FP8 ? 1 : 2;
   void* y_base = (unsigned char*)p.Y + (b * p.sy + (int64_t)m0 * p.ldy + n0) * esize;
   const __amdgpu_buffer_rsrc_t y_rs =
       make_rsrc(y_base, ((int64_t)(M - 1 - m0) * p.ldy + (N - n0)) * esize);
-  __amdgpu_buffer_rsrc_t r_rs = y_rs;
-  if (flags & F_RESIDUAL)
-    r_rs = make_rsrc(p.R + b * p.sr + (int64_t)m0 * p.ldr + n0, ((int64_t)(M - 1 - m0) * p.ldr + (N - n0)) * 2);
+  const __amdgpu_buffer_rsrc_t r_rs =
+      has_res ? make_rsrc(p.R + b * p.sr + (int64_t)m0 * p.ldr + n0, ((int64_t)(M - 1 - m0) * p.ldr + (N - n0)) * 2)
+              : y_rs;
+  const uint32_t ldy_b = (uint32_t)p.ldy * (uint32_t)esize, ldr_b = (uint32_t)p.ldr * 2u;
+  const uint32_t col_y = col_ok ? (uint32_t)(wn0 + p2_col) * (uint32_t)esize : kOOB;
+  const uint32_t col_r = col_ok ? (uint32_t)(wn0 + p2_col) * 2u : kOOB;
 
   uint32_t amax_bits = 0;
+  auto phase2 = [&](int j, auto res_c) {
+    constexpr bool RES = decltype(res_c)::value;
+    u32x2_t rv[PASSES];
+    if constexpr (RES) {
+#pragma unroll
+      for (int ps = 0; ps < PASSES; ++ps) {
+        const int ml = wm0 + 32 * j + ps * RPP + p2_row;
+        const uint32_t off = (m0 + ml < M) ? (uint32_t)ml * ldr_b + col_r : kOOB;
+        rv[ps] = __builtin_amdgcn_raw_buffer_load_b64(r_rs, off | (col_r & kOOB), 0, 0);
+      }
+    }
+    f32x4_t vv[PASSES];
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) vv[ps] = *(const f32x4_t*)(ep + (ps * RPP + p2_row) * EP_LD + p2_col);
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int r = ps * RPP + p2_row;
+      const int ml = wm0 + 32 * j + r;
+      const bool ok = (m0 + ml < M) & col_ok;
+      const f32x4_t v = vv[ps];
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (T::PAIR) {
+          y[e] = v[e];
+        } else {
+          y[e] = activate<ACT>(v[e] + bias4[e]);
+        }
+      }
+      if constexpr (RES) {
+        y[0] += bf16_lo(rv[ps][0]);
+        y[1] += bf16_hi(rv[ps][0]);
+        y[2] += bf16_lo(rv[ps][1]);
+        y[3] += bf16_hi(rv[ps][1]);
+      }
+      const uint32_t m01 = max(__float_as_uint(y[0]) & 0x7FFFFFFFu, __float_as_uint(y[1]) & 0x7FFFFFFFu);
+      const uint32_t m23 = max(__float_as_uint(y[2]) & 0x7FFFFFFFu, __float_as_uint(y[3]) & 0x7FFFFFFFu);
+      amax_bits = ok ? max(amax_bits, max(m01, m23)) : amax_bits;
+      const uint32_t yoff = ok ? (uint32_t)ml * ldy_b + col_y : kOOB;
+      if constexpr (FP8) {
+        const float qs = p.qscale;
+        float z[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[e] = fminf(fmaxf(y[e] * qs, -448.0f), 448.0f);
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(z[0], z[1], 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(z[2], z[3], w, true);
+        __builtin_amdgcn_raw_buffer_store_b32((unsigned)w, y_rs, yoff, 0, 0);
+      } else {
+        u32x2_t w;
+        w[0] = pack_bf16x2(y[0], y[1]);
+        w[1] = pack_bf16x2(y[2], y[3]);
+        __builtin_amdgcn_raw_buffer_store_b64(w, y_rs, yoff, 0, 0);
+      }
+    }
+  };
+
 #pragma unroll
   for (int j = 0; j < T::FM; ++j) {
     const int ml = wm0 + 32 * j + lrow;
-    const bool m_ok = m0 + ml < M;
     float rscale = alpha;
     if constexpr (ROWSTAT) {
-      if (flags & F_ROW_RMS) rscale *= __builtin_amdgcn_rsqf(row_ss[ml] * inv_k + p.eps);
+      if (has_rms) rscale *= __builtin_amdgcn_rsqf(row_ss[ml] * inv_k + p.eps);
     }
-    if (flags & F_ROW_SCALE) rscale *= m_ok ? p.row_scale[(int64_t)b * M + m0 + ml] : 0.0f;
+    if (has_rs) rscale *= (m0 + ml < M) ? p.row_scale[(int64_t)b * M + m0 + ml] : 0.0f;
+    // phase 1: lane's row lrow, columns 32i + 8g + 4*lhalf + e of the wave's block
 #pragma unroll
-    for (int i = 0; i < T::FN; ++i) {
+    for (int i = 0; i < T::FN; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int nl = wn0 + 32 * i + 8 * g + 4 * lhalf;
-        const bool ok = m_ok && (n0 + nl < N);
-        float res[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (flags & F_RESIDUAL) {
-          const uint32_t roff = ok ? (uint32_t)(((int64_t)ml * p.ldr + nl) * 2) : kOOB;
-          const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(r_rs, roff, 0, 0);
-          res[0] = bf16_lo(w[0]);
-          res[1] = bf16_hi(w[0]);
-          res[2] = bf16_lo(w[1]);
-          res[3] = bf16_hi(w[1]);
-        }
-        float y[4];
+        f32x4_t t;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float t = acc[i][j][4 * g + e] * rscale + bias_v[i][g][e];
           if constexpr (T::PAIR) {
-            const float up = acc2[i][j][4 * g + e] * rscale;
-            y[e] = activate<ACT>(t) * up;
+            t[e] = activate<ACT>(acc[i][j][4 * g + e] * rscale) * (acc2[i][j][4 * g + e] * rscale);
           } else {
-            y[e] = activate<ACT>(t);
+            t[e] = acc[i][j][4 * g + e] * rscale;
           }
-          y[e] += res[e];
-          const uint32_t mag = __float_as_uint(y[e]) & 0x7FFFFFFFu;
-          amax_bits = (ok && mag > amax_bits) ? mag : amax_bits;
         }
-        const uint32_t yoff = ok ? (uint32_t)(((int64_t)ml * p.ldy + nl) * esize) : kOOB;
-        if constexpr (FP8) {
-          const float qs = p.qscale;
-          float z[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) z[e] = fminf(fmaxf(y[e] * qs, -448.0f), 448.0f);
-          int w = __builtin_amdgcn_cvt_pk_fp8_f32(z[0], z[1], 0, false);
-          w = __builtin_amdgcn_cvt_pk_fp8_f32(z[2], z[3], w, true);
-          __builtin_amdgcn_raw_buffer_store_b32((unsigned)w, y_rs, yoff, 0, 0);
-        } else {
-          u32x2_t w;
-          w[0] = pack_bf16x2(y[0], y[1]);
-          w[1] = pack_bf16x2(y[2], y[3]);
-          __builtin_amdgcn_raw_buffer_store_b64(w, y_rs, yoff, 0, 0);
-        }
+        *(f32x4_t*)(ep + lrow * EP_LD + 32 * i + 8 * g + 4 * lhalf) = t;
       }
-    }
+    // phase 2 reads what this wave just wrote; a wave's LDS operations complete in order
+    if (has_res)
+      phase2(j, std::integral_constant<bool, true>{});
+    else
+      phase2(j, std::integral_constant<bool, false>{});
   }
 
-  // ---- AMAX: wave max on the |y| bit patterns (integer max keeps NaN), one atomic per
-  // workgroup into the workspace slot; the last workgroup to finish publishes the result
-  // and leaves the workspace zeroed for the next run.  Non-negative floats order like
-  // their bit patterns, so unsigned max is float max.
+  // ---- AMAX ----
+  // Wave max on the |y| bit patterns (integer max keeps NaN; non-negative floats order like
+  // their bit patterns), then a workgroup max.  Each workgroup stores its partial maximum
+  // in its own workspace slot (no contended read-modify-write), waits for the store to be
+  // performed at device scope, and takes a ticket from the counter of its dispatch group
+  // (workgroup id mod 8 = the XCD it runs on).  The workgroup completing a group takes a
+  // ticket from the top counter; the one completing the top counter is last: every slot is
+  // in place, it reduces them and publishes *amax.  Counters are reset by the workgroup
+  // that completes them, so the workspace is zero again when the kernel ends.
   if (flags & F_AMAX) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -497,18 +582,44 @@ void fused_gemm_epilogue(Params p) {
     }
     if (lane == 0) wave_amax[wave] = amax_bits;
     __syncthreads();
+    const uint32_t total = (uint32_t)p.tiles_m * (uint32_t)p.tiles_n * (uint32_t)p.batch;
     if (tid == 0) {
       uint32_t m = wave_amax[0];
 #pragma unroll
       for (int w = 1; w < T::WAVES; ++w) m = wave_amax[w] > m ? wave_amax[w] : m;
-      __hip_atomic_fetch_max(&p.ws[0], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t total = (uint32_t)p.tiles_m * (uint32_t)p.tiles_n * (uint32_t)p.batch;
-      const uint32_t ticket = __hip_atomic_fetch_add(&p.ws[1], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      if (ticket == total - 1) {
-        const uint32_t v = __hip_atomic_load(&p.ws[0], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t wg = blockIdx.x;
+      __hip_atomic_store(&p.ws[kAmaxSlot0 + wg], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);              // slot performed before the ticket
+      const uint32_t grp = wg % kAmaxGroups;
+      const uint32_t gsize = (total + kAmaxGroups - 1u - grp) / kAmaxGroups;
+      const uint32_t ngroups = total < kAmaxGroups ? total : kAmaxGroups;
+      uint32_t* gctr = &p.ws[grp * kAmaxCounterStride];
+      uint32_t* tctr = &p.ws[kAmaxGroups * kAmaxCounterStride];
+      bool last = false;
+      if (__hip_atomic_fetch_add(gctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gsize - 1u) {
+        __hip_atomic_exchange(gctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (__hip_atomic_fetch_add(tctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ngroups - 1u) {
+          __hip_atomic_exchange(tctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          last = true;
+        }
+      }
+      wave_amax[0] = last ? 1u : 0u;
+    }
+    __syncthreads();
+    if (wave_amax[0]) {                                  // uniform: the last workgroup
+      uint32_t mm = 0;
+      for (uint32_t i = (uint32_t)tid; i < total; i += T::NT)
+        mm = max(mm, __hip_atomic_load(&p.ws[kAmaxSlot0 + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) mm = max(mm, (uint32_t)__shfl_xor((int)mm, off));
+      __syncthreads();
+      if (lane == 0) wave_amax[wave] = mm;
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t v = wave_amax[0];
+#pragma unroll
+        for (int w = 1; w < T::WAVES; ++w) v = max(v, wave_amax[w]);
         __hip_atomic_store(p.amax, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&p.ws[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&p.ws[1], 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }

@@ -147,14 +147,15 @@ ge_status_t gemm_epilogue_validate(const ge_desc_t* desc);
  * plan; on failure *out is set to NULL.  Launches nothing. */
 ge_status_t gemm_epilogue_create(const ge_desc_t* desc, ge_handle_t* out);
 
-/* Device scratch the plan needs from the caller, in bytes: 256 when the chain
- * has AMAX (a running maximum and a finished-workgroup counter), else 0. */
+/* Device scratch the plan needs from the caller, in bytes: with AMAX in the
+ * chain 4 * (1024 + number of workgroups) -- nine ticket counters on their own
+ * cache lines plus one partial-maximum slot per workgroup; 0 otherwise. */
 ge_status_t gemm_epilogue_workspace_size(ge_handle_t handle, size_t* bytes);
 
 /* Enqueues the fused GEMM + epilogue on `stream` (a hipStream_t; NULL = the
  * null stream) as ONE kernel launch and returns without waiting.  With AMAX
  * in the chain, *amax is overwritten with max|y| when the kernel completes
- * (the last workgroup to finish publishes it).  Returns GE_ERR_INVALID_ARG for
+ * (the last workgroup to finish reduces the per-workgroup maxima and publishes it).  Returns GE_ERR_INVALID_ARG for
  * a pointer an op needs that is NULL or misaligned (or a too-small AMAX
  * workspace), GE_ERR_HIP if the launch fails.  An empty problem (batch, M or
  * N zero) launches only a one-thread kernel that writes *amax = 0. */
