@@ -61,7 +61,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kGeluC = -2.0f * 1.4426950408889634f * 0.7978845608028654f;
 constexpr float kGeluCubic = 0.044715f;
 
-template <int BM_, int BN_, bool PAIR_, int WPE_>
+template <int BM_, int BN_, bool PAIR_, int WPE_, int PD_ = 2>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr bool PAIR = PAIR_;
@@ -73,6 +73,11 @@ struct Tile {
   // Pipeline: K steps of BK, NS LDS stages in a ring, so the tile of step k+NS-1 is
   // fetched while step k computes (three steps of latency cover for L2 misses).
   static constexpr int BK = 32, NS = 4;
+  // Prefetch distance in steps (tile kt+PD is fetched during step kt).  With PD = NS-1 the
+  // stage refilled right after a barrier was read just before it, so the barrier must also
+  // drain this wave's LDS reads; with PD = NS-2 that stage's last reads were consumed by
+  // MFMAs before the previous barrier and the barrier waits for the next tile only.
+  static constexpr int PD = PD_;
   static constexpr int GROUPS = BK / 16;             // 16-deep MFMA groups per step
   // One LDS stage: A as [BM][BK] (64-byte rows), then each B operand as [BK][BN].
   static constexpr int A_ROWB = BK * 2;
@@ -94,7 +99,8 @@ struct Tile {
   static_assert(A_LOADS >= 1 && A_BYTES % (1024 * WAVES) == 0, "A loads must divide over the waves");
   static_assert(B_LOADS >= 1 && (NB * B_LOADS_PER_OP) % WAVES == 0, "B loads must divide over the waves");
   static_assert(B_LOADS_PER_OP % B_LOADS == 0 || B_LOADS % B_LOADS_PER_OP == 0, "one operand per load");
-  static_assert((NS - 2) * LOADS < 64, "vmcnt range");
+  static_assert((PD - 1) * LOADS < 64, "vmcnt range");
+  static_assert(PD == NS - 1 || PD == NS - 2, "prefetch distance");
 };
 
 using T256 = Tile<256, 256, false, 1>;
@@ -374,7 +380,7 @@ void fused_gemm_epilogue(Params p) {
     }
   };
   // One K step on stage S (tile kt), entered with the fragments of its first group in f0:
-  // start the direct loads of tile kt+NS-1 into the stage freed by the previous step, run
+  // start the direct loads of tile kt+PD into the stage it maps to (freed earlier), run
   // the groups with the following group's fragments in flight, read the last group's
   // fragments, wait until tile kt+1 has landed (later tiles stay in flight), meet the other
   // waves at the barrier, then run the last group while the first fragments of tile kt+1
@@ -385,15 +391,18 @@ void fused_gemm_epilogue(Params p) {
   auto k_step = [&](auto s_c, int kt) {
     constexpr int S = decltype(s_c)::value;
     const unsigned char* cur = stage(std::integral_constant<int, S>{});
-    issue_loads((kt + T::NS - 1) * T::BK, stage(std::integral_constant<int, S + T::NS - 1>{}));
+    issue_loads((kt + T::PD) * T::BK, stage(std::integral_constant<int, S + T::PD>{}));
     static_assert(T::GROUPS == 2, "two groups per step");
     read_frags(cur, 1, f1);
     mfmas(f0);
     interleave(true);
     // Cross-wave facts the barrier publishes: this wave's direct loads of tile kt+1 have
-    // landed in LDS, and its fragment reads of this stage have returned (the stage is
-    // refilled one step later).  No memory fence: the later tiles stay in flight.
-    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((T::NS - 2) * T::LOADS));
+    // landed in LDS (and, at distance NS-1, its fragment reads of this stage, refilled right
+    // after the barrier, have returned).  No memory fence: later tiles stay in flight.
+    if constexpr (T::PD == T::NS - 1)
+      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((T::PD - 1) * T::LOADS));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((T::PD - 1) * T::LOADS));
     __builtin_amdgcn_s_barrier();
     read_frags(stage(std::integral_constant<int, S + 1>{}), 0, f0);
     mfmas(f1);
@@ -407,8 +416,8 @@ void fused_gemm_epilogue(Params p) {
   int kt = nk - nsteps;
   issue_loads((kt + 0) * T::BK, stage(S0{}));
   issue_loads((kt + 1) * T::BK, stage(S1{}));
-  issue_loads((kt + 2) * T::BK, stage(S2{}));
-  __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((T::NS - 2) * T::LOADS));
+  if constexpr (T::PD == 3) issue_loads((kt + 2) * T::BK, stage(S2{}));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((T::PD - 1) * T::LOADS));
   __builtin_amdgcn_s_barrier();
   read_frags(stage(S0{}), 0, f0);
   for (; kt < nk; kt += T::NS) {
