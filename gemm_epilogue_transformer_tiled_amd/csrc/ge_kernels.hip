@@ -11,26 +11,26 @@
 // superoptimizer write-up's section 9 is gathered from the A operand while it
 // is staged, so no separate scale kernel or round trip of S is needed.
 //
-// Mainloop design (per workgroup of 4 waves):
-//   * A tile [BM x 64] and B tile [64 x BN] (two B tiles when pairwise) per K
-//     step, loaded from HBM with 16-byte buffer loads.  Out-of-range rows,
-//     columns and K chunks are given an offset past the buffer extent, so the
-//     hardware returns zeros (and drops stores) -- ragged tails need no branches.
-//   * B is row-major [K, N] (N contiguous), but the matrix core wants K packed
-//     inside each lane's registers for both operands.  Each thread loads an
-//     8(k) x 8(n) block of B and transposes it in registers with byte permutes,
-//     so LDS holds B as [n][k] exactly like A's [m][k].
-//   * LDS rows are 128 bytes (64 bf16 of K); the eight 16-byte chunks of row r
-//     are XOR-swizzled by (r ^ r>>3) & 7 so fragment reads and transposed
-//     writes hit distinct banks.  Two LDS stages: the next tile is fetched into
-//     registers while the matrix cores work on the current stage, then written
-//     to the other stage; one barrier per K step.
-//   * v_mfma_f32_32x32x16_bf16 with the operands swapped (B fragment as the
-//     first source) so that each lane's accumulators hold four consecutive
-//     output columns of one output row: the epilogue then loads bias/residual
-//     and stores Y with 8-byte (bf16) or 4-byte (fp8) vector accesses.
-//   * Workgroup ids are remapped so each XCD (own L2) receives a contiguous run
-//     of tiles, which are then walked in groups of 8 tile-rows for L2 reuse.
+// Mainloop design (per workgroup of 4 waves, 2 x 2 over the output tile):
+//   * Operands reach LDS with direct global->LDS buffer loads (16 bytes per lane, 1 KB per
+//     instruction, no register staging).  Out-of-range rows, columns and K chunks are
+//     given an offset past the buffer extent, so the hardware returns zeros -- ragged
+//     tails need no branches.
+//   * K advances in steps of 32.  A ([M, K], K contiguous) is staged two steps at a time
+//     as [BM][64] with 128-byte rows, so every cache line fetched from L2 is used whole
+//     and fetched once; B ([K, N], N contiguous) is staged per step as [32][BN], row-major
+//     as it sits in memory.  Two A slots and a ring of four B stages let the loads of
+//     step k+2 run while step k computes; one barrier per step.
+//   * 16-byte chunks are XOR-swizzled within each LDS row so that fragment reads are free
+//     of bank conflicts while the direct loads still write whole 1-KB blocks.
+//   * A fragments are plain 16-byte LDS reads; B fragments (K packed inside each lane, as
+//     the matrix core wants) come from transposing LDS reads (ds_read_b64_tr_b16).
+//   * v_mfma_f32_32x32x16_bf16 with the operands swapped (B fragment as the first source)
+//     so that each lane's accumulators hold four consecutive output columns of one output
+//     row.  The epilogue stages each 32-row block through LDS once so that bias/residual
+//     loads and Y stores cover whole rows.
+//   * Workgroup ids are remapped so each XCD (own L2) receives a contiguous run of tiles,
+//     which are then walked in groups of 8 tile-rows for L2 reuse.
 #include <type_traits>
 
 #include "ge_internal.h"
@@ -61,7 +61,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kGeluC = -2.0f * 1.4426950408889634f * 0.7978845608028654f;
 constexpr float kGeluCubic = 0.044715f;
 
-template <int BM_, int BN_, bool PAIR_, int WPE_, int PD_ = 2>
+template <int BM_, int BN_, bool PAIR_, int WPE_>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr bool PAIR = PAIR_;
@@ -70,37 +70,37 @@ struct Tile {
   static constexpr int WM = BM / 2, WN = BN / 2;     // per-wave output tile
   static constexpr int FM = WM / 32, FN = WN / 32;   // 32x32 MFMA blocks per wave
   static constexpr int NB = PAIR ? 2 : 1;            // B operands
-  // Pipeline: K steps of BK, NS LDS stages in a ring, so the tile of step k+NS-1 is
-  // fetched while step k computes (three steps of latency cover for L2 misses).
-  static constexpr int BK = 32, NS = 4;
-  // Prefetch distance in steps (tile kt+PD is fetched during step kt).  With PD = NS-1 the
-  // stage refilled right after a barrier was read just before it, so the barrier must also
-  // drain this wave's LDS reads; with PD = NS-2 that stage's last reads were consumed by
-  // MFMAs before the previous barrier and the barrier waits for the next tile only.
-  static constexpr int PD = PD_;
+  // Pipeline: K steps of BK = 32.  B tiles ([BK][BN] per operand) go through a ring of
+  // NS = 4 LDS stages; A tiles are staged two steps at a time ([BM][64], 128-byte rows, so
+  // every fetched cache line is used whole) in two slots.  The tiles of step k+2 are
+  // fetched while step k computes.
+  static constexpr int BK = 32, NS = 4, PD = 2;
   static constexpr int GROUPS = BK / 16;             // 16-deep MFMA groups per step
-  // One LDS stage: A as [BM][BK] (64-byte rows), then each B operand as [BK][BN].
-  static constexpr int A_ROWB = BK * 2;
+  static constexpr int A_ROWB = 128;                 // one A row: 64 K values
   static constexpr int A_CHUNKS = A_ROWB / 16;
-  static constexpr int A_BYTES = BM * A_ROWB;
+  static constexpr int A_SLOT = BM * A_ROWB;         // two steps of A
   static constexpr int B_ROWB = BN * 2;              // bytes per staged B row
   static constexpr int B_CHUNKS = B_ROWB / 16;       // 16-byte chunks per B row
-  static constexpr int B_BYTES = BK * B_ROWB;        // one B operand
-  static constexpr int STAGE = A_BYTES + NB * B_BYTES;
-  static constexpr int LDS = NS * STAGE;
+  static constexpr int B_BYTES = BK * B_ROWB;        // one B operand, one step
+  static constexpr int B_STAGE = NB * B_BYTES;
+  // Epilogue: each wave stages a 32-row block of fp32 rows (WN + 4 floats) in LDS; two
+  // waves share an A slot, which is sized to hold them.
+  static constexpr int EP_LD = WN + 4;
+  static constexpr int EP_WAVE_BYTES = 32 * EP_LD * 4;
+  static constexpr int A_ALLOC = A_SLOT > 2 * EP_WAVE_BYTES ? A_SLOT : 2 * EP_WAVE_BYTES;
+  static constexpr int LDS = 2 * A_ALLOC + NS * B_STAGE;
   // Direct global->LDS loads: one instruction moves 1 KB (64 lanes x 16 bytes).
   static constexpr int A_ROWS_PER_LOAD = 1024 / A_ROWB;
-  static constexpr int A_LOADS = A_BYTES / 1024 / WAVES;          // per wave per step
+  static constexpr int A_LOADS = A_SLOT / 1024 / WAVES;            // per wave per A slot
   static constexpr int B_ROWS_PER_LOAD = 1024 / B_ROWB;
   static constexpr int B_LOADS_PER_OP = BK / B_ROWS_PER_LOAD;     // per operand per step
   static constexpr int B_LOADS = NB * B_LOADS_PER_OP / WAVES;     // per wave per step
-  static constexpr int LOADS = A_LOADS + B_LOADS;                 // per wave per step
   static_assert(BM % 64 == 0 && BN % 64 == 0, "tile must split into 2x2 waves of 32x32 blocks");
-  static_assert(A_LOADS >= 1 && A_BYTES % (1024 * WAVES) == 0, "A loads must divide over the waves");
+  static_assert(A_LOADS >= 1 && A_SLOT % (1024 * WAVES) == 0, "A loads must divide over the waves");
   static_assert(B_LOADS >= 1 && (NB * B_LOADS_PER_OP) % WAVES == 0, "B loads must divide over the waves");
   static_assert(B_LOADS_PER_OP % B_LOADS == 0 || B_LOADS % B_LOADS_PER_OP == 0, "one operand per load");
-  static_assert((PD - 1) * LOADS < 64, "vmcnt range");
-  static_assert(PD == NS - 1 || PD == NS - 2, "prefetch distance");
+  static_assert(A_LOADS + B_LOADS < 64, "vmcnt range");
+  static_assert(LDS + 1024 + 64 <= 160 * 1024, "LDS budget of one workgroup");
 };
 
 using T256 = Tile<256, 256, false, 1>;
@@ -114,17 +114,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// A rows are 2*BK bytes (CHUNKS 16-byte chunks).  Chunk c of row r lives at chunk
-// c ^ swz_a(r).  The swizzle uses only r mod 16, so it is the same for every 32-row MFMA
-// block; 32 consecutive rows read at one logical chunk land on distinct banks both for
-// 128-byte and 256-byte LDS cycles.
-template <int CHUNKS>
+// A rows are 128 bytes (eight 16-byte chunks).  Chunk c of row r lives at chunk
+// c ^ swz_a(r).  The swizzle uses only r mod 32, so it is the same for every 32-row MFMA
+// block; 16 consecutive rows read at one logical chunk land on distinct banks for both
+// 128-byte and 256-byte LDS cycles (even rows take all eight chunks, odd rows too).
 __device__ __forceinline__ uint32_t swz_a(uint32_t row) {
-  if constexpr (CHUNKS == 4) {
-    return ((row >> 1) ^ (row >> 2)) & 3u;
-  } else {
-    return (row & 7u) ^ ((row >> 3) & 3u);
-  }
+  return (row & 7u) ^ ((row >> 3) & 3u);
 }
 
 // B rows ([k][n], 2*BN bytes).  Chunk c of row k lives at chunk c ^ swz_b(k).  A
@@ -184,24 +179,48 @@ __device__ __forceinline__ void tile_coords(int wg, const Params& p, int& b, int
   tn = in_g / gsize;
 }
 
+// Scheduling recipe for one 16-deep MFMA group of MF instructions: after MFMA m come
+// ceil(NL / MF) of the step's NL direct loads (VMEM = 0x010, while any remain) and, for
+// m < RD, one of the next group's fragment reads (DS read = 0x100); MFMA = 0x008.
+template <int MF, int NL, int RD, int M = 0>
+__device__ __forceinline__ void sched_group() {
+  if constexpr (M < MF) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int per = (NL + MF - 1) / MF;
+    constexpr int left = NL - M * per;
+    constexpr int n = left < per ? left : per;
+    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x010, n, 0);
+    if constexpr (M < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    sched_group<MF, NL, RD, M + 1>();
+  }
+}
+
 template <class T, int ACT, bool FP8, bool ROWSTAT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(T::WPE, T::WPE)))
 void fused_gemm_epilogue(Params p) {
-  // The LDS stages are distinct arrays, so the compiler can tell that the direct loads
-  // filling one stage never alias the fragment reads of another.
-  __shared__ __attribute__((aligned(1024))) unsigned char stage0[T::STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char stage1[T::STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char stage2[T::STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char stage3[T::STAGE];
+  // The LDS stages and slots are distinct arrays, so the compiler can tell that the direct
+  // loads filling one never alias the fragment reads of another.
+  __shared__ __attribute__((aligned(1024))) unsigned char aslot0[T::A_ALLOC];
+  __shared__ __attribute__((aligned(1024))) unsigned char aslot1[T::A_ALLOC];
+  __shared__ __attribute__((aligned(1024))) unsigned char bstage0[T::B_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char bstage1[T::B_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char bstage2[T::B_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char bstage3[T::B_STAGE];
   __shared__ float row_ss[ROWSTAT ? T::BM : 1];
   __shared__ uint32_t wave_amax[T::WAVES];
-  static_assert(T::NS == 4, "four stage arrays");
-  auto stage = [&](auto s_c) -> unsigned char* {
+  static_assert(T::NS == 4, "four B stage arrays");
+  // B stage of step s, A slot of step s (two consecutive steps share a slot).
+  auto bstage = [&](auto s_c) -> unsigned char* {
     constexpr int S = decltype(s_c)::value % T::NS;
-    if constexpr (S == 0) return stage0;
-    else if constexpr (S == 1) return stage1;
-    else if constexpr (S == 2) return stage2;
-    else return stage3;
+    if constexpr (S == 0) return bstage0;
+    else if constexpr (S == 1) return bstage1;
+    else if constexpr (S == 2) return bstage2;
+    else return bstage3;
+  };
+  auto aslot = [&](auto s_c) -> unsigned char* {
+    constexpr int S = decltype(s_c)::value % T::NS;
+    if constexpr (S / 2 == 0) return aslot0;
+    else return aslot1;
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
@@ -227,19 +246,15 @@ void fused_gemm_epilogue(Params p) {
   if constexpr (T::PAIR) b2_rs = make_rsrc(p.B2 + b * p.sb + n0, b_ext);
 
   // ---- direct global->LDS loads: per-lane source offsets, fixed for the whole K loop ----
-  // A load t of this wave fills A_ROWS_PER_LOAD staged rows (1 KB): lane -> row
-  // lane/A_CHUNKS of the load, physical chunk lane%A_CHUNKS, so it fetches logical chunk
-  // (lane%A_CHUNKS) ^ swz_a(row).  Rows past M fall outside the resource extent
-  // (lda >= K); K-tail chunks get the out-of-range offset.
-  const uint32_t ldb2 = (uint32_t)p.ldb * 2u;
-  uint32_t a_voff[T::A_LOADS], a_kcol[T::A_LOADS];
-#pragma unroll
-  for (int t = 0; t < T::A_LOADS; ++t) {
-    const uint32_t row = (uint32_t)(wave * T::A_LOADS + t) * T::A_ROWS_PER_LOAD + (uint32_t)(lane / T::A_CHUNKS);
-    const uint32_t lchunk = (uint32_t)(lane % T::A_CHUNKS) ^ swz_a<T::A_CHUNKS>(row);
-    a_voff[t] = row * (uint32_t)p.lda * 2u + lchunk * 16u;
-    a_kcol[t] = lchunk * 8u;
-  }
+  // A load t of this wave fills slot rows 8u .. 8u+7 (1 KB), u = wave * A_LOADS + t:
+  // lane -> row 8u + lane/8, physical chunk lane%8, so it fetches logical chunk
+  // (lane%8) ^ swz_a(row) = a_x ^ (u & 3), i.e. K columns 8 * that chunk of the slot's 64.
+  // Rows past M fall outside the resource extent (lda >= K); chunks outside [0, K) get the
+  // out-of-range offset.
+  static_assert(T::A_ROWS_PER_LOAD == 8 && T::A_CHUNKS == 8, "one 128-byte row per 8 lanes");
+  const uint32_t lda2 = (uint32_t)p.lda * 2u, ldb2 = (uint32_t)p.ldb * 2u;
+  const uint32_t a_x = (uint32_t)((lane & 7) ^ (lane >> 3));
+  const uint32_t a_row = (uint32_t)(lane >> 3) * lda2;
   // B load t fills B_ROWS_PER_LOAD rows of one operand: lane -> row lane/B_CHUNKS (within
   // the load), physical chunk lane%B_CHUNKS, logical chunk ^ swz_b(row).  Rows past K fall
   // outside the extent; a column block past N gets the out-of-range offset.
@@ -252,21 +267,29 @@ void fused_gemm_epilogue(Params p) {
     b_voff[t] = (n0 + (int)lchunk * 8 < N) ? row * ldb2 + lchunk * 16u : kOOB;
   }
 
-  auto issue_loads = [&](int k0, unsigned char* st) {
-    const bool live = k0 >= 0;     // k0 < 0: an all-zero leading tile
+  // A slot for steps k0/BK and k0/BK + 1.  k0 may be negative (leading all-zero steps):
+  // one unsigned compare sends every chunk outside [0, K) out of range.
+  auto issue_a = [&](int k0, unsigned char* slot) {
 #pragma unroll
     for (int t = 0; t < T::A_LOADS; ++t) {
-      const uint32_t off = (live & (k0 + (int)a_kcol[t] < K)) ? a_voff[t] + (uint32_t)k0 * 2u : kOOB;
+      const uint32_t u = (uint32_t)(wave * T::A_LOADS + t);          // wave-uniform
+      const uint32_t c = a_x ^ (u & 3u);
+      const uint32_t off = ((uint32_t)(k0 + (int)(c * 8u)) < (uint32_t)K)
+                               ? a_row + u * 8u * lda2 + c * 16u + (uint32_t)k0 * 2u : kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          a_rs, (__attribute__((address_space(3))) void*)(st + (wave * T::A_LOADS + t) * 1024), 16, off, 0, 0, 0);
+          a_rs, (__attribute__((address_space(3))) void*)(slot + (wave * T::A_LOADS + t) * 1024), 16, off, 0, 0, 0);
     }
+  };
+  // B stage of the step starting at K column k0.
+  auto issue_b = [&](int k0, unsigned char* st) {
+    const bool live = k0 >= 0;     // k0 < 0: an all-zero leading step
 #pragma unroll
     for (int t = 0; t < T::B_LOADS; ++t) {
       const int gblk = wave * T::B_LOADS + t;           // wave-uniform
       const int op = gblk / T::B_LOADS_PER_OP;
       const int blk = gblk % T::B_LOADS_PER_OP;
       const uint32_t off = live ? b_voff[t] + (uint32_t)k0 * ldb2 : kOOB;
-      unsigned char* dst = st + T::A_BYTES + op * T::B_BYTES + blk * 1024;
+      unsigned char* dst = st + op * T::B_BYTES + blk * 1024;
       if (T::PAIR && op == 1)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(b2_rs, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
       else
@@ -275,14 +298,15 @@ void fused_gemm_epilogue(Params p) {
   };
 
   // ---- fragment addressing ----
-  // A (second MFMA source): lane reads row wm0 + 32j + lane%32, logical chunk 2g + lane/32
-  // (eight consecutive K); the swizzle depends on lane%32 only, so j is an immediate offset.
+  // A (second MFMA source): for group g of the step in slot half h, lane reads row
+  // wm0 + 32j + lane%32, logical chunk 4h + 2g + lane/32 (eight consecutive K); the swizzle
+  // depends on lane%32 only, so j is an immediate offset.
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int wm0 = wave_m * T::WM, wn0 = wave_n * T::WN;
-  uint32_t a_frag[T::GROUPS];
+  uint32_t a_frag[2 * T::GROUPS];
 #pragma unroll
-  for (int g = 0; g < T::GROUPS; ++g)
-    a_frag[g] = (uint32_t)(wm0 + lrow) * T::A_ROWB + (((uint32_t)(2 * g + lhalf) ^ swz_a<T::A_CHUNKS>(lrow)) << 4);
+  for (int hg = 0; hg < 2 * T::GROUPS; ++hg)
+    a_frag[hg] = (uint32_t)(wm0 + lrow) * T::A_ROWB + (((uint32_t)(2 * hg + lhalf) ^ swz_a(lrow)) << 4);
   // B (first MFMA source) through 16-lane transpose reads: in each group of 16 lanes, lane s
   // points at row k0 + s/4 and columns nb + 4(s%4) .. +3, and receives column nb + s of rows
   // k0 .. k0+3.  Two reads (rows +0..3, +4..7) give the eight K values of A's lane layout.
@@ -295,7 +319,7 @@ void fused_gemm_epilogue(Params p) {
     for (int i = 0; i < T::FN; ++i) {
       const uint32_t ncol = (uint32_t)(wn0 + 32 * i + 16 * (grp & 1) + 4 * (sl & 3));
       const uint32_t lchunk = ncol >> 3;
-      b_frag[op][i] = (uint32_t)(T::A_BYTES + op * T::B_BYTES) + kl * T::B_ROWB +
+      b_frag[op][i] = (uint32_t)(op * T::B_BYTES) + kl * T::B_ROWB +
                       ((lchunk ^ swz_b<T::B_CHUNKS>(kl)) << 4) + (ncol & 7u) * 2u;
     }
 
@@ -322,15 +346,15 @@ void fused_gemm_epilogue(Params p) {
     bf16x8_t b[T::NB][T::FN];
   };
   typedef __attribute__((address_space(3))) v4bf16_t lds_v4bf16;
-  auto read_frags = [&](const unsigned char* st, int g, Frags& f) {
+  auto read_frags = [&](const unsigned char* as, const unsigned char* bs, int h, int g, Frags& f) {
 #pragma unroll
     for (int j = 0; j < T::FM; ++j)
-      f.a[j] = *(const bf16x8_t*)(st + a_frag[g] + j * 32 * T::A_ROWB);
+      f.a[j] = *(const bf16x8_t*)(as + a_frag[h * T::GROUPS + g] + j * 32 * T::A_ROWB);
 #pragma unroll
     for (int op = 0; op < T::NB; ++op)
 #pragma unroll
       for (int i = 0; i < T::FN; ++i) {
-        const unsigned char* q = st + b_frag[op][i] + 16 * g * T::B_ROWB;
+        const unsigned char* q = bs + b_frag[op][i] + 16 * g * T::B_ROWB;
         const v4bf16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf16*)(q));
         const v4bf16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf16*)(q + 4 * T::B_ROWB));
         f.b[op][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -360,66 +384,58 @@ void fused_gemm_epilogue(Params p) {
       }
     }
   };
-  // Interleave the fragment reads of the next 16-deep group with this group's MFMAs
-  // (DS read = 0x100, MFMA = 0x008 in the scheduling-group masks).  The first group of a
-  // step also carries the step's direct loads (VMEM = 0x010), in pairs after its first MFMAs.
   constexpr int READS_PER_GROUP = T::FM + 2 * T::NB * T::FN;
   constexpr int MFMAS_PER_GROUP = T::FM * T::FN * T::NB;
-  static_assert(T::LOADS % 2 == 0, "loads are slotted in pairs");
-  constexpr bool LOAD_PAIRS = T::LOADS / 2 <= MFMAS_PER_GROUP;
-  auto interleave = [&](bool with_loads) {
-#pragma unroll
-    for (int m = 0; m < MFMAS_PER_GROUP; ++m) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if constexpr (LOAD_PAIRS) {
-        if (with_loads && m < T::LOADS / 2) __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);
-      } else {
-        if (with_loads && m == 0) __builtin_amdgcn_sched_group_barrier(0x010, T::LOADS, 0);
-      }
-      if (m < READS_PER_GROUP) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-  };
-  // One K step on stage S (tile kt), entered with the fragments of its first group in f0:
-  // start the direct loads of tile kt+PD into the stage it maps to (freed earlier), run
-  // the groups with the following group's fragments in flight, read the last group's
-  // fragments, wait until tile kt+1 has landed (later tiles stay in flight), meet the other
-  // waves at the barrier, then run the last group while the first fragments of tile kt+1
-  // are read -- the matrix cores stay busy across the barrier.  Loads are issued even past
-  // the last tile: those offsets are all out of range, so they only write zeros into stages
-  // whose reads are discarded (no branch in the loop body).
+  // One K step s (tile kt), entered with the fragments of its first group in f0:
+  //   * start the direct loads of step kt+2 -- its B stage, and on even steps the A slot of
+  //     steps kt+2 and kt+3.  Both were freed before the previous barrier: the B stage held
+  //     step kt-2, the A slot steps kt-2 and kt-1, whose last fragment reads (issued before
+  //     the previous barrier) were waited for there;
+  //   * run group 0 with group 1's fragments in flight;
+  //   * wait until step kt+1 has landed: on an even step every load but this step's; on an
+  //     odd step every load but this step's B loads (the A slot of kt+1 came with the
+  //     previous step's loads), and also this wave's LDS reads of the A slot, which the
+  //     next step refills;
+  //   * meet the other waves at the barrier, then run group 1 while the first fragments of
+  //     step kt+1 are read -- the matrix cores stay busy across the barrier.
+  // Loads are issued even past the last step: those offsets are all out of range, so they
+  // only write zeros into stages whose reads are discarded (no branch in the loop body).
   Frags f0, f1;
   auto k_step = [&](auto s_c, int kt) {
     constexpr int S = decltype(s_c)::value;
-    const unsigned char* cur = stage(std::integral_constant<int, S>{});
-    issue_loads((kt + T::PD) * T::BK, stage(std::integral_constant<int, S + T::PD>{}));
+    constexpr bool EVEN = S % 2 == 0;
+    using Cur = std::integral_constant<int, S>;
+    using Next = std::integral_constant<int, S + 1>;
+    using Fill = std::integral_constant<int, S + 2>;
+    issue_b((kt + 2) * T::BK, bstage(Fill{}));
+    if constexpr (EVEN) issue_a((kt + 2) * T::BK, aslot(Fill{}));
     static_assert(T::GROUPS == 2, "two groups per step");
-    read_frags(cur, 1, f1);
+    read_frags(aslot(Cur{}), bstage(Cur{}), S % 2, 1, f1);
     mfmas(f0);
-    interleave(true);
-    // Cross-wave facts the barrier publishes: this wave's direct loads of tile kt+1 have
-    // landed in LDS (and, at distance NS-1, its fragment reads of this stage, refilled right
-    // after the barrier, have returned).  No memory fence: later tiles stay in flight.
-    if constexpr (T::PD == T::NS - 1)
-      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((T::PD - 1) * T::LOADS));
+    sched_group<MFMAS_PER_GROUP, EVEN ? T::A_LOADS + T::B_LOADS : T::B_LOADS, READS_PER_GROUP>();
+    // No memory fence: the later loads stay in flight across the barrier.
+    if constexpr (EVEN)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(T::A_LOADS + T::B_LOADS));
     else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm((T::PD - 1) * T::LOADS));
+      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(T::B_LOADS));
     __builtin_amdgcn_s_barrier();
-    read_frags(stage(std::integral_constant<int, S + 1>{}), 0, f0);
+    read_frags(aslot(Next{}), bstage(Next{}), (S + 1) % 2, 0, f0);
     mfmas(f1);
-    interleave(false);
+    sched_group<MFMAS_PER_GROUP, 0, READS_PER_GROUP>();
   };
 
-  // Step count rounded up to a multiple of NS with leading all-zero tiles, so the loop
-  // always runs whole stage rings and the accumulators have one exit path.
+  // Step count rounded up to a multiple of NS with leading all-zero steps, so the loop
+  // always runs whole stage rings, A slots pair steps (0,1) and (2,3) of each ring, and the
+  // accumulators have one exit path.
   const int nk = (K + T::BK - 1) / T::BK;
   const int nsteps = (nk + T::NS - 1) / T::NS * T::NS;
   int kt = nk - nsteps;
-  issue_loads((kt + 0) * T::BK, stage(S0{}));
-  issue_loads((kt + 1) * T::BK, stage(S1{}));
-  if constexpr (T::PD == 3) issue_loads((kt + 2) * T::BK, stage(S2{}));
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm((T::PD - 1) * T::LOADS));
+  issue_a(kt * T::BK, aslot(S0{}));
+  issue_b(kt * T::BK, bstage(S0{}));
+  issue_b((kt + 1) * T::BK, bstage(S1{}));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(T::B_LOADS));
   __builtin_amdgcn_s_barrier();
-  read_frags(stage(S0{}), 0, f0);
+  read_frags(aslot(S0{}), bstage(S0{}), 0, 0, f0);
   for (; kt < nk; kt += T::NS) {
     k_step(S0{}, kt);
     k_step(S1{}, kt + 1);
@@ -454,14 +470,12 @@ void fused_gemm_epilogue(Params p) {
   const float alpha = (flags & F_SCALE) ? p.alpha : 1.0f;
   const float inv_k = K > 0 ? 1.0f / (float)K : 0.0f;
 
-  constexpr int EP_LD = T::WN + 4;                      // floats per LDS row
-  constexpr int EP_WAVE_BYTES = 32 * EP_LD * 4;
-  static_assert(EP_WAVE_BYTES <= T::STAGE, "one wave's epilogue block per stage");
+  constexpr int EP_LD = T::EP_LD;                       // floats per LDS row
   constexpr int LPR = T::WN / 4;                        // phase-2 lanes per row
   constexpr int RPP = 64 / LPR;                         // rows per phase-2 pass
   constexpr int PASSES = 32 / RPP;
   __syncthreads();                                      // every wave is done with the stages
-  float* ep = (float*)(wave == 0 ? stage0 : wave == 1 ? stage1 : wave == 2 ? stage2 : stage3);
+  float* ep = (float*)((wave < 2 ? aslot0 : aslot1) + (wave & 1) * T::EP_WAVE_BYTES);
 
   const int p2_row = lane / LPR, p2_col = 4 * (lane % LPR);
   const int gcol = n0 + wn0 + p2_col;
