@@ -6,10 +6,16 @@ workload's seeded synthetic inputs, already resident in HBM.  The default
 workload is the batched one (batch 16 x 1024^3, alpha 1.25, column bias, ReLU,
 AMAX over all outputs, bf16 output); ``--config c1..c5`` selects another.
 
+The K timed steps run back to back on one stream, issued either eagerly or as one
+replay of a HIP graph holding the K launches (``--launch``; by default the faster
+on an untimed probe, named in the output).
+
 Prints ONE JSON line:
   value      whole-job TFLOP/s = 2*M*N*K*batch (x2 pairwise) / (timed wall time / steps)
-  roofline   the fused kernel's achieved TFLOP/s from per-launch HIP events on its
-             stream, against the MI355X dense bf16 MFMA peak (2.5 PFLOP/s)
+  roofline   the fused kernel's achieved TFLOP/s over its average launch duration (HIP
+             events on its stream around the back-to-back steps) against the MI355X dense
+             bf16 MFMA peak (2.5 PFLOP/s); traffic = HBM bytes per launch from the
+             FETCH_SIZE / WRITE_SIZE counters, when they were taken on this kernel source
   cpu_baseline  the float64 oracle on this host's cores over a bounded sample
   epilogue_overhead_pct  fused kernel time over the same kernel instance with the
              chain reduced to a plain bf16 store (pairwise: the bare product g*u)
@@ -17,6 +23,7 @@ Prints ONE JSON line:
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,9 +37,17 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 METRIC = "fused GEMM-epilogue TFLOP/s (% of MI355X bf16 MFMA peak) per config"
 
-# HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE of this kernel at this workload,
-# scaled by the copy-kernel calibration factor; None until counters are taken for the current kernel.
-MEASURED_TRAFFIC = {}
+# HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE (x2.0) + WRITE_SIZE (x1.0) of the fused
+# kernel at each workload; the factors scale the counters to the bytes of a plain 1 GiB device
+# copy.  Valid only for the kernel source they were taken on (sha256 prefix below).
+MEASURED_TRAFFIC_SOURCE = "0a4fc6489d185a05"
+MEASURED_TRAFFIC = {"c1": 1043223, "c2": 101168759, "c3": 3053782077, "c4": 537491895, "c5": 1833042778}
+
+
+def kernel_source_hash():
+    path = os.path.join(ROOT, "gemm_epilogue_transformer_tiled_amd", "csrc", "ge_kernels.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 def parse():
@@ -41,6 +56,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--launch", default="auto", choices=["auto", "eager", "graph"],
+                    help="issue the timed steps eagerly or as one HIP-graph replay (auto: the faster on a probe)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle timing sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bare", action="store_true", help="skip the bare-GEMM comparison")
@@ -62,31 +79,67 @@ def calibrate_copy(mib):
     print(json.dumps({"copy_bytes_read_per_launch": n * 4, "copy_bytes_written_per_launch": n * 4, "launches": 10}))
 
 
-def time_launches(prob, steps, warmup):
-    """(ms per step over the bracketed region, mean per-launch ms from event pairs)."""
+def _region_ms(fn, stream):
+    """Elapsed ms of fn() between two HIP events on `stream`, device synchronised both sides."""
     import torch
 
+    r0 = torch.cuda.Event(enable_timing=True)
+    r1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    r0.record(stream)
+    fn()
+    r1.record(stream)
+    torch.cuda.synchronize()
+    return r0.elapsed_time(r1)
+
+
+def _graph_of(prob, steps):
+    import torch
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(steps):
+            prob.run()
+    graph.replay()                       # untimed first replay
+    torch.cuda.synchronize()
+    return graph
+
+
+def time_launches(prob, steps, warmup, launch="auto"):
+    """Times `steps` back-to-back launches with inputs resident in HBM.
+
+    Two ways to issue the steps: eagerly (one Python call, one hipLaunchKernel per step) or
+    as one replay of a HIP graph holding the `steps` launches.  "auto" picks the faster on
+    an untimed probe of 10 steps each (graphs remove the host launch cost that bounds small
+    kernels; eager launches avoid the graph's inter-node overhead on long ones), then times
+    the `steps` steps in that mode.  Returns (ms per step, mode, probe {mode: ms per step}).
+    """
+    import torch
+
+    stream = torch.cuda.current_stream()
     for _ in range(warmup):
         prob.run()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    region0 = torch.cuda.Event(enable_timing=True)
-    region1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    region0.record(stream)
-    for i in range(steps):
-        starts[i].record(stream)
-        prob.run(stream.cuda_stream)
-        ends[i].record(stream)
-    region1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = region0.elapsed_time(region1)
-    per_launch = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    per_launch.sort()
-    mean_ms = sum(per_launch) / len(per_launch)
-    return total_ms / steps, mean_ms, per_launch[len(per_launch) // 2]
+
+    def eager(n):
+        for _ in range(n):
+            prob.run(stream.cuda_stream)
+
+    probe = {}
+    if launch == "auto":
+        n = min(steps, 10)
+        probe["eager"] = _region_ms(lambda: eager(n), stream) / n
+        g = _graph_of(prob, n)
+        probe["graph"] = _region_ms(g.replay, stream) / n
+        del g
+        launch = min(probe, key=probe.get)
+    if launch == "graph":
+        g = _graph_of(prob, steps)
+        ms = _region_ms(g.replay, stream) / steps
+        del g
+    else:
+        ms = _region_ms(lambda: eager(steps), stream) / steps
+    return ms, launch, {k: round(v, 6) for k, v in probe.items()}
 
 
 def bare_chain(w):
@@ -148,10 +201,12 @@ def main():
     w = workloads.WORKLOADS[args.config]
     inputs = workloads.generate(w)
     prob = runner.prepare(w, inputs)
-    ms_step, launch_ms, launch_med = time_launches(prob, args.steps, args.warmup)
+    ms_step, mode, probe = time_launches(prob, args.steps, args.warmup, args.launch)
     flops = w.flops()
     value = flops / (ms_step * 1e-3) / 1e12
-    achieved = flops / (launch_ms * 1e-3) / 1e12
+    # The steps run back to back, so the kernel's average launch duration is the step time.
+    launch_ms = ms_step
+    achieved = value
     result = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -172,16 +227,16 @@ def main():
             "output": w.out,
             "kernel": prob.plan.describe(),
         },
+        "launch": {"mode": mode, "probe_ms_per_step": probe},
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 3),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": MEASURED_TRAFFIC.get(w.name),
+            "traffic": MEASURED_TRAFFIC.get(w.name) if kernel_source_hash() == MEASURED_TRAFFIC_SOURCE else None,
             "kernel": "fused_gemm_epilogue",
             "launch_ms_mean": round(launch_ms, 6),
-            "launch_ms_median": round(launch_med, 6),
             "algorithmic_flops_per_launch": flops,
             "algorithmic_bytes_per_launch": w.algorithmic_bytes(),
             "hbm_gbs_at_algorithmic_bytes": round(w.algorithmic_bytes() / (launch_ms * 1e-3) / 1e9, 1),
@@ -191,7 +246,7 @@ def main():
     if not args.no_bare:
         wb = w.__class__(**{**w.__dict__, "chain": bare_chain(w), "out": "bf16", "name": w.name + "-bare"})
         bare = runner.prepare(wb, inputs)
-        _, bare_ms, _ = time_launches(bare, args.steps, args.warmup)
+        bare_ms, _, _ = time_launches(bare, args.steps, args.warmup, mode)
         result["bare_gemm_ms"] = round(bare_ms, 6)
         result["epilogue_overhead_pct"] = round((launch_ms / bare_ms - 1.0) * 100.0, 2)
         del bare

@@ -278,3 +278,33 @@ def test_repeated_runs_are_identical_and_amax_is_overwritten():
     torch.cuda.synchronize()
     assert torch.equal(prob.Y, y1)
     assert prob.amax_host() == a1
+
+
+@pytest.mark.parametrize("name", ["c2", "c5"])
+def test_graph_replays_match_eager_runs(name):
+    """The benchmark replays the launches from a HIP graph: every replay, with eager work and
+    synchronisation between replays, gives the eager output and AMAX, and leaves the AMAX
+    ticket counters at zero."""
+    w = workloads.WORKLOADS[name]
+    if name == "c5":
+        w = w.with_shape(M=1024, N=2048, K=1024)
+    inp = workloads.generate(w)
+    prob = gpu_run(w, inp)
+    y_eager, a_eager = prob.Y.clone(), prob.amax_host()
+    compare(w, inp, prob, f"{name} eager")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(3):
+            prob.run()
+    for rep in range(3):
+        prob.Y.zero_()
+        prob.amax.fill_(-1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(prob.Y, y_eager), f"replay {rep}"
+        assert prob.amax_host() == a_eager, f"replay {rep}"
+        assert int(prob.plan.workspace[:4096].count_nonzero()) == 0, f"replay {rep}"
+        prob.run()                                  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(prob.Y, y_eager)
