@@ -19,6 +19,10 @@ Prints ONE JSON line:
   cpu_baseline  the float64 oracle on this host's cores over a bounded sample
   epilogue_overhead_pct  fused kernel time over the same kernel instance with the
              chain reduced to a plain bf16 store (pairwise: the bare product g*u)
+  cold       median single launch with L2/MALL flushed before each launch
+  unfused    the same chain run unfused (GEMM writes bf16 C, one kernel per operation):
+             its time, kernels and algorithmic HBM bytes, and the bytes the fusion saves
+  measured_peaks  what the MFMA and streaming-copy probes sustain on this GPU
 """
 from __future__ import annotations
 
@@ -61,6 +65,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle timing sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bare", action="store_true", help="skip the bare-GEMM comparison")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache single-launch timing")
+    ap.add_argument("--no-unfused", action="store_true", help="skip the unfused-sequence comparison")
+    ap.add_argument("--no-probes", action="store_true", help="skip the MFMA / copy calibration probes")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark: run a plain device copy of MIB MiB ten times (the "
                          "reference kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -117,8 +124,15 @@ def time_launches(prob, steps, warmup, launch="auto"):
     import torch
 
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
+    # warm-up: `warmup` steps, continued until 0.25 s have passed when warmup > 0 (the clocks
+    # take that long to settle under load)
+    t0 = time.perf_counter()
+    done = 0
+    while done < warmup or (warmup > 0 and time.perf_counter() - t0 < 0.25):
         prob.run()
+        done += 1
+        if done % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     def eager(n):
@@ -140,6 +154,23 @@ def time_launches(prob, steps, warmup, launch="auto"):
     else:
         ms = _region_ms(lambda: eager(steps), stream) / steps
     return ms, launch, {k: round(v, 6) for k, v in probe.items()}
+
+
+def cold_launches(prob, n, flops):
+    """Median single-launch time with L2 and MALL flushed before each launch (a 1 GiB write
+    between launches, outside the events)."""
+    import torch
+
+    scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(n):
+        scrub.fill_(1.0)
+        times.append(_region_ms(lambda: prob.run(stream.cuda_stream), stream))
+    del scrub
+    times.sort()
+    med = times[len(times) // 2]
+    return {"launches": n, "ms_median": round(med, 6), "tflops": round(flops / (med * 1e-3) / 1e12, 3)}
 
 
 def bare_chain(w):
@@ -244,14 +275,40 @@ def main():
         },
     }
     if not args.no_bare:
+        # fused, bare, fused again: the overhead compares the bare kernel with the mean of the
+        # fused runs on either side of it, so slow clock drift cancels
         wb = w.__class__(**{**w.__dict__, "chain": bare_chain(w), "out": "bf16", "name": w.name + "-bare"})
         bare = runner.prepare(wb, inputs)
         bare_ms, _, _ = time_launches(bare, args.steps, args.warmup, mode)
+        again_ms, _, _ = time_launches(prob, args.steps, 0, mode)
         result["bare_gemm_ms"] = round(bare_ms, 6)
-        result["epilogue_overhead_pct"] = round((launch_ms / bare_ms - 1.0) * 100.0, 2)
+        result["epilogue_overhead_pct"] = round(((launch_ms + again_ms) / 2 / bare_ms - 1.0) * 100.0, 2)
         del bare
+    if not args.no_cold:
+        result["cold"] = cold_launches(prob, min(args.steps, 20), flops)
+    if not args.no_unfused:
+        from gemm_epilogue_transformer_tiled_amd import baselines
+        unf = baselines.Unfused(w, inputs)
+        unf_ms, _, _ = time_launches(unf, args.steps, args.warmup, mode)
+        ub = unf.algorithmic_bytes()
+        result["unfused"] = {
+            "kernels": unf.kernels(),
+            "ms_per_step": round(unf_ms, 6),
+            "fused_speedup": round(unf_ms / launch_ms, 3),
+            "algorithmic_bytes": ub,
+            "bytes_saved": ub - w.algorithmic_bytes(),
+            "bytes_ratio": round(ub / w.algorithmic_bytes(), 3),
+        }
+        del unf
     del prob
     torch.cuda.synchronize()
+    if not args.no_probes:
+        from gemm_epilogue_transformer_tiled_amd import baselines
+        mf = baselines.probe_mfma()
+        cp = baselines.probe_copy()
+        result["measured_peaks"] = {"mfma_bf16_tflops": mf["tflops"], "mfma_implied_clock_ghz": mf["implied_clock_ghz"],
+                                    "copy_gbs": cp["gbs"]}
+        result["roofline"]["frac_of_measured_mfma_peak"] = round(achieved / mf["tflops"], 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_seconds)
     print(json.dumps(result), flush=True)

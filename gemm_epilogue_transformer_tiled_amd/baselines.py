@@ -1,0 +1,219 @@
+"""Binding of libge_baselines.so: the unfused comparator sequence and the calibration probes.
+
+Measurement infrastructure, not the fused path.  `Unfused` runs a workload the way the pages
+describe it before fusion -- the GEMM (libgemm_epilogue.so with an empty chain) writes bf16 C,
+then every epilogue operation is its own kernel reading and writing a whole bf16 array -- so that
+the fused kernel's HBM bytes saved and speed-up are measured.  Argument marshalling only: all the
+arithmetic runs in the kernels declared in ``include/ge_baselines.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional, Tuple
+
+import torch
+
+from . import GE_DT_BF16, Plan, make_args, make_desc, make_ops
+from .runner import to_device_bf16
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libge_baselines.so")
+
+EXPORTED = ("ge_unfused_scale", "ge_unfused_bias_col", "ge_unfused_act", "ge_unfused_act_mul",
+            "ge_unfused_row_rms", "ge_unfused_row_scale", "ge_unfused_add", "ge_unfused_amax",
+            "ge_unfused_quant_fp8", "ge_probe_mfma", "ge_probe_copy")
+ACTS = {"none": 0, "relu": 1, "gelu_tanh": 2, "silu": 3}
+
+_p, _i64, _i, _f = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+_SIGS = {
+    "ge_unfused_scale": [_p, _p, _i64, _f, _p],
+    "ge_unfused_bias_col": [_p, _p, _p, _i64, _i64, _p],
+    "ge_unfused_act": [_p, _p, _i64, _i, _p],
+    "ge_unfused_act_mul": [_p, _p, _p, _i64, _i, _p],
+    "ge_unfused_row_rms": [_p, _p, _i64, _i64, _f, _p],
+    "ge_unfused_row_scale": [_p, _p, _p, _i64, _i64, _p],
+    "ge_unfused_add": [_p, _p, _p, _i64, _p],
+    "ge_unfused_amax": [_p, _i64, _p, _p],
+    "ge_unfused_quant_fp8": [_p, _p, _i64, _f, _p],
+    "ge_probe_mfma": [_p, _i, _i, _p],
+    "ge_probe_copy": [_p, _p, _i64, _p],
+}
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python gemm_epilogue_transformer_tiled_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, args in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def call(name: str, *args) -> None:
+    st = getattr(lib, name)(*args)
+    if st != 0:
+        raise RuntimeError(f"{name} failed with status {st}")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+class Unfused:
+    """The unfused sequence for workload `w` on uploaded inputs.
+
+    steps: list of (name, callable, bytes read, bytes written) -- the bytes are the algorithmic
+    HBM traffic of that kernel (each input read once, each output written once)."""
+
+    def __init__(self, w, inputs: Dict, device="cuda"):
+        self.w = w
+        t = {k: to_device_bf16(v, device) for k, v in inputs.items() if k in ("A", "B", "B2", "bias", "R")}
+        if "row_scale" in inputs:
+            import numpy as np
+            t["row_scale"] = torch.from_numpy(np.ascontiguousarray(inputs["row_scale"], dtype=np.float32)).to(device)
+        self.t = t
+        rows, n_out = w.batch * w.M, w.batch * w.M * w.N
+        bf = lambda *shape: torch.empty(*shape, dtype=torch.bfloat16, device=device)
+        self.amax = torch.zeros(1, dtype=torch.float32, device=device) if w.has("amax") else None
+        self.plans: List[Plan] = []
+        steps: List[Tuple[str, object, int, int]] = []
+        A = t["A"]
+        a_bytes = A.numel() * 2
+        # RMS: statistic kernel, normalisation kernel, then the GEMM on the normalised rows
+        if w.has("row_rms"):
+            S = torch.empty(rows, dtype=torch.float32, device=device)
+            Xn = bf(A.shape)
+            eps = float(w.op("row_rms")[1])
+            steps.append(("row_rms", lambda A=A, S=S, eps=eps: call(
+                "ge_unfused_row_rms", A.data_ptr(), S.data_ptr(), rows, w.K, eps, _stream()), a_bytes, rows * 4))
+            steps.append(("row_normalise", lambda A=A, S=S, Xn=Xn: call(
+                "ge_unfused_row_scale", A.data_ptr(), S.data_ptr(), Xn.data_ptr(), rows, w.K, _stream()),
+                a_bytes + rows * 4, a_bytes))
+            A = Xn
+        C = bf(w.batch, w.M, w.N)
+        steps.append(("gemm", self._gemm(A, t["B"], C), A.numel() * 2 + t["B"].numel() * 2, n_out * 2))
+        cur = C
+        if w.pairwise:
+            U = bf(w.batch, w.M, w.N)
+            steps.append(("gemm_up", self._gemm(A, t["B2"], U), A.numel() * 2 + t["B2"].numel() * 2, n_out * 2))
+            Y = bf(w.batch, w.M, w.N)
+            act = ACTS[w.op("pairwise")[1]]
+            steps.append(("act_mul", lambda g=cur, u=U, y=Y, act=act: call(
+                "ge_unfused_act_mul", g.data_ptr(), u.data_ptr(), y.data_ptr(), n_out, act, _stream()),
+                2 * n_out * 2, n_out * 2))
+            cur = Y
+        for op in w.chain:
+            kind = op[0]
+            if kind in ("pairwise", "row_rms"):
+                continue
+            if kind == "amax":
+                steps.append(("amax", lambda x=cur: call(
+                    "ge_unfused_amax", x.data_ptr(), n_out, self.amax.data_ptr(), _stream()), n_out * 2, 4))
+                continue
+            if kind == "quant_fp8":
+                Y8 = torch.empty(w.batch, w.M, w.N, dtype=torch.uint8, device=device)
+                steps.append(("quant_fp8", lambda x=cur, y=Y8: call(
+                    "ge_unfused_quant_fp8", x.data_ptr(), y.data_ptr(), n_out, float(w.quant_scale), _stream()),
+                    n_out * 2, n_out))
+                cur = Y8
+                continue
+            Y = bf(w.batch, w.M, w.N)
+            if kind == "scale":
+                fn = lambda x=cur, y=Y: call("ge_unfused_scale", x.data_ptr(), y.data_ptr(), n_out,
+                                             float(w.alpha), _stream())
+                rd = n_out * 2
+            elif kind == "row_scale":
+                s = t["row_scale"]
+                fn = lambda x=cur, y=Y, s=s: call("ge_unfused_row_scale", x.data_ptr(), s.data_ptr(), y.data_ptr(),
+                                                  rows, w.N, _stream())
+                rd = n_out * 2 + rows * 4
+            elif kind == "bias":
+                fn = lambda x=cur, y=Y: call("ge_unfused_bias_col", x.data_ptr(), t["bias"].data_ptr(), y.data_ptr(),
+                                             rows, w.N, _stream())
+                rd = n_out * 2 + w.N * 2
+            elif kind == "act":
+                act = ACTS[op[1]]
+                fn = lambda x=cur, y=Y, act=act: call("ge_unfused_act", x.data_ptr(), y.data_ptr(), n_out, act,
+                                                      _stream())
+                rd = n_out * 2
+            elif kind == "residual":
+                fn = lambda x=cur, y=Y: call("ge_unfused_add", x.data_ptr(), t["R"].data_ptr(), y.data_ptr(), n_out,
+                                             _stream())
+                rd = 2 * n_out * 2
+            else:
+                raise ValueError(f"no unfused kernel for {kind}")
+            steps.append((kind, fn, rd, n_out * 2))
+            cur = Y
+        self.steps = steps
+        self.Y = cur
+
+    def _gemm(self, A, B, C):
+        w = self.w
+        plan = Plan(make_desc(w.batch, w.M, w.N, w.K, make_ops([]), y_type=GE_DT_BF16))
+        self.plans.append(plan)
+        args = make_args(A=A, B=B, Y=C)
+        return lambda: plan.run(args)
+
+    def run(self, stream: Optional[int] = None) -> None:
+        for _, fn, _, _ in self.steps:
+            fn()
+
+    def algorithmic_bytes(self) -> int:
+        return sum(r + wr for _, _, r, wr in self.steps)
+
+    def kernels(self) -> List[str]:
+        return [s[0] for s in self.steps]
+
+    def amax_host(self) -> Optional[float]:
+        return None if self.amax is None else float(self.amax.item())
+
+    def y_host_bits(self):
+        y = self.Y.cpu()
+        if self.w.out == "fp8_e4m3":
+            return y.view(torch.uint8).numpy()
+        import numpy as np
+        return y.view(torch.int16).numpy().view(np.uint16)
+
+
+def probe_mfma(workgroups: int = 1024, iters: int = 4096) -> Dict:
+    """Sustained matrix-core TFLOP/s (v_mfma_f32_32x32x16_bf16 on register data)."""
+    sink = torch.empty(workgroups * 256, dtype=torch.float32, device="cuda")
+    call("ge_probe_mfma", sink.data_ptr(), workgroups, 16, _stream())     # warm
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for _ in range(3):
+        e0.record()
+        call("ge_probe_mfma", sink.data_ptr(), workgroups, iters, _stream())
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    flops = workgroups * 4 * 16 * iters * 32768.0
+    return {"tflops": round(flops / best / 1e9, 1), "ms": round(best, 4),
+            "implied_clock_ghz": round(flops / (best * 1e-3) / (256 * 4096) / 1e9, 3)}
+
+
+def probe_copy(mib: int = 1024) -> Dict:
+    """Sustained device copy GB/s (bytes read + bytes written per second)."""
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    call("ge_probe_copy", src.data_ptr(), dst.data_ptr(), n, _stream())
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for _ in range(5):
+        e0.record()
+        call("ge_probe_copy", src.data_ptr(), dst.data_ptr(), n, _stream())
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    return {"gbs": round(2 * n / (best * 1e-3) / 1e9, 1), "ms": round(best, 4), "bytes_each_way": n}

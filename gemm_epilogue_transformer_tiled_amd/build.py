@@ -1,4 +1,5 @@
-"""Builds libgemm_epilogue.so in-tree with hipcc for gfx950.
+"""Builds libgemm_epilogue.so (the fused path) and libge_baselines.so (unfused comparators and
+calibration probes) in-tree with hipcc for gfx950.
 
 Usage: python gemm_epilogue_transformer_tiled_amd/build.py  (runs by path: importing the
 package itself needs the library this script builds)
@@ -12,9 +13,13 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-LIB = os.path.join(HERE, "libgemm_epilogue.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["ge_kernels.hip", "api.cpp"]
+# library -> its sources
+TARGETS = {
+    os.path.join(HERE, "libgemm_epilogue.so"): ["ge_kernels.hip", "api.cpp"],
+    os.path.join(HERE, "libge_baselines.so"): ["baselines.hip"],
+}
+LIB = os.path.join(HERE, "libgemm_epilogue.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -36,16 +41,18 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr[-6000:]}")
-    os.replace(tmp, LIB)
-    if verbose:
-        print("built", LIB)
+    sources = [src for srcs in TARGETS.values() for src in srcs]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(sources)) as ex:
+        objs = dict(zip(sources, ex.map(_compile, sources)))
+    for lib, srcs in TARGETS.items():
+        tmp = lib + ".tmp"
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *[objs[s] for s in srcs]]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed for {lib}:\n{r.stderr[-6000:]}")
+        os.replace(tmp, lib)
+        if verbose:
+            print("built", lib)
     return LIB
 
 

@@ -113,6 +113,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   // raw buffer: stride 0, num_records = extent in bytes (< 2^31, checked on the host)
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+// Step resources are built at kernel scope, between the (host-device) step lambdas.
 
 // A rows are 128 bytes (eight 16-byte chunks).  Chunk c of row r lives at chunk
 // c ^ swz_a(r).  The swizzle uses only r mod 32, so it is the same for every 32-row MFMA
@@ -195,7 +196,8 @@ __device__ __forceinline__ void sched_group() {
   }
 }
 
-template <class T, int ACT, bool FP8, bool ROWSTAT>
+// KMASK: K is not a multiple of 64, so one A slot straddles K and needs per-lane masking.
+template <class T, int ACT, bool FP8, bool ROWSTAT, bool KMASK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(T::WPE, T::WPE)))
 void fused_gemm_epilogue(Params p) {
   // The LDS stages and slots are distinct arrays, so the compiler can tell that the direct
@@ -238,23 +240,34 @@ void fused_gemm_epilogue(Params p) {
   const int M = p.M, N = p.N, K = p.K;
 
   // ---- buffer resources (extent = last byte this tile may touch; an offset past it reads 0) ----
+  // The K position of a step is carried by the resource: its base moves to column (A) or row
+  // (B) k0 and its extent shrinks by the same amount, so per-lane offsets stay fixed for the
+  // whole loop (no vector instructions for addressing).  A step entirely outside [0, K) gets
+  // an empty resource, which reads zeros.
   const uint16_t* a_base = p.A + b * p.sa + (int64_t)m0 * p.lda;
-  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(a_base, ((int64_t)(M - 1 - m0) * p.lda + K) * 2);
+  const int64_t a_ext = ((int64_t)(M - 1 - m0) * p.lda + K) * 2;
+  const uint16_t* b_base = p.B + b * p.sb + n0;
+  const uint16_t* b2_base = T::PAIR ? p.B2 + b * p.sb + n0 : b_base;
   const int64_t b_ext = K > 0 ? ((int64_t)(K - 1) * p.ldb + (N - n0)) * 2 : 0;
-  const __amdgpu_buffer_rsrc_t b_rs = make_rsrc(p.B + b * p.sb + n0, b_ext);
-  __amdgpu_buffer_rsrc_t b2_rs = b_rs;
-  if constexpr (T::PAIR) b2_rs = make_rsrc(p.B2 + b * p.sb + n0, b_ext);
+  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(a_base, a_ext);       // ragged K: fixed resource
 
   // ---- direct global->LDS loads: per-lane source offsets, fixed for the whole K loop ----
   // A load t of this wave fills slot rows 8u .. 8u+7 (1 KB), u = wave * A_LOADS + t:
   // lane -> row 8u + lane/8, physical chunk lane%8, so it fetches logical chunk
   // (lane%8) ^ swz_a(row) = a_x ^ (u & 3), i.e. K columns 8 * that chunk of the slot's 64.
-  // Rows past M fall outside the resource extent (lda >= K); chunks outside [0, K) get the
-  // out-of-range offset.
+  // Rows past M fall outside the resource extent (lda >= K).  With K a multiple of 64 every
+  // slot is wholly inside or outside [0, K); otherwise chunks outside [0, K) get the
+  // out-of-range offset, per lane, with k0 added to the offset instead of the resource.
   static_assert(T::A_ROWS_PER_LOAD == 8 && T::A_CHUNKS == 8, "one 128-byte row per 8 lanes");
   const uint32_t lda2 = (uint32_t)p.lda * 2u, ldb2 = (uint32_t)p.ldb * 2u;
   const uint32_t a_x = (uint32_t)((lane & 7) ^ (lane >> 3));
   const uint32_t a_row = (uint32_t)(lane >> 3) * lda2;
+  uint32_t a_voff[T::A_LOADS];
+#pragma unroll
+  for (int t = 0; t < T::A_LOADS; ++t) {
+    const uint32_t u = (uint32_t)(wave * T::A_LOADS + t);
+    a_voff[t] = a_row + u * 8u * lda2 + (a_x ^ (u & 3u)) * 16u;
+  }
   // B load t fills B_ROWS_PER_LOAD rows of one operand: lane -> row lane/B_CHUNKS (within
   // the load), physical chunk lane%B_CHUNKS, logical chunk ^ swz_b(row).  Rows past K fall
   // outside the extent; a column block past N gets the out-of-range offset.
@@ -267,33 +280,50 @@ void fused_gemm_epilogue(Params p) {
     b_voff[t] = (n0 + (int)lchunk * 8 < N) ? row * ldb2 + lchunk * 16u : kOOB;
   }
 
-  // A slot for steps k0/BK and k0/BK + 1.  k0 may be negative (leading all-zero steps):
-  // one unsigned compare sends every chunk outside [0, K) out of range.
+  // Resources of the step starting at K column/row k0 (a multiple of 32, so a B step -- and,
+  // with K a multiple of 64, an A slot -- is wholly inside or outside [0, K)): the base is
+  // clamped into range and an out-of-range step gets extent 0.  Byte offsets fit 32 bits:
+  // every extent is checked below 2^31 on the host.  Scalar, branch-free code.
+#define GE_KCLAMP(k0) ((k0) < 0 ? 0 : ((k0) > K ? K : (k0)))
+#define GE_KLIVE(k0) (((k0) >= 0) & ((k0) < K))
+#define GE_A_RS(k0) make_rsrc(a_base + GE_KCLAMP(k0), GE_KLIVE(k0) ? a_ext - 2 * (int64_t)GE_KCLAMP(k0) : 0)
+#define GE_B_RS(base, k0) \
+  make_rsrc((const unsigned char*)(base) + (uint32_t)GE_KCLAMP(k0) * ldb2, \
+            GE_KLIVE(k0) ? b_ext - (int64_t)((uint32_t)GE_KCLAMP(k0) * ldb2) : 0)
+
+  // A slot for steps k0/BK and k0/BK + 1; k0 may be negative (leading all-zero steps).
+  // K a multiple of 64: `rs` is the step's resource and the offsets are fixed.  Otherwise the
+  // fixed resource a_rs, with k0 in the offset and one unsigned compare per chunk sending
+  // every chunk outside [0, K) out of range.
+  __amdgpu_buffer_rsrc_t ars = a_rs, brs = a_rs, b2rs = a_rs;      // the step being filled
   auto issue_a = [&](int k0, unsigned char* slot) {
 #pragma unroll
     for (int t = 0; t < T::A_LOADS; ++t) {
-      const uint32_t u = (uint32_t)(wave * T::A_LOADS + t);          // wave-uniform
-      const uint32_t c = a_x ^ (u & 3u);
-      const uint32_t off = ((uint32_t)(k0 + (int)(c * 8u)) < (uint32_t)K)
-                               ? a_row + u * 8u * lda2 + c * 16u + (uint32_t)k0 * 2u : kOOB;
+      uint32_t off = a_voff[t];
+      if constexpr (KMASK) {
+        const uint32_t u = (uint32_t)(wave * T::A_LOADS + t);          // wave-uniform
+        const uint32_t c = a_x ^ (u & 3u);
+        off = ((uint32_t)(k0 + (int)(c * 8u)) < (uint32_t)K) ? off + (uint32_t)k0 * 2u : kOOB;
+      }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          a_rs, (__attribute__((address_space(3))) void*)(slot + (wave * T::A_LOADS + t) * 1024), 16, off, 0, 0, 0);
+          ars, (__attribute__((address_space(3))) void*)(slot + (wave * T::A_LOADS + t) * 1024), 16, off, 0, 0, 0);
     }
   };
-  // B stage of the step starting at K column k0.
-  auto issue_b = [&](int k0, unsigned char* st) {
-    const bool live = k0 >= 0;     // k0 < 0: an all-zero leading step
+  // B stage of one step from its resources (rows past K fall outside the shrunk extent).
+  auto issue_b = [&](unsigned char* st) {
 #pragma unroll
     for (int t = 0; t < T::B_LOADS; ++t) {
       const int gblk = wave * T::B_LOADS + t;           // wave-uniform
       const int op = gblk / T::B_LOADS_PER_OP;
       const int blk = gblk % T::B_LOADS_PER_OP;
-      const uint32_t off = live ? b_voff[t] + (uint32_t)k0 * ldb2 : kOOB;
       unsigned char* dst = st + op * T::B_BYTES + blk * 1024;
+      // (a local copy: a captured array element passed straight to the builtin makes the
+      // host pass drop the launch stub)
+      const uint32_t off = b_voff[t];
       if (T::PAIR && op == 1)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(b2_rs, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(b2rs, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rs, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
     }
   };
 
@@ -407,7 +437,7 @@ void fused_gemm_epilogue(Params p) {
     using Cur = std::integral_constant<int, S>;
     using Next = std::integral_constant<int, S + 1>;
     using Fill = std::integral_constant<int, S + 2>;
-    issue_b((kt + 2) * T::BK, bstage(Fill{}));
+    issue_b(bstage(Fill{}));
     if constexpr (EVEN) issue_a((kt + 2) * T::BK, aslot(Fill{}));
     static_assert(T::GROUPS == 2, "two groups per step");
     read_frags(aslot(Cur{}), bstage(Cur{}), S % 2, 1, f1);
@@ -430,18 +460,36 @@ void fused_gemm_epilogue(Params p) {
   const int nk = (K + T::BK - 1) / T::BK;
   const int nsteps = (nk + T::NS - 1) / T::NS * T::NS;
   int kt = nk - nsteps;
+#define GE_SET_RS(ka, kb)                                                      \
+  do {                                                                         \
+    if constexpr (!KMASK) ars = GE_A_RS(ka);                                   \
+    brs = GE_B_RS(b_base, kb);                                                 \
+    if constexpr (T::PAIR) b2rs = GE_B_RS(b2_base, kb);                        \
+  } while (0)
+  GE_SET_RS(kt * T::BK, kt * T::BK);
   issue_a(kt * T::BK, aslot(S0{}));
-  issue_b(kt * T::BK, bstage(S0{}));
-  issue_b((kt + 1) * T::BK, bstage(S1{}));
+  issue_b(bstage(S0{}));
+  GE_SET_RS(kt * T::BK, (kt + 1) * T::BK);
+  issue_b(bstage(S1{}));
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(T::B_LOADS));
   __builtin_amdgcn_s_barrier();
   read_frags(aslot(S0{}), bstage(S0{}), 0, 0, f0);
   for (; kt < nk; kt += T::NS) {
+    // each step fills the stages of step + 2 (A: on even steps, the slot of steps + 2, + 3)
+    GE_SET_RS((kt + 2) * T::BK, (kt + 2) * T::BK);
     k_step(S0{}, kt);
+    GE_SET_RS((kt + 2) * T::BK, (kt + 3) * T::BK);
     k_step(S1{}, kt + 1);
+    GE_SET_RS((kt + 4) * T::BK, (kt + 4) * T::BK);
     k_step(S2{}, kt + 2);
+    GE_SET_RS((kt + 4) * T::BK, (kt + 5) * T::BK);
     k_step(S3{}, kt + 3);
   }
+#undef GE_SET_RS
+#undef GE_B_RS
+#undef GE_A_RS
+#undef GE_KLIVE
+#undef GE_KCLAMP
   __builtin_amdgcn_s_waitcnt(kVmcnt0);                 // trailing zero-tile loads into the stages
 
   // ---- RMS row statistic: the two lane halves hold different K of the same rows ----
@@ -657,14 +705,22 @@ constexpr TileInfo info_of() {
   return TileInfo{T::BM, T::BN, T::NT, T::WAVES, T::PAIR, T::LDS};
 }
 
+template <class T, int ACT, bool FP8, bool ROWSTAT>
+void launch_k(const Params& p, hipStream_t s, unsigned grid) {
+  if (p.K % 64 != 0)
+    hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, FP8, ROWSTAT, true>), dim3(grid), dim3(T::NT), 0, s, p);
+  else
+    hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, FP8, ROWSTAT, false>), dim3(grid), dim3(T::NT), 0, s, p);
+}
+
 template <class T, int ACT, bool FP8>
 hipError_t launch_t(const Params& p, hipStream_t s) {
   const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * p.batch;
   if (grid <= 0) return hipSuccess;
   if (p.flags & F_ROW_RMS)
-    hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, FP8, true>), dim3((unsigned)grid), dim3(T::NT), 0, s, p);
+    launch_k<T, ACT, FP8, true>(p, s, (unsigned)grid);
   else
-    hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, FP8, false>), dim3((unsigned)grid), dim3(T::NT), 0, s, p);
+    launch_k<T, ACT, FP8, false>(p, s, (unsigned)grid);
   return hipGetLastError();
 }
 

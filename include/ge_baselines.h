@@ -1,0 +1,81 @@
+/* Comparators and calibration probes for the fused GEMM-epilogue library (gfx950).
+ *
+ * libge_baselines.so is measurement infrastructure, not part of the fused path:
+ *
+ *  - The unfused sequence.  The pages' point is that the memory-bound operations around a GEMM
+ *    (scale, bias, activation, gating, normalisation statistics, residual, reductions) each move
+ *    a whole intermediate through HBM when they run as separate kernels ("Optimising GPU kernels
+ *    with TileLang", fused-epilogue paragraph; superoptimizer write-up, sections 7 and 9: the
+ *    two-kernel RMSNorm that lost for its extra launch and round trip of S; CODA news item, "How
+ *    CODA works"; cuDNN tutorial, graph with an AMAX node).  These kernels run that sequence
+ *    literally -- one kernel per operation, bf16 in and bf16 out (fp8 for the quantiser), the
+ *    GEMM itself being libgemm_epilogue.so with an empty chain -- so that the bytes the fused
+ *    kernel saves and its speed-up can be measured, not assumed.
+ *  - Calibration probes: a matrix-core loop and a streaming copy, giving the MFMA throughput and
+ *    HBM bandwidth this GPU sustains, next to the published peaks.
+ *
+ * Conventions.  Every pointer is a device pointer owned by the caller; arrays are dense and
+ * row-major; bf16 values are passed as their 16-bit patterns, fp8 as OCP e4m3 bytes.  Work is
+ * enqueued on `stream` (a hipStream_t, NULL = the legacy default stream) and nothing
+ * synchronises.  Return value: 0 on success, 1 for an invalid argument (null pointer with a
+ * non-zero size, negative size, unknown activation), 2 when the launch itself failed (the HIP
+ * error is cleared).  Sizes of zero enqueue nothing (AMAX then stores 0).  Rounding: every
+ * bf16 result is rounded to nearest even from the fp32 value the operation computes.
+ */
+#ifndef GE_BASELINES_H
+#define GE_BASELINES_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* y[i] = bf16(alpha * x[i]), i < n. */
+int ge_unfused_scale(const uint16_t* x, uint16_t* y, int64_t n, float alpha, void* stream);
+
+/* y[r][c] = bf16(x[r][c] + bias[c]) for rows x cols (bias has cols entries, shared by rows);
+ * cols % 8 == 0 and rows * cols / 8 < 2^32, else 1. */
+int ge_unfused_bias_col(const uint16_t* x, const uint16_t* bias, uint16_t* y, int64_t rows, int64_t cols,
+                        void* stream);
+
+/* y[i] = bf16(act(x[i])); act as ge_act_t: 0 none, 1 ReLU, 2 GELU (tanh form), 3 SiLU. */
+int ge_unfused_act(const uint16_t* x, uint16_t* y, int64_t n, int act, void* stream);
+
+/* y[i] = bf16(act(g[i]) * u[i]) -- the pairwise gate over two GEMM outputs. */
+int ge_unfused_act_mul(const uint16_t* g, const uint16_t* u, uint16_t* y, int64_t n, int act, void* stream);
+
+/* s[r] = 1 / sqrt(sum_k x[r][k]^2 / cols + eps) in fp32, for rows x cols bf16 x (the separate
+ * statistic kernel of the superoptimizer's two-kernel RMSNorm). */
+int ge_unfused_row_rms(const uint16_t* x, float* s, int64_t rows, int64_t cols, float eps, void* stream);
+
+/* y[r][c] = bf16(x[r][c] * s[r]) -- normalisation of the rows by an fp32 row scale; same size
+ * limits as ge_unfused_bias_col. */
+int ge_unfused_row_scale(const uint16_t* x, const float* s, uint16_t* y, int64_t rows, int64_t cols,
+                         void* stream);
+
+/* y[i] = bf16(x[i] + r[i]) -- residual add. */
+int ge_unfused_add(const uint16_t* x, const uint16_t* r, uint16_t* y, int64_t n, void* stream);
+
+/* *amax = max_i |x[i]| over bf16 x, as fp32 (NaN propagates as the largest pattern). */
+int ge_unfused_amax(const uint16_t* x, int64_t n, float* amax, void* stream);
+
+/* y[i] = e4m3(clamp(x[i] * scale, -448, 448)), round to nearest even. */
+int ge_unfused_quant_fp8(const uint16_t* x, uint8_t* y, int64_t n, float scale, void* stream);
+
+/* Matrix-core probe: `workgroups` workgroups of 4 waves, each wave running 16 independent
+ * chains of `iters` v_mfma_f32_32x32x16_bf16 on register data; `sink` receives
+ * workgroups * 256 floats (keeps the work live).  Floating-point work per launch:
+ * workgroups * 4 * 16 * iters * 32768. */
+int ge_probe_mfma(float* sink, int workgroups, int iters, void* stream);
+
+/* Streaming copy of `bytes` (a multiple of 16, 16-byte aligned pointers): reads and writes each
+ * byte once. */
+int ge_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GE_BASELINES_H */

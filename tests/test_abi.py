@@ -13,12 +13,12 @@ import gemm_epilogue_transformer_tiled_amd as ge
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared_symbols():
+def _declared_symbols(pattern=r"gemm_epilogue_\w+"):
     names = set()
     for path in glob.glob(os.path.join(ROOT, "include", "*.h")):
         text = open(path).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        names.update(re.findall(r"\b(gemm_epilogue_\w+)\s*\(", text))
+        names.update(re.findall(r"\b(" + pattern + r")\s*\(", text))
     return sorted(names)
 
 
@@ -29,6 +29,29 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(ge.EXPORTED)
+
+
+def test_baselines_library_exports_every_declared_symbol():
+    from gemm_epilogue_transformer_tiled_amd import baselines
+    names = _declared_symbols(r"ge_(?:unfused|probe)_\w+")
+    assert len(names) == 11
+    lib = ctypes.CDLL(baselines.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(baselines.EXPORTED)
+
+
+def test_baselines_reject_invalid_arguments_without_launching():
+    from gemm_epilogue_transformer_tiled_amd import baselines
+    lib = baselines.lib
+    assert lib.ge_unfused_scale(None, None, -1, 1.0, None) == 1
+    assert lib.ge_unfused_act(None, None, 8, 1, None) == 1          # null pointers with n > 0
+    assert lib.ge_unfused_act(None, None, 0, 7, None) == 1          # unknown activation
+    assert lib.ge_unfused_bias_col(None, None, None, 0, 12, None) == 1
+    assert lib.ge_unfused_amax(None, 0, None, None) == 1
+    assert lib.ge_probe_copy(None, None, 24, None) == 1             # not a multiple of 16
+    assert lib.ge_probe_mfma(None, 1, 1, None) == 1
+    assert lib.ge_unfused_scale(None, None, 0, 1.0, None) == 0      # empty: nothing to do
 
 
 def _desc(**kw):
