@@ -49,9 +49,14 @@ MEASURED_TRAFFIC = {"c1": 1043223, "c2": 101168759, "c3": 3053782077, "c4": 5374
 
 
 def kernel_source_hash():
-    path = os.path.join(ROOT, "gemm_epilogue_transformer_tiled_amd", "csrc", "ge_kernels.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 prefix over the fused kernel's sources (csrc/ge_*, in name order)."""
+    csrc = os.path.join(ROOT, "gemm_epilogue_transformer_tiled_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.startswith("ge_"):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
 def parse():

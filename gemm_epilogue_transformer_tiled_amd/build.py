@@ -16,7 +16,9 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 # library -> its sources
 TARGETS = {
-    os.path.join(HERE, "libgemm_epilogue.so"): ["ge_kernels.hip", "api.cpp"],
+    os.path.join(HERE, "libgemm_epilogue.so"): [
+        "ge_tile_256x256.hip", "ge_tile_256x128_pair.hip", "ge_tile_128x128.hip", "ge_tile_64x64.hip",
+        "ge_tile_128x128_pair.hip", "ge_kernels.hip", "api.cpp"],
     os.path.join(HERE, "libge_baselines.so"): ["baselines.hip"],
 }
 LIB = os.path.join(HERE, "libgemm_epilogue.so")

@@ -54,6 +54,18 @@ struct TileInfo {
 
 TileInfo tile_info(TileKind kind);
 
+// Per-tile instance sets (ge_tile_*.hip).
+hipError_t launch_tile_256x256(int act, bool fp8_out, const Params& p, hipStream_t stream);
+TileInfo tile_info_256x256();
+hipError_t launch_tile_256x128_pair(int act, bool fp8_out, const Params& p, hipStream_t stream);
+TileInfo tile_info_256x128_pair();
+hipError_t launch_tile_128x128(int act, bool fp8_out, const Params& p, hipStream_t stream);
+TileInfo tile_info_128x128();
+hipError_t launch_tile_64x64(int act, bool fp8_out, const Params& p, hipStream_t stream);
+TileInfo tile_info_64x64();
+hipError_t launch_tile_128x128_pair(int act, bool fp8_out, const Params& p, hipStream_t stream);
+TileInfo tile_info_128x128_pair();
+
 // Enqueues the fused kernel.  `act` in Act, `fp8_out` selects the E4M3 writer.
 hipError_t launch_fused(TileKind kind, int act, bool fp8_out, const Params& p, hipStream_t stream);
 

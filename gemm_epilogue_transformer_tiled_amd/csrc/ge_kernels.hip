@@ -1,761 +1,36 @@
-// Fused bf16 GEMM + register-resident epilogue for MI355X (gfx950, CDNA4).
-//
-// What is computed (pages as titled): the tiled GEMM whose output tile stays in
-// register fragments while the epilogue runs, then one store ("Optimising GPU
-// kernels with TileLang", tiled-matmul and fused-epilogue paragraphs;
-// superoptimizer write-up, section 8); the epilogue primitives of the CODA news
-// item ("How CODA works"): scale, per-row scale, column bias, activation or the
-// pairwise SwiGLU gate (superoptimizer write-up, section 7), residual
-// accumulation, the AMAX reduction of the cuDNN tutorial's batched-matmul
-// paragraph, and bf16 / OCP fp8-e4m3 writers.  The RMS row statistic of the
-// superoptimizer write-up's section 9 is gathered from the A operand while it
-// is staged, so no separate scale kernel or round trip of S is needed.
-//
-// Mainloop design (per workgroup of 4 waves, 2 x 2 over the output tile):
-//   * Operands reach LDS with direct global->LDS buffer loads (16 bytes per lane, 1 KB per
-//     instruction, no register staging).  Out-of-range rows, columns and K chunks are
-//     given an offset past the buffer extent, so the hardware returns zeros -- ragged
-//     tails need no branches.
-//   * K advances in steps of 32.  A ([M, K], K contiguous) is staged two steps at a time
-//     as [BM][64] with 128-byte rows, so every cache line fetched from L2 is used whole
-//     and fetched once; B ([K, N], N contiguous) is staged per step as [32][BN], row-major
-//     as it sits in memory.  Two A slots and a ring of four B stages let the loads of
-//     step k+2 run while step k computes; one barrier per step.
-//   * 16-byte chunks are XOR-swizzled within each LDS row so that fragment reads are free
-//     of bank conflicts while the direct loads still write whole 1-KB blocks.
-//   * A fragments are plain 16-byte LDS reads; B fragments (K packed inside each lane, as
-//     the matrix core wants) come from transposing LDS reads (ds_read_b64_tr_b16).
-//   * v_mfma_f32_32x32x16_bf16 with the operands swapped (B fragment as the first source)
-//     so that each lane's accumulators hold four consecutive output columns of one output
-//     row.  The epilogue stages each 32-row block through LDS once so that bias/residual
-//     loads and Y stores cover whole rows.
-//   * Workgroup ids are remapped so each XCD (own L2) receives a contiguous run of tiles,
-//     which are then walked in groups of 8 tile-rows for L2 reuse.
-#include <type_traits>
+// Dispatch of the fused kernel instances (one translation unit per tile shape) and the
+// zero-fill kernel for AMAX on empty problems.
+#include <hip/hip_runtime.h>
 
 #include "ge_internal.h"
 
 namespace ge {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 v4bf16_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-constexpr uint32_t kOOB = 0x80000000u;    // offset past every buffer extent
-constexpr int kXCDs = 8;                  // MI355X: 8 accelerator dies, each with its own L2
-constexpr int kGroupM = 8;                // tile-rows walked together for L2 reuse
-// s_waitcnt immediate for "vector memory count 0" with the other counters left free
-// (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]).
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
-constexpr int kVmcnt0 = vmcnt_imm(0);
-// Same, with the LDS counter (lgkmcnt) also drained to zero.
-constexpr int vmcnt_lgkm0_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4); }
-constexpr float kLog2e = 1.4426950408889634f;
-// GELU tanh form as t * sigmoid(2u), u = sqrt(2/pi) (t + 0.044715 t^3):
-// sigmoid(2u) = 1 / (1 + 2^(-2 log2(e) u)).
-constexpr float kGeluC = -2.0f * 1.4426950408889634f * 0.7978845608028654f;
-constexpr float kGeluCubic = 0.044715f;
-
-template <int BM_, int BN_, bool PAIR_, int WPE_>
-struct Tile {
-  static constexpr int BM = BM_, BN = BN_;
-  static constexpr bool PAIR = PAIR_;
-  static constexpr int WPE = WPE_;                   // waves per SIMD the kernel is built for
-  static constexpr int WAVES = 4, NT = 256;          // 2 x 2 waves
-  static constexpr int WM = BM / 2, WN = BN / 2;     // per-wave output tile
-  static constexpr int FM = WM / 32, FN = WN / 32;   // 32x32 MFMA blocks per wave
-  static constexpr int NB = PAIR ? 2 : 1;            // B operands
-  // Pipeline: K steps of BK = 32.  B tiles ([BK][BN] per operand) go through a ring of
-  // NS = 4 LDS stages; A tiles are staged two steps at a time ([BM][64], 128-byte rows, so
-  // every fetched cache line is used whole) in two slots.  The tiles of step k+2 are
-  // fetched while step k computes.
-  static constexpr int BK = 32, NS = 4, PD = 2;
-  static constexpr int GROUPS = BK / 16;             // 16-deep MFMA groups per step
-  static constexpr int A_ROWB = 128;                 // one A row: 64 K values
-  static constexpr int A_CHUNKS = A_ROWB / 16;
-  static constexpr int A_SLOT = BM * A_ROWB;         // two steps of A
-  static constexpr int B_ROWB = BN * 2;              // bytes per staged B row
-  static constexpr int B_CHUNKS = B_ROWB / 16;       // 16-byte chunks per B row
-  static constexpr int B_BYTES = BK * B_ROWB;        // one B operand, one step
-  static constexpr int B_STAGE = NB * B_BYTES;
-  // Epilogue: each wave stages a 32-row block of fp32 rows (WN + 4 floats) in LDS; two
-  // waves share an A slot, which is sized to hold them.
-  static constexpr int EP_LD = WN + 4;
-  static constexpr int EP_WAVE_BYTES = 32 * EP_LD * 4;
-  static constexpr int A_ALLOC = A_SLOT > 2 * EP_WAVE_BYTES ? A_SLOT : 2 * EP_WAVE_BYTES;
-  static constexpr int LDS = 2 * A_ALLOC + NS * B_STAGE;
-  // Direct global->LDS loads: one instruction moves 1 KB (64 lanes x 16 bytes).
-  static constexpr int A_ROWS_PER_LOAD = 1024 / A_ROWB;
-  static constexpr int A_LOADS = A_SLOT / 1024 / WAVES;            // per wave per A slot
-  static constexpr int B_ROWS_PER_LOAD = 1024 / B_ROWB;
-  static constexpr int B_LOADS_PER_OP = BK / B_ROWS_PER_LOAD;     // per operand per step
-  static constexpr int B_LOADS = NB * B_LOADS_PER_OP / WAVES;     // per wave per step
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile must split into 2x2 waves of 32x32 blocks");
-  static_assert(A_LOADS >= 1 && A_SLOT % (1024 * WAVES) == 0, "A loads must divide over the waves");
-  static_assert(B_LOADS >= 1 && (NB * B_LOADS_PER_OP) % WAVES == 0, "B loads must divide over the waves");
-  static_assert(B_LOADS_PER_OP % B_LOADS == 0 || B_LOADS % B_LOADS_PER_OP == 0, "one operand per load");
-  static_assert(A_LOADS + B_LOADS < 64, "vmcnt range");
-  static_assert(LDS + 1024 + 64 <= 160 * 1024, "LDS budget of one workgroup");
-};
-
-using T256 = Tile<256, 256, false, 1>;
-using T256P = Tile<256, 128, true, 1>;
-using T128 = Tile<128, 128, false, 2>;
-using T64 = Tile<64, 64, false, 2>;
-using T128P = Tile<128, 128, true, 1>;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  // raw buffer: stride 0, num_records = extent in bytes (< 2^31, checked on the host)
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-// Step resources are built at kernel scope, between the (host-device) step lambdas.
-
-// A rows are 128 bytes (eight 16-byte chunks).  Chunk c of row r lives at chunk
-// c ^ swz_a(r).  The swizzle uses only r mod 32, so it is the same for every 32-row MFMA
-// block; 16 consecutive rows read at one logical chunk land on distinct banks for both
-// 128-byte and 256-byte LDS cycles (even rows take all eight chunks, odd rows too).
-__device__ __forceinline__ uint32_t swz_a(uint32_t row) {
-  return (row & 7u) ^ ((row >> 3) & 3u);
-}
-
-// B rows ([k][n], 2*BN bytes).  Chunk c of row k lives at chunk c ^ swz_b(k).  A
-// 16-lane transpose read touches rows k..k+3 (k % 4 == 0) and one pair of chunks;
-// the XOR pattern {0, 4, 10, 14} sends those four pairs to four different pairs of
-// every aligned group of four (distinct banks for 128-byte LDS cycles) and the two
-// 16-lane groups of a half-wave to complementary halves (256-byte cycles).
-template <int CHUNKS>
-__device__ __forceinline__ uint32_t swz_b(uint32_t k) {
-  const uint32_t q = k & 3u;
-  return ((q << 2) | ((q >> 1) << 1)) & (uint32_t)(CHUNKS - 1);
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  bf16x2_t h = {(__bf16)a, (__bf16)b};   // round to nearest even
-  return __builtin_bit_cast(uint32_t, h);
-}
-
-template <int ACT>
-__device__ __forceinline__ float activate(float t) {
-  if constexpr (ACT == ACT_RELU) {
-    return fmaxf(t, 0.0f);
-  } else if constexpr (ACT == ACT_GELU_TANH) {
-    const float e = __builtin_amdgcn_exp2f(kGeluC * (t + kGeluCubic * t * t * t));
-    return t * __builtin_amdgcn_rcpf(1.0f + e);
-  } else if constexpr (ACT == ACT_SILU) {
-    const float e = __builtin_amdgcn_exp2f(-kLog2e * t);
-    return t * __builtin_amdgcn_rcpf(1.0f + e);
-  } else {
-    return t;
-  }
-}
-
-// Workgroup id -> (batch, tile row, tile column).
-__device__ __forceinline__ void tile_coords(int wg, const Params& p, int& b, int& tm, int& tn) {
-  const int per_batch = p.tiles_m * p.tiles_n;
-  const int total = per_batch * p.batch;
-  // XCD-aware remap: hardware deals consecutive ids round-robin over the 8 XCDs;
-  // give each XCD a contiguous run of tiles instead.
-  const int xcd = wg % kXCDs, local = wg / kXCDs;
-  const int per_xcd = (total + kXCDs - 1) / kXCDs;
-  int tall = total % kXCDs;
-  if (tall == 0) tall = kXCDs;
-  const int id = xcd < tall ? xcd * per_xcd + local
-                            : tall * per_xcd + (xcd - tall) * (per_xcd - 1) + local;
-  b = id / per_batch;
-  const int r = id - b * per_batch;
-  const int group_span = kGroupM * p.tiles_n;
-  const int g = r / group_span;
-  const int first_m = g * kGroupM;
-  const int gsize = min(p.tiles_m - first_m, kGroupM);
-  const int in_g = r - g * group_span;
-  tm = first_m + in_g % gsize;
-  tn = in_g / gsize;
-}
-
-// Scheduling recipe for one 16-deep MFMA group of MF instructions: after MFMA m come
-// ceil(NL / MF) of the step's NL direct loads (VMEM = 0x010, while any remain) and, for
-// m < RD, one of the next group's fragment reads (DS read = 0x100); MFMA = 0x008.
-template <int MF, int NL, int RD, int M = 0>
-__device__ __forceinline__ void sched_group() {
-  if constexpr (M < MF) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    constexpr int per = (NL + MF - 1) / MF;
-    constexpr int left = NL - M * per;
-    constexpr int n = left < per ? left : per;
-    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x010, n, 0);
-    if constexpr (M < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    sched_group<MF, NL, RD, M + 1>();
-  }
-}
-
-// KMASK: K is not a multiple of 64, so one A slot straddles K and needs per-lane masking.
-template <class T, int ACT, bool FP8, bool ROWSTAT, bool KMASK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(T::WPE, T::WPE)))
-void fused_gemm_epilogue(Params p) {
-  // The LDS stages and slots are distinct arrays, so the compiler can tell that the direct
-  // loads filling one never alias the fragment reads of another.
-  __shared__ __attribute__((aligned(1024))) unsigned char aslot0[T::A_ALLOC];
-  __shared__ __attribute__((aligned(1024))) unsigned char aslot1[T::A_ALLOC];
-  __shared__ __attribute__((aligned(1024))) unsigned char bstage0[T::B_STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char bstage1[T::B_STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char bstage2[T::B_STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char bstage3[T::B_STAGE];
-  __shared__ float row_ss[ROWSTAT ? T::BM : 1];
-  __shared__ uint32_t wave_amax[T::WAVES];
-  static_assert(T::NS == 4, "four B stage arrays");
-  // B stage of step s, A slot of step s (two consecutive steps share a slot).
-  auto bstage = [&](auto s_c) -> unsigned char* {
-    constexpr int S = decltype(s_c)::value % T::NS;
-    if constexpr (S == 0) return bstage0;
-    else if constexpr (S == 1) return bstage1;
-    else if constexpr (S == 2) return bstage2;
-    else return bstage3;
-  };
-  auto aslot = [&](auto s_c) -> unsigned char* {
-    constexpr int S = decltype(s_c)::value % T::NS;
-    if constexpr (S / 2 == 0) return aslot0;
-    else return aslot1;
-  };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  using S3 = std::integral_constant<int, 3>;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wave_m = wave & 1, wave_n = wave >> 1;
-
-  int b, tm, tn;
-  tile_coords(blockIdx.x, p, b, tm, tn);
-  const int m0 = tm * T::BM, n0 = tn * T::BN;
-  const int M = p.M, N = p.N, K = p.K;
-
-  // ---- buffer resources (extent = last byte this tile may touch; an offset past it reads 0) ----
-  // The K position of a step is carried by the resource: its base moves to column (A) or row
-  // (B) k0 and its extent shrinks by the same amount, so per-lane offsets stay fixed for the
-  // whole loop (no vector instructions for addressing).  A step entirely outside [0, K) gets
-  // an empty resource, which reads zeros.
-  const uint16_t* a_base = p.A + b * p.sa + (int64_t)m0 * p.lda;
-  const int64_t a_ext = ((int64_t)(M - 1 - m0) * p.lda + K) * 2;
-  const uint16_t* b_base = p.B + b * p.sb + n0;
-  const uint16_t* b2_base = T::PAIR ? p.B2 + b * p.sb + n0 : b_base;
-  const int64_t b_ext = K > 0 ? ((int64_t)(K - 1) * p.ldb + (N - n0)) * 2 : 0;
-  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(a_base, a_ext);       // ragged K: fixed resource
-
-  // ---- direct global->LDS loads: per-lane source offsets, fixed for the whole K loop ----
-  // A load t of this wave fills slot rows 8u .. 8u+7 (1 KB), u = wave * A_LOADS + t:
-  // lane -> row 8u + lane/8, physical chunk lane%8, so it fetches logical chunk
-  // (lane%8) ^ swz_a(row) = a_x ^ (u & 3), i.e. K columns 8 * that chunk of the slot's 64.
-  // Rows past M fall outside the resource extent (lda >= K).  With K a multiple of 64 every
-  // slot is wholly inside or outside [0, K); otherwise chunks outside [0, K) get the
-  // out-of-range offset, per lane, with k0 added to the offset instead of the resource.
-  static_assert(T::A_ROWS_PER_LOAD == 8 && T::A_CHUNKS == 8, "one 128-byte row per 8 lanes");
-  const uint32_t lda2 = (uint32_t)p.lda * 2u, ldb2 = (uint32_t)p.ldb * 2u;
-  const uint32_t a_x = (uint32_t)((lane & 7) ^ (lane >> 3));
-  const uint32_t a_row = (uint32_t)(lane >> 3) * lda2;
-  uint32_t a_voff[T::A_LOADS];
-#pragma unroll
-  for (int t = 0; t < T::A_LOADS; ++t) {
-    const uint32_t u = (uint32_t)(wave * T::A_LOADS + t);
-    a_voff[t] = a_row + u * 8u * lda2 + (a_x ^ (u & 3u)) * 16u;
-  }
-  // B load t fills B_ROWS_PER_LOAD rows of one operand: lane -> row lane/B_CHUNKS (within
-  // the load), physical chunk lane%B_CHUNKS, logical chunk ^ swz_b(row).  Rows past K fall
-  // outside the extent; a column block past N gets the out-of-range offset.
-  uint32_t b_voff[T::B_LOADS];
-#pragma unroll
-  for (int t = 0; t < T::B_LOADS; ++t) {
-    const int blk = (wave * T::B_LOADS + t) % T::B_LOADS_PER_OP;
-    const uint32_t row = (uint32_t)blk * T::B_ROWS_PER_LOAD + (uint32_t)(lane / T::B_CHUNKS);
-    const uint32_t lchunk = (uint32_t)(lane % T::B_CHUNKS) ^ swz_b<T::B_CHUNKS>(row);
-    b_voff[t] = (n0 + (int)lchunk * 8 < N) ? row * ldb2 + lchunk * 16u : kOOB;
-  }
-
-  // Resources of the step starting at K column/row k0 (a multiple of 32, so a B step -- and,
-  // with K a multiple of 64, an A slot -- is wholly inside or outside [0, K)): the base is
-  // clamped into range and an out-of-range step gets extent 0.  Byte offsets fit 32 bits:
-  // every extent is checked below 2^31 on the host.  Scalar, branch-free code.
-#define GE_KCLAMP(k0) ((k0) < 0 ? 0 : ((k0) > K ? K : (k0)))
-#define GE_KLIVE(k0) (((k0) >= 0) & ((k0) < K))
-#define GE_A_RS(k0) make_rsrc(a_base + GE_KCLAMP(k0), GE_KLIVE(k0) ? a_ext - 2 * (int64_t)GE_KCLAMP(k0) : 0)
-#define GE_B_RS(base, k0) \
-  make_rsrc((const unsigned char*)(base) + (uint32_t)GE_KCLAMP(k0) * ldb2, \
-            GE_KLIVE(k0) ? b_ext - (int64_t)((uint32_t)GE_KCLAMP(k0) * ldb2) : 0)
-
-  // A slot for steps k0/BK and k0/BK + 1; k0 may be negative (leading all-zero steps).
-  // K a multiple of 64: `rs` is the step's resource and the offsets are fixed.  Otherwise the
-  // fixed resource a_rs, with k0 in the offset and one unsigned compare per chunk sending
-  // every chunk outside [0, K) out of range.
-  __amdgpu_buffer_rsrc_t ars = a_rs, brs = a_rs, b2rs = a_rs;      // the step being filled
-  auto issue_a = [&](int k0, unsigned char* slot) {
-#pragma unroll
-    for (int t = 0; t < T::A_LOADS; ++t) {
-      uint32_t off = a_voff[t];
-      if constexpr (KMASK) {
-        const uint32_t u = (uint32_t)(wave * T::A_LOADS + t);          // wave-uniform
-        const uint32_t c = a_x ^ (u & 3u);
-        off = ((uint32_t)(k0 + (int)(c * 8u)) < (uint32_t)K) ? off + (uint32_t)k0 * 2u : kOOB;
-      }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ars, (__attribute__((address_space(3))) void*)(slot + (wave * T::A_LOADS + t) * 1024), 16, off, 0, 0, 0);
-    }
-  };
-  // B stage of one step from its resources (rows past K fall outside the shrunk extent).
-  auto issue_b = [&](unsigned char* st) {
-#pragma unroll
-    for (int t = 0; t < T::B_LOADS; ++t) {
-      const int gblk = wave * T::B_LOADS + t;           // wave-uniform
-      const int op = gblk / T::B_LOADS_PER_OP;
-      const int blk = gblk % T::B_LOADS_PER_OP;
-      unsigned char* dst = st + op * T::B_BYTES + blk * 1024;
-      // (a local copy: a captured array element passed straight to the builtin makes the
-      // host pass drop the launch stub)
-      const uint32_t off = b_voff[t];
-      if (T::PAIR && op == 1)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(b2rs, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
-    }
-  };
-
-  // ---- fragment addressing ----
-  // A (second MFMA source): for group g of the step in slot half h, lane reads row
-  // wm0 + 32j + lane%32, logical chunk 4h + 2g + lane/32 (eight consecutive K); the swizzle
-  // depends on lane%32 only, so j is an immediate offset.
-  const int lrow = lane & 31, lhalf = lane >> 5;
-  const int wm0 = wave_m * T::WM, wn0 = wave_n * T::WN;
-  uint32_t a_frag[2 * T::GROUPS];
-#pragma unroll
-  for (int hg = 0; hg < 2 * T::GROUPS; ++hg)
-    a_frag[hg] = (uint32_t)(wm0 + lrow) * T::A_ROWB + (((uint32_t)(2 * hg + lhalf) ^ swz_a(lrow)) << 4);
-  // B (first MFMA source) through 16-lane transpose reads: in each group of 16 lanes, lane s
-  // points at row k0 + s/4 and columns nb + 4(s%4) .. +3, and receives column nb + s of rows
-  // k0 .. k0+3.  Two reads (rows +0..3, +4..7) give the eight K values of A's lane layout.
-  const int grp = lane >> 4, sl = lane & 15;
-  const uint32_t kl = (uint32_t)(8 * (grp >> 1) + (sl >> 2));            // row within the 16-K slice
-  uint32_t b_frag[T::NB][T::FN];
-#pragma unroll
-  for (int op = 0; op < T::NB; ++op)
-#pragma unroll
-    for (int i = 0; i < T::FN; ++i) {
-      const uint32_t ncol = (uint32_t)(wn0 + 32 * i + 16 * (grp & 1) + 4 * (sl & 3));
-      const uint32_t lchunk = ncol >> 3;
-      b_frag[op][i] = (uint32_t)(op * T::B_BYTES) + kl * T::B_ROWB +
-                      ((lchunk ^ swz_b<T::B_CHUNKS>(kl)) << 4) + (ncol & 7u) * 2u;
-    }
-
-  f32x16_t acc[T::FN][T::FM];
-  f32x16_t acc2[T::PAIR ? T::FN : 1][T::PAIR ? T::FM : 1];
-#pragma unroll
-  for (int i = 0; i < T::FN; ++i)
-#pragma unroll
-    for (int j = 0; j < T::FM; ++j) {
-      acc[i][j] = f32x16_t{};
-      if constexpr (T::PAIR) acc2[i][j] = f32x16_t{};
-    }
-  // RMS statistic from the A fragments: waves with wave_n == 0 own the first half of the
-  // wave's 32-row blocks, wave_n == 1 the second half (all of them when FM == 1 and wave_n == 0).
-  constexpr int SS_J = T::FM > 1 ? T::FM / 2 : 1;
-  float ss[SS_J];
-#pragma unroll
-  for (int j = 0; j < SS_J; ++j) ss[j] = 0.0f;
-  const bool ss_owner = T::FM > 1 || wave_n == 0;
-  const int ss_j0 = T::FM > 1 ? wave_n * SS_J : 0;
-
-  struct Frags {
-    bf16x8_t a[T::FM];
-    bf16x8_t b[T::NB][T::FN];
-  };
-  typedef __attribute__((address_space(3))) v4bf16_t lds_v4bf16;
-  auto read_frags = [&](const unsigned char* as, const unsigned char* bs, int h, int g, Frags& f) {
-#pragma unroll
-    for (int j = 0; j < T::FM; ++j)
-      f.a[j] = *(const bf16x8_t*)(as + a_frag[h * T::GROUPS + g] + j * 32 * T::A_ROWB);
-#pragma unroll
-    for (int op = 0; op < T::NB; ++op)
-#pragma unroll
-      for (int i = 0; i < T::FN; ++i) {
-        const unsigned char* q = bs + b_frag[op][i] + 16 * g * T::B_ROWB;
-        const v4bf16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf16*)(q));
-        const v4bf16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf16*)(q + 4 * T::B_ROWB));
-        f.b[op][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-  };
-  auto mfmas = [&](const Frags& f) {
-#pragma unroll
-    for (int i = 0; i < T::FN; ++i)
-#pragma unroll
-      for (int j = 0; j < T::FM; ++j) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[0][i], f.a[j], acc[i][j], 0, 0, 0);
-        if constexpr (T::PAIR)
-          acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[T::NB - 1][i], f.a[j], acc2[i][j], 0, 0, 0);
-      }
-    if constexpr (ROWSTAT) {
-      if (ss_owner) {
-#pragma unroll
-        for (int j = 0; j < SS_J; ++j) {
-          const bf16x8_t v = (T::FM > 1 && wave_n == 1) ? f.a[(T::FM > 1 ? SS_J : 0) + j] : f.a[j];
-          const bf16x2_t p0 = __builtin_shufflevector(v, v, 0, 1), p1 = __builtin_shufflevector(v, v, 2, 3);
-          const bf16x2_t p2 = __builtin_shufflevector(v, v, 4, 5), p3 = __builtin_shufflevector(v, v, 6, 7);
-          ss[j] = __builtin_amdgcn_fdot2_f32_bf16(p0, p0, ss[j], false);
-          ss[j] = __builtin_amdgcn_fdot2_f32_bf16(p1, p1, ss[j], false);
-          ss[j] = __builtin_amdgcn_fdot2_f32_bf16(p2, p2, ss[j], false);
-          ss[j] = __builtin_amdgcn_fdot2_f32_bf16(p3, p3, ss[j], false);
-        }
-      }
-    }
-  };
-  constexpr int READS_PER_GROUP = T::FM + 2 * T::NB * T::FN;
-  constexpr int MFMAS_PER_GROUP = T::FM * T::FN * T::NB;
-  // One K step s (tile kt), entered with the fragments of its first group in f0:
-  //   * start the direct loads of step kt+2 -- its B stage, and on even steps the A slot of
-  //     steps kt+2 and kt+3.  Both were freed before the previous barrier: the B stage held
-  //     step kt-2, the A slot steps kt-2 and kt-1, whose last fragment reads (issued before
-  //     the previous barrier) were waited for there;
-  //   * run group 0 with group 1's fragments in flight;
-  //   * wait until step kt+1 has landed: on an even step every load but this step's; on an
-  //     odd step every load but this step's B loads (the A slot of kt+1 came with the
-  //     previous step's loads), and also this wave's LDS reads of the A slot, which the
-  //     next step refills;
-  //   * meet the other waves at the barrier, then run group 1 while the first fragments of
-  //     step kt+1 are read -- the matrix cores stay busy across the barrier.
-  // Loads are issued even past the last step: those offsets are all out of range, so they
-  // only write zeros into stages whose reads are discarded (no branch in the loop body).
-  Frags f0, f1;
-  auto k_step = [&](auto s_c, int kt) {
-    constexpr int S = decltype(s_c)::value;
-    constexpr bool EVEN = S % 2 == 0;
-    using Cur = std::integral_constant<int, S>;
-    using Next = std::integral_constant<int, S + 1>;
-    using Fill = std::integral_constant<int, S + 2>;
-    issue_b(bstage(Fill{}));
-    if constexpr (EVEN) issue_a((kt + 2) * T::BK, aslot(Fill{}));
-    static_assert(T::GROUPS == 2, "two groups per step");
-    read_frags(aslot(Cur{}), bstage(Cur{}), S % 2, 1, f1);
-    mfmas(f0);
-    sched_group<MFMAS_PER_GROUP, EVEN ? T::A_LOADS + T::B_LOADS : T::B_LOADS, READS_PER_GROUP>();
-    // No memory fence: the later loads stay in flight across the barrier.
-    if constexpr (EVEN)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(T::A_LOADS + T::B_LOADS));
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(T::B_LOADS));
-    __builtin_amdgcn_s_barrier();
-    read_frags(aslot(Next{}), bstage(Next{}), (S + 1) % 2, 0, f0);
-    mfmas(f1);
-    sched_group<MFMAS_PER_GROUP, 0, READS_PER_GROUP>();
-  };
-
-  // Step count rounded up to a multiple of NS with leading all-zero steps, so the loop
-  // always runs whole stage rings, A slots pair steps (0,1) and (2,3) of each ring, and the
-  // accumulators have one exit path.
-  const int nk = (K + T::BK - 1) / T::BK;
-  const int nsteps = (nk + T::NS - 1) / T::NS * T::NS;
-  int kt = nk - nsteps;
-#define GE_SET_RS(ka, kb)                                                      \
-  do {                                                                         \
-    if constexpr (!KMASK) ars = GE_A_RS(ka);                                   \
-    brs = GE_B_RS(b_base, kb);                                                 \
-    if constexpr (T::PAIR) b2rs = GE_B_RS(b2_base, kb);                        \
-  } while (0)
-  GE_SET_RS(kt * T::BK, kt * T::BK);
-  issue_a(kt * T::BK, aslot(S0{}));
-  issue_b(bstage(S0{}));
-  GE_SET_RS(kt * T::BK, (kt + 1) * T::BK);
-  issue_b(bstage(S1{}));
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(T::B_LOADS));
-  __builtin_amdgcn_s_barrier();
-  read_frags(aslot(S0{}), bstage(S0{}), 0, 0, f0);
-  for (; kt < nk; kt += T::NS) {
-    // each step fills the stages of step + 2 (A: on even steps, the slot of steps + 2, + 3)
-    GE_SET_RS((kt + 2) * T::BK, (kt + 2) * T::BK);
-    k_step(S0{}, kt);
-    GE_SET_RS((kt + 2) * T::BK, (kt + 3) * T::BK);
-    k_step(S1{}, kt + 1);
-    GE_SET_RS((kt + 4) * T::BK, (kt + 4) * T::BK);
-    k_step(S2{}, kt + 2);
-    GE_SET_RS((kt + 4) * T::BK, (kt + 5) * T::BK);
-    k_step(S3{}, kt + 3);
-  }
-#undef GE_SET_RS
-#undef GE_B_RS
-#undef GE_A_RS
-#undef GE_KLIVE
-#undef GE_KCLAMP
-  __builtin_amdgcn_s_waitcnt(kVmcnt0);                 // trailing zero-tile loads into the stages
-
-  // ---- RMS row statistic: the two lane halves hold different K of the same rows ----
-  if constexpr (ROWSTAT) {
-#pragma unroll
-    for (int j = 0; j < SS_J; ++j) {
-      const float s = ss[j] + __shfl_xor(ss[j], 32);
-      if (ss_owner && lhalf == 0) row_ss[wm0 + 32 * (ss_j0 + j) + lrow] = s;
-    }
-    __syncthreads();
-  }
-
-  // ---- epilogue, two phases per 32-row block of the wave's tile ----
-  // Phase 1 (registers -> LDS): the per-row linear part t = acc * alpha * s[m] (for the
-  // pairwise op the finished product act(t_gate) * t_up) goes to a wave-private fp32
-  // block in LDS, rows padded by 16 bytes so the 32 rows written at one column spread
-  // over all banks.  Phase 2 (LDS -> HBM): each lane takes 4 consecutive columns of a
-  // row, adds the column bias, applies the activation, adds the residual, folds |y|
-  // into AMAX (fp32, before rounding), converts and stores; one instruction covers whole
-  // rows, so residual loads and output stores are fully coalesced.
-  const uint32_t flags = p.flags;
-  const bool has_bias = (flags & F_BIAS) != 0;
-  const bool has_res = (flags & F_RESIDUAL) != 0;
-  const bool has_rs = (flags & F_ROW_SCALE) != 0;
-  const bool has_rms = ROWSTAT && (flags & F_ROW_RMS) != 0;
-  const float alpha = (flags & F_SCALE) ? p.alpha : 1.0f;
-  const float inv_k = K > 0 ? 1.0f / (float)K : 0.0f;
-
-  constexpr int EP_LD = T::EP_LD;                       // floats per LDS row
-  constexpr int LPR = T::WN / 4;                        // phase-2 lanes per row
-  constexpr int RPP = 64 / LPR;                         // rows per phase-2 pass
-  constexpr int PASSES = 32 / RPP;
-  __syncthreads();                                      // every wave is done with the stages
-  float* ep = (float*)((wave < 2 ? aslot0 : aslot1) + (wave & 1) * T::EP_WAVE_BYTES);
-
-  const int p2_row = lane / LPR, p2_col = 4 * (lane % LPR);
-  const int gcol = n0 + wn0 + p2_col;
-  const bool col_ok = gcol < N;
-  float bias4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (has_bias) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.bias + n0, (int64_t)(N - n0) * 2);
-    const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(rs, col_ok ? (uint32_t)(gcol - n0) * 2u : kOOB, 0, 0);
-    bias4[0] = bf16_lo(w[0]);
-    bias4[1] = bf16_hi(w[0]);
-    bias4[2] = bf16_lo(w[1]);
-    bias4[3] = bf16_hi(w[1]);
-  }
-  const int esize = FP8 ? 1 : 2;
-  void* y_base = (unsigned char*)p.Y + (b * p.sy + (int64_t)m0 * p.ldy + n0) * esize;
-  const __amdgpu_buffer_rsrc_t y_rs =
-      make_rsrc(y_base, ((int64_t)(M - 1 - m0) * p.ldy + (N - n0)) * esize);
-  const __amdgpu_buffer_rsrc_t r_rs =
-      has_res ? make_rsrc(p.R + b * p.sr + (int64_t)m0 * p.ldr + n0, ((int64_t)(M - 1 - m0) * p.ldr + (N - n0)) * 2)
-              : y_rs;
-  const uint32_t ldy_b = (uint32_t)p.ldy * (uint32_t)esize, ldr_b = (uint32_t)p.ldr * 2u;
-  const uint32_t col_y = col_ok ? (uint32_t)(wn0 + p2_col) * (uint32_t)esize : kOOB;
-  const uint32_t col_r = col_ok ? (uint32_t)(wn0 + p2_col) * 2u : kOOB;
-
-  uint32_t amax_bits = 0;
-  auto phase2 = [&](int j, auto res_c) {
-    constexpr bool RES = decltype(res_c)::value;
-    u32x2_t rv[PASSES];
-    if constexpr (RES) {
-#pragma unroll
-      for (int ps = 0; ps < PASSES; ++ps) {
-        const int ml = wm0 + 32 * j + ps * RPP + p2_row;
-        const uint32_t off = (m0 + ml < M) ? (uint32_t)ml * ldr_b + col_r : kOOB;
-        rv[ps] = __builtin_amdgcn_raw_buffer_load_b64(r_rs, off | (col_r & kOOB), 0, 0);
-      }
-    }
-    f32x4_t vv[PASSES];
-#pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) vv[ps] = *(const f32x4_t*)(ep + (ps * RPP + p2_row) * EP_LD + p2_col);
-#pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
-      const int r = ps * RPP + p2_row;
-      const int ml = wm0 + 32 * j + r;
-      const bool ok = (m0 + ml < M) & col_ok;
-      const f32x4_t v = vv[ps];
-      float y[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (T::PAIR) {
-          y[e] = v[e];
-        } else {
-          y[e] = activate<ACT>(v[e] + bias4[e]);
-        }
-      }
-      if constexpr (RES) {
-        y[0] += bf16_lo(rv[ps][0]);
-        y[1] += bf16_hi(rv[ps][0]);
-        y[2] += bf16_lo(rv[ps][1]);
-        y[3] += bf16_hi(rv[ps][1]);
-      }
-      const uint32_t m01 = max(__float_as_uint(y[0]) & 0x7FFFFFFFu, __float_as_uint(y[1]) & 0x7FFFFFFFu);
-      const uint32_t m23 = max(__float_as_uint(y[2]) & 0x7FFFFFFFu, __float_as_uint(y[3]) & 0x7FFFFFFFu);
-      amax_bits = ok ? max(amax_bits, max(m01, m23)) : amax_bits;
-      const uint32_t yoff = ok ? (uint32_t)ml * ldy_b + col_y : kOOB;
-      if constexpr (FP8) {
-        const float qs = p.qscale;
-        float z[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) z[e] = fminf(fmaxf(y[e] * qs, -448.0f), 448.0f);
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(z[0], z[1], 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(z[2], z[3], w, true);
-        __builtin_amdgcn_raw_buffer_store_b32((unsigned)w, y_rs, yoff, 0, 0);
-      } else {
-        u32x2_t w;
-        w[0] = pack_bf16x2(y[0], y[1]);
-        w[1] = pack_bf16x2(y[2], y[3]);
-        __builtin_amdgcn_raw_buffer_store_b64(w, y_rs, yoff, 0, 0);
-      }
-    }
-  };
-
-#pragma unroll
-  for (int j = 0; j < T::FM; ++j) {
-    const int ml = wm0 + 32 * j + lrow;
-    float rscale = alpha;
-    if constexpr (ROWSTAT) {
-      if (has_rms) rscale *= __builtin_amdgcn_rsqf(row_ss[ml] * inv_k + p.eps);
-    }
-    if (has_rs) rscale *= (m0 + ml < M) ? p.row_scale[(int64_t)b * M + m0 + ml] : 0.0f;
-    // phase 1: lane's row lrow, columns 32i + 8g + 4*lhalf + e of the wave's block
-#pragma unroll
-    for (int i = 0; i < T::FN; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4_t t;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if constexpr (T::PAIR) {
-            t[e] = activate<ACT>(acc[i][j][4 * g + e] * rscale) * (acc2[i][j][4 * g + e] * rscale);
-          } else {
-            t[e] = acc[i][j][4 * g + e] * rscale;
-          }
-        }
-        *(f32x4_t*)(ep + lrow * EP_LD + 32 * i + 8 * g + 4 * lhalf) = t;
-      }
-    // phase 2 reads what this wave just wrote; a wave's LDS operations complete in order
-    if (has_res)
-      phase2(j, std::integral_constant<bool, true>{});
-    else
-      phase2(j, std::integral_constant<bool, false>{});
-  }
-
-  // ---- AMAX ----
-  // Wave max on the |y| bit patterns (integer max keeps NaN; non-negative floats order like
-  // their bit patterns), then a workgroup max.  Each workgroup stores its partial maximum
-  // in its own workspace slot (no contended read-modify-write), waits for the store to be
-  // performed at device scope, and takes a ticket from the counter of its dispatch group
-  // (workgroup id mod 8 = the XCD it runs on).  The workgroup completing a group takes a
-  // ticket from the top counter; the one completing the top counter is last: every slot is
-  // in place, it reduces them and publishes *amax.  Counters are reset by the workgroup
-  // that completes them, so the workspace is zero again when the kernel ends.
-  if (flags & F_AMAX) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const uint32_t o = (uint32_t)__shfl_xor((int)amax_bits, off);
-      amax_bits = o > amax_bits ? o : amax_bits;
-    }
-    if (lane == 0) wave_amax[wave] = amax_bits;
-    __syncthreads();
-    const uint32_t total = (uint32_t)p.tiles_m * (uint32_t)p.tiles_n * (uint32_t)p.batch;
-    if (tid == 0) {
-      uint32_t m = wave_amax[0];
-#pragma unroll
-      for (int w = 1; w < T::WAVES; ++w) m = wave_amax[w] > m ? wave_amax[w] : m;
-      const uint32_t wg = blockIdx.x;
-      __hip_atomic_store(&p.ws[kAmaxSlot0 + wg], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __builtin_amdgcn_s_waitcnt(kVmcnt0);              // slot performed before the ticket
-      const uint32_t grp = wg % kAmaxGroups;
-      const uint32_t gsize = (total + kAmaxGroups - 1u - grp) / kAmaxGroups;
-      const uint32_t ngroups = total < kAmaxGroups ? total : kAmaxGroups;
-      uint32_t* gctr = &p.ws[grp * kAmaxCounterStride];
-      uint32_t* tctr = &p.ws[kAmaxGroups * kAmaxCounterStride];
-      bool last = false;
-      if (__hip_atomic_fetch_add(gctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gsize - 1u) {
-        __hip_atomic_exchange(gctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (__hip_atomic_fetch_add(tctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ngroups - 1u) {
-          __hip_atomic_exchange(tctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          last = true;
-        }
-      }
-      wave_amax[0] = last ? 1u : 0u;
-    }
-    __syncthreads();
-    if (wave_amax[0]) {                                  // uniform: the last workgroup
-      uint32_t mm = 0;
-      for (uint32_t i = (uint32_t)tid; i < total; i += T::NT)
-        mm = max(mm, __hip_atomic_load(&p.ws[kAmaxSlot0 + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) mm = max(mm, (uint32_t)__shfl_xor((int)mm, off));
-      __syncthreads();
-      if (lane == 0) wave_amax[wave] = mm;
-      __syncthreads();
-      if (tid == 0) {
-        uint32_t v = wave_amax[0];
-#pragma unroll
-        for (int w = 1; w < T::WAVES; ++w) v = max(v, wave_amax[w]);
-        __hip_atomic_store(p.amax, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
-}
-
 __global__ void amax_zero_kernel(uint32_t* amax) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *amax = 0u;
-}
-
-template <class T>
-constexpr TileInfo info_of() {
-  return TileInfo{T::BM, T::BN, T::NT, T::WAVES, T::PAIR, T::LDS};
-}
-
-template <class T, int ACT, bool FP8, bool ROWSTAT>
-void launch_k(const Params& p, hipStream_t s, unsigned grid) {
-  if (p.K % 64 != 0)
-    hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, FP8, ROWSTAT, true>), dim3(grid), dim3(T::NT), 0, s, p);
-  else
-    hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, FP8, ROWSTAT, false>), dim3(grid), dim3(T::NT), 0, s, p);
-}
-
-template <class T, int ACT, bool FP8>
-hipError_t launch_t(const Params& p, hipStream_t s) {
-  const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * p.batch;
-  if (grid <= 0) return hipSuccess;
-  if (p.flags & F_ROW_RMS)
-    launch_k<T, ACT, FP8, true>(p, s, (unsigned)grid);
-  else
-    launch_k<T, ACT, FP8, false>(p, s, (unsigned)grid);
-  return hipGetLastError();
-}
-
-template <class T>
-hipError_t launch_tile(int act, bool fp8, const Params& p, hipStream_t s) {
-  switch (act) {
-    case ACT_NONE: return fp8 ? launch_t<T, ACT_NONE, true>(p, s) : launch_t<T, ACT_NONE, false>(p, s);
-    case ACT_RELU: return fp8 ? launch_t<T, ACT_RELU, true>(p, s) : launch_t<T, ACT_RELU, false>(p, s);
-    case ACT_GELU_TANH:
-      return fp8 ? launch_t<T, ACT_GELU_TANH, true>(p, s) : launch_t<T, ACT_GELU_TANH, false>(p, s);
-    case ACT_SILU: return fp8 ? launch_t<T, ACT_SILU, true>(p, s) : launch_t<T, ACT_SILU, false>(p, s);
-    default: return hipErrorInvalidValue;
-  }
 }
 
 }  // namespace
 
 TileInfo tile_info(TileKind kind) {
   switch (kind) {
-    case TILE_256x256: return info_of<T256>();
-    case TILE_256x128_PAIR: return info_of<T256P>();
-    case TILE_128x128: return info_of<T128>();
-    case TILE_64x64: return info_of<T64>();
-    case TILE_128x128_PAIR: return info_of<T128P>();
+    case TILE_256x256: return tile_info_256x256();
+    case TILE_256x128_PAIR: return tile_info_256x128_pair();
+    case TILE_128x128: return tile_info_128x128();
+    case TILE_64x64: return tile_info_64x64();
+    case TILE_128x128_PAIR: return tile_info_128x128_pair();
     default: return TileInfo{0, 0, 0, 0, false, 0};
   }
 }
 
 hipError_t launch_fused(TileKind kind, int act, bool fp8_out, const Params& p, hipStream_t stream) {
   switch (kind) {
-    case TILE_256x256: return launch_tile<T256>(act, fp8_out, p, stream);
-    case TILE_256x128_PAIR: return launch_tile<T256P>(act, fp8_out, p, stream);
-    case TILE_128x128: return launch_tile<T128>(act, fp8_out, p, stream);
-    case TILE_64x64: return launch_tile<T64>(act, fp8_out, p, stream);
-    case TILE_128x128_PAIR: return launch_tile<T128P>(act, fp8_out, p, stream);
+    case TILE_256x256: return launch_tile_256x256(act, fp8_out, p, stream);
+    case TILE_256x128_PAIR: return launch_tile_256x128_pair(act, fp8_out, p, stream);
+    case TILE_128x128: return launch_tile_128x128(act, fp8_out, p, stream);
+    case TILE_64x64: return launch_tile_64x64(act, fp8_out, p, stream);
+    case TILE_128x128_PAIR: return launch_tile_128x128_pair(act, fp8_out, p, stream);
     default: return hipErrorInvalidValue;
   }
 }
