@@ -77,6 +77,7 @@ hipError_t launch_amax_zero(uint32_t* amax, hipStream_t stream);
 constexpr uint32_t kAmaxGroups = 8;
 constexpr uint32_t kAmaxCounterStride = 64;
 constexpr uint32_t kAmaxSlot0 = 1024;
+constexpr uint32_t kAmaxFlatGrid = 64;   // up to this many workgroups take one ticket each on the top counter
 inline size_t amax_workspace_bytes(int64_t workgroups) { return 4 * ((size_t)kAmaxSlot0 + (size_t)workgroups); }
 
 }  // namespace ge

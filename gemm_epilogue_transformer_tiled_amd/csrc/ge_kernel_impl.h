@@ -553,17 +553,19 @@ void fused_gemm_epilogue(Params p) {
   const uint32_t col_r = col_ok ? (uint32_t)(wn0 + p2_col) * 2u : kOOB;
 
   uint32_t amax_bits = 0;
-  auto phase2 = [&](int j, auto res_c) {
-    constexpr bool RES = decltype(res_c)::value;
-    u32x2_t rv[PASSES];
-    if constexpr (RES) {
+  // Residual rows of a 32-row block, in phase-2 layout.  Two blocks are kept: the loads of
+  // block j+1 are issued before block j is processed, so their latency is hidden.
+  u32x2_t rvb[2][PASSES];
+  auto load_res = [&](int j, u32x2_t* rv) {
 #pragma unroll
-      for (int ps = 0; ps < PASSES; ++ps) {
-        const int ml = wm0 + 32 * j + ps * RPP + p2_row;
-        const uint32_t off = (m0 + ml < M) ? (uint32_t)ml * ldr_b + col_r : kOOB;
-        rv[ps] = __builtin_amdgcn_raw_buffer_load_b64(r_rs, off | (col_r & kOOB), 0, 0);
-      }
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int ml = wm0 + 32 * j + ps * RPP + p2_row;
+      const uint32_t off = (m0 + ml < M) ? (uint32_t)ml * ldr_b + col_r : kOOB;
+      rv[ps] = __builtin_amdgcn_raw_buffer_load_b64(r_rs, off | (col_r & kOOB), 0, 0);
     }
+  };
+  auto phase2 = [&](int j, auto res_c, const u32x2_t* rv) {
+    constexpr bool RES = decltype(res_c)::value;
     f32x4_t vv[PASSES];
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) vv[ps] = *(const f32x4_t*)(ep + (ps * RPP + p2_row) * EP_LD + p2_col);
@@ -609,8 +611,10 @@ void fused_gemm_epilogue(Params p) {
     }
   };
 
+  if (has_res) load_res(0, rvb[0]);
 #pragma unroll
   for (int j = 0; j < T::FM; ++j) {
+    if (has_res && j + 1 < T::FM) load_res(j + 1, rvb[(j + 1) & 1]);
     const int ml = wm0 + 32 * j + lrow;
     float rscale = alpha;
     if constexpr (ROWSTAT) {
@@ -634,10 +638,11 @@ void fused_gemm_epilogue(Params p) {
         *(f32x4_t*)(ep + lrow * EP_LD + 32 * i + 8 * g + 4 * lhalf) = t;
       }
     // phase 2 reads what this wave just wrote; a wave's LDS operations complete in order
-    if (has_res)
-      phase2(j, std::integral_constant<bool, true>{});
-    else
-      phase2(j, std::integral_constant<bool, false>{});
+    if (has_res) {
+      phase2(j, std::integral_constant<bool, true>{}, rvb[j & 1]);
+    } else {
+      phase2(j, std::integral_constant<bool, false>{}, rvb[0]);
+    }
   }
 
   // ---- AMAX ----
@@ -647,8 +652,9 @@ void fused_gemm_epilogue(Params p) {
   // performed at device scope, and takes a ticket from the counter of its dispatch group
   // (workgroup id mod 8 = the XCD it runs on).  The workgroup completing a group takes a
   // ticket from the top counter; the one completing the top counter is last: every slot is
-  // in place, it reduces them and publishes *amax.  Counters are reset by the workgroup
-  // that completes them, so the workspace is zero again when the kernel ends.
+  // in place, it reduces them and publishes *amax.  Grids of at most kAmaxFlatGrid
+  // workgroups take their ticket from the top counter directly.  Counters are reset by the
+  // workgroup that completes them, so the workspace is zero again when the kernel ends.
   if (flags & F_AMAX) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -671,7 +677,13 @@ void fused_gemm_epilogue(Params p) {
       uint32_t* gctr = &p.ws[grp * kAmaxCounterStride];
       uint32_t* tctr = &p.ws[kAmaxGroups * kAmaxCounterStride];
       bool last = false;
-      if (__hip_atomic_fetch_add(gctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gsize - 1u) {
+      if (total <= kAmaxFlatGrid) {
+        // small grids: one ticket on the top counter (saves a round trip on the critical path)
+        if (__hip_atomic_fetch_add(tctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == total - 1u) {
+          __hip_atomic_exchange(tctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          last = true;
+        }
+      } else if (__hip_atomic_fetch_add(gctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gsize - 1u) {
         __hip_atomic_exchange(gctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (__hip_atomic_fetch_add(tctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ngroups - 1u) {
           __hip_atomic_exchange(tctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
