@@ -233,7 +233,7 @@ def test_fp8_writer_over_every_bf16_value_in_range():
 # The five workloads at full size, in the benchmark's launch configuration.
 # ---------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", workloads.CONFIG_ORDER)
+@pytest.mark.parametrize("name", workloads.CONFIG_ORDER + ["f1"])
 def test_full_workload(name):
     w = workloads.WORKLOADS[name]
     inp = workloads.generate(w)

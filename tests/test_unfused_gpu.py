@@ -30,6 +30,7 @@ SHAPES = {
     "c3": dict(M=512, N=704, K=512),
     "c4": dict(M=512, N=512, K=1024),
     "c5": dict(M=512, N=1024, K=512),
+    "f1": dict(M=512, N=704, K=512),
 }
 
 

@@ -50,6 +50,19 @@ def test_rms_fold_is_row_scaling_over_k():
     assert np.allclose(ratio[base != 0], np.broadcast_to(g[:, None], base.shape)[base != 0], rtol=2 ** -7)
 
 
+def test_rmsnorm_mlp_folds_the_gain_into_both_weights():
+    w = workloads.WORKLOADS["f1"].with_shape(M=8, N=16, K=32)
+    inp = workloads.generate(w)
+    g = inp["g"]
+    for base_key, key in (("W_base", "B"), ("W2_base", "B2")):
+        base = oracle.decode_bf16(inp[base_key])[0]
+        folded = oracle.decode_bf16(inp[key])[0]
+        ratio = folded / np.where(base == 0, 1, base)
+        assert np.allclose(ratio[base != 0], np.broadcast_to(g[:, None], base.shape)[base != 0], rtol=2 ** -7)
+    assert not np.array_equal(inp["W_base"], inp["W2_base"])
+    assert w.pairwise and w.op("pairwise")[1] == "none" and w.has("row_rms")
+
+
 def test_flops_and_bytes_of_the_full_workloads():
     W = workloads.WORKLOADS
     assert W["c1"].flops() == 2 * 256 ** 3

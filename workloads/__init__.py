@@ -128,6 +128,16 @@ WORKLOADS: Dict[str, Workload] = {
         description="M=N=K=8192, bias N(0,0.1), GELU_tanh, fp8 e4m3 output with scale 112 and fp32 AMAX"),
 }
 
+# Beyond the five configurations: the RMSNorm-MLP of the superoptimizer write-up (section 10),
+# the row RMS statistic feeding the pairwise product with no activation, out = up * gate, at
+# the SwiGLU shapes.
+WORKLOADS["f1"] = Workload(
+    name="f1", config_id=6, batch=1, M=8192, N=11008, K=4096,
+    chain=(("row_rms", 1e-6), ("pairwise", "none")),
+    a_var="1", b_var="1/K",
+    description="RMSNorm-MLP: (S*X@Wg')*(S*X@Wu'), S = 1/rms(X), gain U(0.5,1.5) folded into Wg and Wu, "
+                "X[8192x4096] N(0,1), W[4096x11008] N(0,1/4096), no activation")
+
 CONFIG_ORDER: List[str] = ["c1", "c2", "c3", "c4", "c5"]
 
 
@@ -141,6 +151,12 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _fold(w_bits: np.ndarray, g: np.ndarray) -> np.ndarray:
+    """bf16(fp32(W[k, n]) * g[k]) for W [batch, K, N] as bf16 bits."""
+    w_f32 = (w_bits.astype(np.uint32) << 16).view(np.float32)
+    return f32_to_bf16_bits(w_f32 * g[None, :, None])
 
 
 def _normal_bf16(config_id: int, tensor_id: int, shape, var: float) -> np.ndarray:
@@ -168,18 +184,21 @@ def generate(w: Workload, sensitive: bool = False, seed_offset: int = 0) -> Dict
     out: Dict[str, np.ndarray] = {}
     a_var = 1.0 if sensitive else _var(w.a_var, K)
     out["A"] = _normal_bf16(cid, T_A, (b, M, K), a_var)
+    g = None
     if w.has("row_rms"):
-        # gain g[k] ~ U(0.5, 1.5) folded into the base weight along the contraction axis
+        # gain g[k] ~ U(0.5, 1.5) folded into the base weight(s) along the contraction axis
         g = _rng(cid, T_G).uniform(0.5, 1.5, size=K).astype(np.float32)
         w_base = _normal_bf16(cid, T_W, (b, K, N), _var(w.b_var, K))
-        w_f32 = (w_base.astype(np.uint32) << 16).view(np.float32)
         out["g"] = g
         out["W_base"] = w_base
-        out["B"] = f32_to_bf16_bits(w_f32 * g[None, :, None])
+        out["B"] = _fold(w_base, g)
     else:
         out["B"] = _normal_bf16(cid, T_B, (b, K, N), _var(w.b_var, K))
     if w.pairwise:
         out["B2"] = _normal_bf16(cid, T_B2, (b, K, N), _var(w.b_var, K))
+        if g is not None:            # RMSNorm-MLP: the same gain scales X before both products
+            out["W2_base"] = out["B2"]
+            out["B2"] = _fold(out["B2"], g)
     if w.has("bias"):
         if sensitive:
             out["bias"] = np.zeros(N, dtype=np.uint16)
