@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libgemm_epilogue.so")
 GE_OK, GE_ERR_INVALID_ARG, GE_ERR_UNSUPPORTED, GE_ERR_DEVICE, GE_ERR_HIP = range(5)
 GE_DT_BF16, GE_DT_FP8_E4M3, GE_DT_FP32 = range(3)
 GE_ACT_NONE, GE_ACT_RELU, GE_ACT_GELU_TANH, GE_ACT_SILU = range(4)
+GE_LAYOUT_KN, GE_LAYOUT_NK = range(2)
 (GE_OP_SCALE, GE_OP_ROW_RMS, GE_OP_ROW_SCALE, GE_OP_BIAS_COL, GE_OP_ACT, GE_OP_PAIRWISE_ACT_MUL,
  GE_OP_RESIDUAL, GE_OP_AMAX, GE_OP_QUANT_FP8) = range(9)
 GE_MAX_OPS = 8
@@ -42,6 +43,7 @@ class ge_desc_t(ctypes.Structure):
         ("a_type", ctypes.c_int32), ("b_type", ctypes.c_int32), ("y_type", ctypes.c_int32),
         ("n_ops", ctypes.c_int32),
         ("ops", ge_op_t * GE_MAX_OPS),
+        ("b_layout", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 
@@ -161,16 +163,19 @@ def make_desc(batch: int, M: int, N: int, K: int, ops: Sequence[Tuple[int, int, 
               y_type: int = GE_DT_BF16, lda: Optional[int] = None, ldb: Optional[int] = None,
               ldy: Optional[int] = None, ldr: Optional[int] = None, stride_a: Optional[int] = None,
               stride_b: Optional[int] = None, stride_y: Optional[int] = None,
-              stride_r: Optional[int] = None, a_type: int = GE_DT_BF16, b_type: int = GE_DT_BF16) -> ge_desc_t:
-    """Descriptor for packed row-major operands unless leading dims / strides are given."""
+              stride_r: Optional[int] = None, a_type: int = GE_DT_BF16, b_type: int = GE_DT_BF16,
+              b_layout: int = GE_LAYOUT_KN) -> ge_desc_t:
+    """Descriptor for packed row-major operands unless leading dims / strides are given.
+    b_layout GE_LAYOUT_NK: B (and B2) are [batch][N][K]."""
     d = ge_desc_t()
     d.batch, d.M, d.N, d.K = batch, M, N, K
+    d.b_layout = b_layout
     d.lda = K if lda is None else lda
-    d.ldb = N if ldb is None else ldb
+    d.ldb = (K if b_layout == GE_LAYOUT_NK else N) if ldb is None else ldb
     d.ldy = N if ldy is None else ldy
     d.ldr = N if ldr is None else ldr
     d.stride_a = M * d.lda if stride_a is None else stride_a
-    d.stride_b = K * d.ldb if stride_b is None else stride_b
+    d.stride_b = (N if b_layout == GE_LAYOUT_NK else K) * d.ldb if stride_b is None else stride_b
     d.stride_y = M * d.ldy if stride_y is None else stride_y
     d.stride_r = M * d.ldr if stride_r is None else stride_r
     d.a_type, d.b_type, d.y_type = a_type, b_type, y_type

@@ -17,8 +17,8 @@ BUILD_DIR = os.path.join(HERE, "_build")
 # library -> its sources
 TARGETS = {
     os.path.join(HERE, "libgemm_epilogue.so"): [
-        "ge_tile_256x256.hip", "ge_tile_256x128_pair.hip", "ge_tile_128x128.hip", "ge_tile_64x64.hip",
-        "ge_tile_128x128_pair.hip", "ge_kernels.hip", "api.cpp"],
+        f"ge_tile_{t}_{lay}.hip" for t in ("256x256", "256x128_pair", "128x128", "64x64", "128x128_pair")
+        for lay in ("kn", "nk")] + ["ge_kernels.hip", "api.cpp"],
     os.path.join(HERE, "libge_baselines.so"): ["baselines.hip"],
 }
 LIB = os.path.join(HERE, "libgemm_epilogue.so")
@@ -44,7 +44,7 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     sources = [src for srcs in TARGETS.values() for src in srcs]
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(sources)) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(sources), os.cpu_count() or 4)) as ex:
         objs = dict(zip(sources, ex.map(_compile, sources)))
     for lib, srcs in TARGETS.items():
         tmp = lib + ".tmp"

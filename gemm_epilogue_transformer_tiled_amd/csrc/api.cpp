@@ -92,6 +92,9 @@ ge_status_t gemm_epilogue_validate(const ge_desc_t* d) {
   if (d->n_ops < 0 || d->n_ops > GE_MAX_OPS) return GE_ERR_INVALID_ARG;
   if (d->lda < 0 || d->ldb < 0 || d->ldy < 0 || d->ldr < 0) return GE_ERR_INVALID_ARG;
   if (d->stride_a < 0 || d->stride_b < 0 || d->stride_y < 0 || d->stride_r < 0) return GE_ERR_INVALID_ARG;
+  if (d->b_layout != GE_LAYOUT_KN && d->b_layout != GE_LAYOUT_NK) return GE_ERR_INVALID_ARG;
+  if (d->reserved != 0) return GE_ERR_INVALID_ARG;
+  const bool bnk = d->b_layout == GE_LAYOUT_NK;
 
   // op chain: known kinds, canonical order, each at most once, exclusive pairs
   int last_rank = -1;
@@ -128,7 +131,8 @@ ge_status_t gemm_epilogue_validate(const ge_desc_t* d) {
   // layout
   const bool res = has_op(d, GE_OP_RESIDUAL);
   if (d->M > 0 && d->lda < d->K) return GE_ERR_INVALID_ARG;
-  if (d->K > 0 && d->ldb < d->N) return GE_ERR_INVALID_ARG;
+  if (!bnk && d->K > 0 && d->ldb < d->N) return GE_ERR_INVALID_ARG;
+  if (bnk && d->N > 0 && d->ldb < d->K) return GE_ERR_INVALID_ARG;
   if (d->M > 0 && d->ldy < d->N) return GE_ERR_INVALID_ARG;
   if (res && d->M > 0 && d->ldr < d->N) return GE_ERR_INVALID_ARG;
   if (d->batch > 1 && d->stride_y == 0 && d->M > 0 && d->N > 0) return GE_ERR_INVALID_ARG;  // batches would race
@@ -145,7 +149,8 @@ ge_status_t gemm_epilogue_validate(const ge_desc_t* d) {
   // masked accesses with an offset of 2^31; every offset a tile can form (one tile and one
   // K step past the end included) must therefore stay below 2^31.
   if (extent_elems(d->M + 256, d->K + 64, d->lda) * 2 > kMaxExtent) return GE_ERR_UNSUPPORTED;
-  if (extent_elems(d->K + 128, d->N, d->ldb) * 2 > kMaxExtent) return GE_ERR_UNSUPPORTED;
+  if (!bnk && extent_elems(d->K + 128, d->N, d->ldb) * 2 > kMaxExtent) return GE_ERR_UNSUPPORTED;
+  if (bnk && extent_elems(d->N + 256, d->K + 64, d->ldb) * 2 > kMaxExtent) return GE_ERR_UNSUPPORTED;
   if (extent_elems(d->M + 256, d->N, d->ldy) * esize > kMaxExtent) return GE_ERR_UNSUPPORTED;
   if (res && extent_elems(d->M + 256, d->N, d->ldr) * 2 > kMaxExtent) return GE_ERR_UNSUPPORTED;
   // grid: one workgroup per 64x64 tile at most
@@ -192,6 +197,7 @@ ge_status_t gemm_epilogue_create(const ge_desc_t* desc, ge_handle_t* out) {
   if (has_op(desc, GE_OP_BIAS_COL)) p->flags |= ge::F_BIAS;
   if (has_op(desc, GE_OP_RESIDUAL)) p->flags |= ge::F_RESIDUAL;
   if (has_op(desc, GE_OP_AMAX)) p->flags |= ge::F_AMAX;
+  if (desc->b_layout == GE_LAYOUT_NK) p->flags |= ge::F_B_NK;
   const ge::TileInfo ti = ge::tile_info(p->tile);
   p->tiles_m = ceil_div(desc->M, ti.bm);
   p->tiles_n = ceil_div(desc->N, ti.bn);
@@ -286,8 +292,8 @@ const char* gemm_epilogue_status_string(ge_status_t s) {
 ge_status_t gemm_epilogue_describe(ge_handle_t h, char* buf, size_t len) {
   if (!h || !buf || len == 0) return GE_ERR_INVALID_ARG;
   const ge::TileInfo ti = ge::tile_info(h->tile);
-  std::snprintf(buf, len, "tile=%dx%dx64 pair=%d threads=%d lds=%d grid=%lld act=%d fp8=%d flags=0x%x",
-                ti.bm, ti.bn, ti.pair ? 1 : 0, ti.threads, ti.lds_bytes,
+  std::snprintf(buf, len, "tile=%dx%dx64 pair=%d b=%s threads=%d lds=%d grid=%lld act=%d fp8=%d flags=0x%x",
+                ti.bm, ti.bn, ti.pair ? 1 : 0, (h->flags & ge::F_B_NK) ? "NK" : "KN", ti.threads, ti.lds_bytes,
                 (long long)(h->tiles_m * h->tiles_n * h->desc.batch), h->act, h->fp8_out ? 1 : 0,
                 (unsigned)h->flags);
   return GE_OK;

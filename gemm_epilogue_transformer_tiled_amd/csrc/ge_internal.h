@@ -14,6 +14,7 @@ enum : uint32_t {
   F_BIAS = 1u << 3,
   F_RESIDUAL = 1u << 4,
   F_AMAX = 1u << 5,
+  F_B_NK = 1u << 6,      // B and B2 given as [batch][N][K] (K contiguous)
 };
 
 enum Act : int { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_TANH = 2, ACT_SILU = 3 };
@@ -55,15 +56,20 @@ struct TileInfo {
 TileInfo tile_info(TileKind kind);
 
 // Per-tile instance sets (ge_tile_*.hip).
-hipError_t launch_tile_256x256(int act, bool fp8_out, const Params& p, hipStream_t stream);
+hipError_t launch_tile_256x256_kn(int act, bool fp8_out, const Params& p, hipStream_t stream);
+hipError_t launch_tile_256x256_nk(int act, bool fp8_out, const Params& p, hipStream_t stream);
 TileInfo tile_info_256x256();
-hipError_t launch_tile_256x128_pair(int act, bool fp8_out, const Params& p, hipStream_t stream);
+hipError_t launch_tile_256x128_pair_kn(int act, bool fp8_out, const Params& p, hipStream_t stream);
+hipError_t launch_tile_256x128_pair_nk(int act, bool fp8_out, const Params& p, hipStream_t stream);
 TileInfo tile_info_256x128_pair();
-hipError_t launch_tile_128x128(int act, bool fp8_out, const Params& p, hipStream_t stream);
+hipError_t launch_tile_128x128_kn(int act, bool fp8_out, const Params& p, hipStream_t stream);
+hipError_t launch_tile_128x128_nk(int act, bool fp8_out, const Params& p, hipStream_t stream);
 TileInfo tile_info_128x128();
-hipError_t launch_tile_64x64(int act, bool fp8_out, const Params& p, hipStream_t stream);
+hipError_t launch_tile_64x64_kn(int act, bool fp8_out, const Params& p, hipStream_t stream);
+hipError_t launch_tile_64x64_nk(int act, bool fp8_out, const Params& p, hipStream_t stream);
 TileInfo tile_info_64x64();
-hipError_t launch_tile_128x128_pair(int act, bool fp8_out, const Params& p, hipStream_t stream);
+hipError_t launch_tile_128x128_pair_kn(int act, bool fp8_out, const Params& p, hipStream_t stream);
+hipError_t launch_tile_128x128_pair_nk(int act, bool fp8_out, const Params& p, hipStream_t stream);
 TileInfo tile_info_128x128_pair();
 
 // Enqueues the fused kernel.  `act` in Act, `fp8_out` selects the E4M3 writer.

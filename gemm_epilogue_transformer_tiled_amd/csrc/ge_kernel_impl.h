@@ -201,27 +201,43 @@ __device__ __forceinline__ void sched_group() {
 }
 
 // KMASK: K is not a multiple of 64, so one A slot straddles K and needs per-lane masking.
-template <class T, int ACT, bool FP8, bool ROWSTAT, bool KMASK>
+// BNK: B (and B2) are given as [N][K] (K contiguous) -- for instance W when the product is
+// dY @ W^T of a backward pass -- and are staged exactly like A: two steps at a time as
+// [BN][64] with 128-byte rows, fragments by plain 16-byte LDS reads.
+template <class T, int ACT, bool FP8, bool ROWSTAT, bool KMASK, bool BNK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(T::WPE, T::WPE)))
 void fused_gemm_epilogue(Params p) {
   // The LDS stages and slots are distinct arrays, so the compiler can tell that the direct
   // loads filling one never alias the fragment reads of another.
   __shared__ __attribute__((aligned(1024))) unsigned char aslot0[T::A_ALLOC];
   __shared__ __attribute__((aligned(1024))) unsigned char aslot1[T::A_ALLOC];
-  __shared__ __attribute__((aligned(1024))) unsigned char bstage0[T::B_STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char bstage1[T::B_STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char bstage2[T::B_STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char bstage3[T::B_STAGE];
+  // B buffers: [N][K] layout -- two slots of two steps each; [K][N] -- a ring of four stages.
+  constexpr int BNK_SLOT = T::NB * T::BN * T::A_ROWB;
+  constexpr int B_BUF = BNK ? BNK_SLOT : T::B_STAGE;
+  constexpr int B_BUF23 = BNK ? 16 : T::B_STAGE;
+  constexpr int BL = BNK ? BNK_SLOT / 1024 / T::WAVES : T::B_LOADS;   // B loads per wave per fill
+  static_assert(!BNK || (BL >= 1 && BNK_SLOT % (1024 * T::WAVES) == 0), "B slot loads divide over the waves");
+  static_assert(2 * T::A_ALLOC + 2 * B_BUF + 2 * B_BUF23 + 4096 <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) unsigned char bstage0[B_BUF];
+  __shared__ __attribute__((aligned(1024))) unsigned char bstage1[B_BUF];
+  __shared__ __attribute__((aligned(1024))) unsigned char bstage2[B_BUF23];
+  __shared__ __attribute__((aligned(1024))) unsigned char bstage3[B_BUF23];
   __shared__ float row_ss[ROWSTAT ? T::BM : 1];
   __shared__ uint32_t wave_amax[T::WAVES];
   static_assert(T::NS == 4, "four B stage arrays");
-  // B stage of step s, A slot of step s (two consecutive steps share a slot).
+  // B buffer of step s ([K][N]: its stage; [N][K]: its slot), A slot of step s (two
+  // consecutive steps share a slot).
   auto bstage = [&](auto s_c) -> unsigned char* {
     constexpr int S = decltype(s_c)::value % T::NS;
-    if constexpr (S == 0) return bstage0;
-    else if constexpr (S == 1) return bstage1;
-    else if constexpr (S == 2) return bstage2;
-    else return bstage3;
+    if constexpr (BNK) {
+      if constexpr (S / 2 == 0) return bstage0;
+      else return bstage1;
+    } else {
+      if constexpr (S == 0) return bstage0;
+      else if constexpr (S == 1) return bstage1;
+      else if constexpr (S == 2) return bstage2;
+      else return bstage3;
+    }
   };
   auto aslot = [&](auto s_c) -> unsigned char* {
     constexpr int S = decltype(s_c)::value % T::NS;
@@ -250,9 +266,14 @@ void fused_gemm_epilogue(Params p) {
   // an empty resource, which reads zeros.
   const uint16_t* a_base = p.A + b * p.sa + (int64_t)m0 * p.lda;
   const int64_t a_ext = ((int64_t)(M - 1 - m0) * p.lda + K) * 2;
-  const uint16_t* b_base = p.B + b * p.sb + n0;
-  const uint16_t* b2_base = T::PAIR ? p.B2 + b * p.sb + n0 : b_base;
-  const int64_t b_ext = K > 0 ? ((int64_t)(K - 1) * p.ldb + (N - n0)) * 2 : 0;
+  // [K][N]: the tile's columns start at n0; [N][K]: its rows start at n0 (like A's at m0)
+  const int64_t b_ofs = BNK ? (int64_t)n0 * p.ldb : (int64_t)n0;
+  const uint16_t* b_base = p.B + b * p.sb + b_ofs;
+  const uint16_t* b2_base = T::PAIR ? p.B2 + b * p.sb + b_ofs : b_base;
+  const int64_t b_ext = BNK ? ((int64_t)(N - 1 - n0) * p.ldb + K) * 2
+                            : (K > 0 ? ((int64_t)(K - 1) * p.ldb + (N - n0)) * 2 : 0);
+  __amdgpu_buffer_rsrc_t b_rs0 = make_rsrc(b_base, b_ext), b2_rs0 = b_rs0;   // ragged K, [N][K]
+  if constexpr (T::PAIR) b2_rs0 = make_rsrc(b2_base, b_ext);
   const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(a_base, a_ext);       // ragged K: fixed resource
 
   // ---- direct global->LDS loads: per-lane source offsets, fixed for the whole K loop ----
@@ -275,13 +296,21 @@ void fused_gemm_epilogue(Params p) {
   // B load t fills B_ROWS_PER_LOAD rows of one operand: lane -> row lane/B_CHUNKS (within
   // the load), physical chunk lane%B_CHUNKS, logical chunk ^ swz_b(row).  Rows past K fall
   // outside the extent; a column block past N gets the out-of-range offset.
-  uint32_t b_voff[T::B_LOADS];
+  // [N][K]: B load t (u = wave * BL + t over the operands) fills slot rows 8r .. 8r+7 of
+  // operand u / (BN/8), r = u % (BN/8), with A's lane mapping and swizzle; rows past N fall
+  // outside the extent (ldb >= K).
+  uint32_t b_voff[BL];
 #pragma unroll
-  for (int t = 0; t < T::B_LOADS; ++t) {
-    const int blk = (wave * T::B_LOADS + t) % T::B_LOADS_PER_OP;
-    const uint32_t row = (uint32_t)blk * T::B_ROWS_PER_LOAD + (uint32_t)(lane / T::B_CHUNKS);
-    const uint32_t lchunk = (uint32_t)(lane % T::B_CHUNKS) ^ swz_b<T::B_CHUNKS>(row);
-    b_voff[t] = (n0 + (int)lchunk * 8 < N) ? row * ldb2 + lchunk * 16u : kOOB;
+  for (int t = 0; t < BL; ++t) {
+    if constexpr (BNK) {
+      const uint32_t r = (uint32_t)(wave * BL + t) % (uint32_t)(T::BN / 8);
+      b_voff[t] = (uint32_t)(lane >> 3) * ldb2 + r * 8u * ldb2 + (a_x ^ (r & 3u)) * 16u;
+    } else {
+      const int blk = (wave * T::B_LOADS + t) % T::B_LOADS_PER_OP;
+      const uint32_t row = (uint32_t)blk * T::B_ROWS_PER_LOAD + (uint32_t)(lane / T::B_CHUNKS);
+      const uint32_t lchunk = (uint32_t)(lane % T::B_CHUNKS) ^ swz_b<T::B_CHUNKS>(row);
+      b_voff[t] = (n0 + (int)lchunk * 8 < N) ? row * ldb2 + lchunk * 16u : kOOB;
+    }
   }
 
   // Resources of the step starting at K column/row k0 (a multiple of 32, so a B step -- and,
@@ -292,8 +321,8 @@ void fused_gemm_epilogue(Params p) {
 #define GE_KLIVE(k0) (((k0) >= 0) & ((k0) < K))
 #define GE_A_RS(k0) make_rsrc(a_base + GE_KCLAMP(k0), GE_KLIVE(k0) ? a_ext - 2 * (int64_t)GE_KCLAMP(k0) : 0)
 #define GE_B_RS(base, k0) \
-  make_rsrc((const unsigned char*)(base) + (uint32_t)GE_KCLAMP(k0) * ldb2, \
-            GE_KLIVE(k0) ? b_ext - (int64_t)((uint32_t)GE_KCLAMP(k0) * ldb2) : 0)
+  make_rsrc((const unsigned char*)(base) + (uint32_t)GE_KCLAMP(k0) * (BNK ? 2u : ldb2), \
+            GE_KLIVE(k0) ? b_ext - (int64_t)((uint32_t)GE_KCLAMP(k0) * (BNK ? 2u : ldb2)) : 0)
 
   // A slot for steps k0/BK and k0/BK + 1; k0 may be negative (leading all-zero steps).
   // K a multiple of 64: `rs` is the step's resource and the offsets are fixed.  Otherwise the
@@ -314,7 +343,26 @@ void fused_gemm_epilogue(Params p) {
     }
   };
   // B stage of one step from its resources (rows past K fall outside the shrunk extent).
-  auto issue_b = [&](unsigned char* st) {
+  auto issue_b = [&](unsigned char* st, int k0) {
+    if constexpr (BNK) {
+#pragma unroll
+      for (int t = 0; t < BL; ++t) {
+        const uint32_t u = (uint32_t)(wave * BL + t);                  // wave-uniform
+        const uint32_t op = u / (uint32_t)(T::BN / 8), r = u % (uint32_t)(T::BN / 8);
+        uint32_t off = b_voff[t];
+        if constexpr (KMASK) {
+          const uint32_t c = a_x ^ (r & 3u);
+          off = ((uint32_t)(k0 + (int)(c * 8u)) < (uint32_t)K) ? off + (uint32_t)k0 * 2u : kOOB;
+        }
+        unsigned char* dst = st + op * (T::BN * T::A_ROWB) + r * 1024;
+        if (T::PAIR && op == 1)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(b2rs, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+      }
+      return;
+    }
+    (void)k0;
 #pragma unroll
     for (int t = 0; t < T::B_LOADS; ++t) {
       const int gblk = wave * T::B_LOADS + t;           // wave-uniform
@@ -356,6 +404,12 @@ void fused_gemm_epilogue(Params p) {
       b_frag[op][i] = (uint32_t)(op * T::B_BYTES) + kl * T::B_ROWB +
                       ((lchunk ^ swz_b<T::B_CHUNKS>(kl)) << 4) + (ncol & 7u) * 2u;
     }
+  // [N][K]: like A -- lane reads slot row wn0 + 32i + lane%32 of operand op, logical chunk
+  // 4h + 2g + lane/32; i and op are immediate offsets.
+  uint32_t bnk_frag[2 * T::GROUPS];
+#pragma unroll
+  for (int hg = 0; hg < 2 * T::GROUPS; ++hg)
+    bnk_frag[hg] = (uint32_t)(wn0 + lrow) * T::A_ROWB + (((uint32_t)(2 * hg + lhalf) ^ swz_a(lrow)) << 4);
 
   f32x16_t acc[T::FN][T::FM];
   f32x16_t acc2[T::PAIR ? T::FN : 1][T::PAIR ? T::FM : 1];
@@ -384,6 +438,15 @@ void fused_gemm_epilogue(Params p) {
 #pragma unroll
     for (int j = 0; j < T::FM; ++j)
       f.a[j] = *(const bf16x8_t*)(as + a_frag[h * T::GROUPS + g] + j * 32 * T::A_ROWB);
+    if constexpr (BNK) {
+#pragma unroll
+      for (int op = 0; op < T::NB; ++op)
+#pragma unroll
+        for (int i = 0; i < T::FN; ++i)
+          f.b[op][i] = *(const bf16x8_t*)(bs + bnk_frag[h * T::GROUPS + g] + op * T::BN * T::A_ROWB +
+                                          i * 32 * T::A_ROWB);
+      return;
+    }
 #pragma unroll
     for (int op = 0; op < T::NB; ++op)
 #pragma unroll
@@ -441,17 +504,19 @@ void fused_gemm_epilogue(Params p) {
     using Cur = std::integral_constant<int, S>;
     using Next = std::integral_constant<int, S + 1>;
     using Fill = std::integral_constant<int, S + 2>;
-    issue_b(bstage(Fill{}));
+    // [K][N]: B every step; [N][K]: B with A, on even steps only
+    constexpr int B_NOW = BNK ? (EVEN ? BL : 0) : BL;
+    if constexpr (!BNK || EVEN) issue_b(bstage(Fill{}), (kt + 2) * T::BK);
     if constexpr (EVEN) issue_a((kt + 2) * T::BK, aslot(Fill{}));
     static_assert(T::GROUPS == 2, "two groups per step");
     read_frags(aslot(Cur{}), bstage(Cur{}), S % 2, 1, f1);
     mfmas(f0);
-    sched_group<MFMAS_PER_GROUP, EVEN ? T::A_LOADS + T::B_LOADS : T::B_LOADS, READS_PER_GROUP>();
+    sched_group<MFMAS_PER_GROUP, EVEN ? T::A_LOADS + B_NOW : B_NOW, READS_PER_GROUP>();
     // No memory fence: the later loads stay in flight across the barrier.
     if constexpr (EVEN)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(T::A_LOADS + T::B_LOADS));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(T::A_LOADS + B_NOW));
     else
-      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(T::B_LOADS));
+      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(B_NOW));
     __builtin_amdgcn_s_barrier();
     read_frags(aslot(Next{}), bstage(Next{}), (S + 1) % 2, 0, f0);
     mfmas(f1);
@@ -464,18 +529,26 @@ void fused_gemm_epilogue(Params p) {
   const int nk = (K + T::BK - 1) / T::BK;
   const int nsteps = (nk + T::NS - 1) / T::NS * T::NS;
   int kt = nk - nsteps;
+  // [N][K] B follows A: slot resources at the slot's first step, fixed ones for ragged K
 #define GE_SET_RS(ka, kb)                                                      \
   do {                                                                         \
     if constexpr (!KMASK) ars = GE_A_RS(ka);                                   \
-    brs = GE_B_RS(b_base, kb);                                                 \
-    if constexpr (T::PAIR) b2rs = GE_B_RS(b2_base, kb);                        \
+    if constexpr (BNK && KMASK) {                                              \
+      brs = b_rs0;                                                             \
+      b2rs = b2_rs0;                                                           \
+    } else {                                                                   \
+      brs = GE_B_RS(b_base, BNK ? (ka) : (kb));                                \
+      if constexpr (T::PAIR) b2rs = GE_B_RS(b2_base, BNK ? (ka) : (kb));       \
+    }                                                                          \
   } while (0)
   GE_SET_RS(kt * T::BK, kt * T::BK);
   issue_a(kt * T::BK, aslot(S0{}));
-  issue_b(bstage(S0{}));
-  GE_SET_RS(kt * T::BK, (kt + 1) * T::BK);
-  issue_b(bstage(S1{}));
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(T::B_LOADS));
+  issue_b(bstage(S0{}), kt * T::BK);
+  if constexpr (!BNK) {
+    GE_SET_RS(kt * T::BK, (kt + 1) * T::BK);
+    issue_b(bstage(S1{}), (kt + 1) * T::BK);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(BNK ? 0 : T::B_LOADS));
   __builtin_amdgcn_s_barrier();
   read_frags(aslot(S0{}), bstage(S0{}), 0, 0, f0);
   for (; kt < nk; kt += T::NS) {
@@ -717,33 +790,34 @@ constexpr TileInfo info_of() {
   return TileInfo{T::BM, T::BN, T::NT, T::WAVES, T::PAIR, T::LDS};
 }
 
-template <class T, int ACT, bool FP8, bool ROWSTAT>
+template <class T, int ACT, bool FP8, bool ROWSTAT, bool BNK>
 void launch_k(const Params& p, hipStream_t s, unsigned grid) {
   if (p.K % 64 != 0)
-    hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, FP8, ROWSTAT, true>), dim3(grid), dim3(T::NT), 0, s, p);
+    hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, FP8, ROWSTAT, true, BNK>), dim3(grid), dim3(T::NT), 0, s, p);
   else
-    hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, FP8, ROWSTAT, false>), dim3(grid), dim3(T::NT), 0, s, p);
+    hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, FP8, ROWSTAT, false, BNK>), dim3(grid), dim3(T::NT), 0, s, p);
 }
 
-template <class T, int ACT, bool FP8>
+template <class T, int ACT, bool FP8, bool BNK>
 hipError_t launch_t(const Params& p, hipStream_t s) {
   const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * p.batch;
   if (grid <= 0) return hipSuccess;
   if (p.flags & F_ROW_RMS)
-    launch_k<T, ACT, FP8, true>(p, s, (unsigned)grid);
+    launch_k<T, ACT, FP8, true, BNK>(p, s, (unsigned)grid);
   else
-    launch_k<T, ACT, FP8, false>(p, s, (unsigned)grid);
+    launch_k<T, ACT, FP8, false, BNK>(p, s, (unsigned)grid);
   return hipGetLastError();
 }
 
-template <class T>
+// The instances of one tile shape and one B layout (one translation unit each).
+template <class T, bool BNK>
 hipError_t launch_tile(int act, bool fp8, const Params& p, hipStream_t s) {
   switch (act) {
-    case ACT_NONE: return fp8 ? launch_t<T, ACT_NONE, true>(p, s) : launch_t<T, ACT_NONE, false>(p, s);
-    case ACT_RELU: return fp8 ? launch_t<T, ACT_RELU, true>(p, s) : launch_t<T, ACT_RELU, false>(p, s);
+    case ACT_NONE: return fp8 ? launch_t<T, ACT_NONE, true, BNK>(p, s) : launch_t<T, ACT_NONE, false, BNK>(p, s);
+    case ACT_RELU: return fp8 ? launch_t<T, ACT_RELU, true, BNK>(p, s) : launch_t<T, ACT_RELU, false, BNK>(p, s);
     case ACT_GELU_TANH:
-      return fp8 ? launch_t<T, ACT_GELU_TANH, true>(p, s) : launch_t<T, ACT_GELU_TANH, false>(p, s);
-    case ACT_SILU: return fp8 ? launch_t<T, ACT_SILU, true>(p, s) : launch_t<T, ACT_SILU, false>(p, s);
+      return fp8 ? launch_t<T, ACT_GELU_TANH, true, BNK>(p, s) : launch_t<T, ACT_GELU_TANH, false, BNK>(p, s);
+    case ACT_SILU: return fp8 ? launch_t<T, ACT_SILU, true, BNK>(p, s) : launch_t<T, ACT_SILU, false, BNK>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -26,11 +26,16 @@ TileInfo tile_info(TileKind kind) {
 
 hipError_t launch_fused(TileKind kind, int act, bool fp8_out, const Params& p, hipStream_t stream) {
   switch (kind) {
-    case TILE_256x256: return launch_tile_256x256(act, fp8_out, p, stream);
-    case TILE_256x128_PAIR: return launch_tile_256x128_pair(act, fp8_out, p, stream);
-    case TILE_128x128: return launch_tile_128x128(act, fp8_out, p, stream);
-    case TILE_64x64: return launch_tile_64x64(act, fp8_out, p, stream);
-    case TILE_128x128_PAIR: return launch_tile_128x128_pair(act, fp8_out, p, stream);
+    case TILE_256x256: return (p.flags & F_B_NK) ? launch_tile_256x256_nk(act, fp8_out, p, stream)
+                                     : launch_tile_256x256_kn(act, fp8_out, p, stream);
+    case TILE_256x128_PAIR: return (p.flags & F_B_NK) ? launch_tile_256x128_pair_nk(act, fp8_out, p, stream)
+                                     : launch_tile_256x128_pair_kn(act, fp8_out, p, stream);
+    case TILE_128x128: return (p.flags & F_B_NK) ? launch_tile_128x128_nk(act, fp8_out, p, stream)
+                                     : launch_tile_128x128_kn(act, fp8_out, p, stream);
+    case TILE_64x64: return (p.flags & F_B_NK) ? launch_tile_64x64_nk(act, fp8_out, p, stream)
+                                     : launch_tile_64x64_kn(act, fp8_out, p, stream);
+    case TILE_128x128_PAIR: return (p.flags & F_B_NK) ? launch_tile_128x128_pair_nk(act, fp8_out, p, stream)
+                                     : launch_tile_128x128_pair_kn(act, fp8_out, p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,0 +1,12 @@
+// Instances of the fused kernel for the 128x128 tile, B laid out [K][N].
+#include "ge_kernel_impl.h"
+
+namespace ge {
+
+hipError_t launch_tile_128x128_kn(int act, bool fp8_out, const Params& p, hipStream_t stream) {
+  return launch_tile<T128, false>(act, fp8_out, p, stream);
+}
+
+TileInfo tile_info_128x128() { return info_of<T128>(); }
+
+}  // namespace ge

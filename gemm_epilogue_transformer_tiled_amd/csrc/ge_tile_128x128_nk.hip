@@ -1,0 +1,10 @@
+// Instances of the fused kernel for the 128x128 tile, B laid out [N][K].
+#include "ge_kernel_impl.h"
+
+namespace ge {
+
+hipError_t launch_tile_128x128_nk(int act, bool fp8_out, const Params& p, hipStream_t stream) {
+  return launch_tile<T128, true>(act, fp8_out, p, stream);
+}
+
+}  // namespace ge

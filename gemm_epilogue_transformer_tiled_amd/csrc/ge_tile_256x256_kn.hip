@@ -1,0 +1,12 @@
+// Instances of the fused kernel for the 256x256 tile, B laid out [K][N].
+#include "ge_kernel_impl.h"
+
+namespace ge {
+
+hipError_t launch_tile_256x256_kn(int act, bool fp8_out, const Params& p, hipStream_t stream) {
+  return launch_tile<T256, false>(act, fp8_out, p, stream);
+}
+
+TileInfo tile_info_256x256() { return info_of<T256>(); }
+
+}  // namespace ge

@@ -1,0 +1,10 @@
+// Instances of the fused kernel for the 256x256 tile, B laid out [N][K].
+#include "ge_kernel_impl.h"
+
+namespace ge {
+
+hipError_t launch_tile_256x256_nk(int act, bool fp8_out, const Params& p, hipStream_t stream) {
+  return launch_tile<T256, true>(act, fp8_out, p, stream);
+}
+
+}  // namespace ge

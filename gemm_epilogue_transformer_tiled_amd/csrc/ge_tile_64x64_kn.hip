@@ -1,0 +1,12 @@
+// Instances of the fused kernel for the 64x64 tile, B laid out [K][N].
+#include "ge_kernel_impl.h"
+
+namespace ge {
+
+hipError_t launch_tile_64x64_kn(int act, bool fp8_out, const Params& p, hipStream_t stream) {
+  return launch_tile<T64, false>(act, fp8_out, p, stream);
+}
+
+TileInfo tile_info_64x64() { return info_of<T64>(); }
+
+}  // namespace ge

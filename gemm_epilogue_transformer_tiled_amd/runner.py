@@ -12,7 +12,8 @@ from typing import Dict, Optional
 import numpy as np
 import torch
 
-from . import (GE_DT_BF16, GE_DT_FP8_E4M3, Plan, make_args, make_desc, make_ops)
+from . import (GE_DT_BF16, GE_DT_FP8_E4M3, GE_LAYOUT_KN, GE_LAYOUT_NK, Plan, make_args, make_desc,
+               make_ops)
 
 
 def to_device_bf16(bits: np.ndarray, device) -> torch.Tensor:
@@ -58,7 +59,8 @@ def prepare(w, inputs: Dict[str, np.ndarray], device="cuda", y_fill: Optional[in
         Y.view(torch.uint8).fill_(y_fill)
     amax = torch.full((1,), -1.0, dtype=torch.float32, device=device) if w.has("amax") else None
     desc = make_desc(w.batch, w.M, w.N, w.K, make_ops(w.chain),
-                     y_type=GE_DT_FP8_E4M3 if fp8 else GE_DT_BF16)
+                     y_type=GE_DT_FP8_E4M3 if fp8 else GE_DT_BF16,
+                     b_layout=GE_LAYOUT_NK if getattr(w, "b_layout", "kn") == "nk" else GE_LAYOUT_KN)
     plan = Plan(desc)
     args = make_args(A=t.get("A"), B=t.get("B"), B2=t.get("B2"), bias=t.get("bias"), residual=t.get("R"),
                      row_scale=t.get("row_scale"), Y=Y, amax=amax, alpha=w.alpha, quant_scale=w.quant_scale)

@@ -25,7 +25,11 @@
  *
  * Layout (all row-major, leading dimensions and batch strides in ELEMENTS):
  *   A  [batch][M][K] bf16, element (b,m,k) at A + b*stride_a + m*lda + k
- *   B  [batch][K][N] bf16, element (b,k,n) at B + b*stride_b + k*ldb + n
+ *   B  b_layout GE_LAYOUT_KN (default): [batch][K][N] bf16, element (b,k,n) at
+ *      B + b*stride_b + k*ldb + n (ldb >= N), as the pages lay W out;
+ *      b_layout GE_LAYOUT_NK: [batch][N][K] bf16, element (b,k,n) at B + b*stride_b +
+ *      n*ldb + k (ldb >= K) -- the product A @ B^T of a backward pass, dY @ W^T with W
+ *      stored [K][N] (CODA news item, "How CODA works": forward and backward epilogues)
  *   B2 same layout, leading dimension and batch stride as B (pairwise only)
  *   Y  [batch][M][N] bf16 or fp8-e4m3 (OCP "e4m3fn"), at Y + b*stride_y + m*ldy + n
  *   R  [batch][M][N] bf16 residual, at R + b*stride_r + m*ldr + n
@@ -89,6 +93,8 @@ typedef enum { GE_DT_BF16 = 0, GE_DT_FP8_E4M3 = 1, GE_DT_FP32 = 2 } ge_dtype_t;
 
 typedef enum { GE_ACT_NONE = 0, GE_ACT_RELU = 1, GE_ACT_GELU_TANH = 2, GE_ACT_SILU = 3 } ge_act_t;
 
+typedef enum { GE_LAYOUT_KN = 0, GE_LAYOUT_NK = 1 } ge_layout_t;
+
 typedef enum {
   GE_OP_SCALE = 0,
   GE_OP_ROW_RMS = 1,
@@ -114,6 +120,8 @@ typedef struct {
   int32_t a_type, b_type, y_type;               /* ge_dtype_t: bf16, bf16, bf16 | fp8_e4m3 */
   int32_t n_ops;
   ge_op_t ops[GE_MAX_OPS];
+  int32_t b_layout;                             /* ge_layout_t of B and B2 (0 = [K][N]) */
+  int32_t reserved;                             /* must be 0 */
 } ge_desc_t;
 
 /* The per-execution "variant pack": borrowed device pointers plus host scalars.

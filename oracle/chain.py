@@ -39,10 +39,12 @@ def run_chain(chain: Sequence[tuple], A: np.ndarray, B: np.ndarray,
               B2: Optional[np.ndarray] = None, bias: Optional[np.ndarray] = None,
               R: Optional[np.ndarray] = None, row_scale_vec: Optional[np.ndarray] = None,
               alpha: float = 1.0, quant_scale: float = 1.0, out: str = "bf16",
-              rows: Optional[np.ndarray] = None) -> OracleResult:
+              rows: Optional[np.ndarray] = None, b_layout: str = "kn") -> OracleResult:
     """Evaluate ``chain`` on bf16-bit inputs.
 
-    A: uint16 [batch, M, K]; B, B2: uint16 [batch, K, N]; bias: uint16 [N];
+    A: uint16 [batch, M, K]; B, B2: uint16 [batch, K, N], or [batch, N, K] with
+    ``b_layout="nk"`` -- then the product is A @ B^T, the backward-pass form dY @ W^T
+    (CODA news item, "How CODA works": forward and backward); bias: uint16 [N];
     R: uint16 [batch, M, N]; row_scale_vec: float32 [batch, M].
     ``rows`` (optional) restricts the evaluation to those rows of every batch
     (the result then has M = len(rows)); AMAX is then over those rows only.
@@ -56,8 +58,13 @@ def run_chain(chain: Sequence[tuple], A: np.ndarray, B: np.ndarray,
             row_scale_vec = np.asarray(row_scale_vec)[:, rows]
     kinds = [op[0] for op in chain]
     Af = decode_bf16(A)
-    acc = ops.gemm(Af, decode_bf16(B))
-    acc2 = ops.gemm(Af, decode_bf16(B2)) if "pairwise" in kinds else None
+
+    def as_kn(W: np.ndarray) -> np.ndarray:
+        W = decode_bf16(W)
+        return np.swapaxes(W, -1, -2) if b_layout == "nk" else W
+
+    acc = ops.gemm(Af, as_kn(B))
+    acc2 = ops.gemm(Af, as_kn(B2)) if "pairwise" in kinds else None
 
     def linear_part(t: np.ndarray) -> np.ndarray:
         for op in chain:
@@ -102,4 +109,5 @@ def run_workload(w, inputs: Dict[str, np.ndarray], rows=None) -> OracleResult:
     """Run a ``workloads.Workload`` on its generated inputs."""
     return run_chain(w.chain, inputs["A"], inputs["B"], inputs.get("B2"), inputs.get("bias"),
                      inputs.get("R"), inputs.get("row_scale"), alpha=w.alpha,
-                     quant_scale=w.quant_scale, out=w.out, rows=rows)
+                     quant_scale=w.quant_scale, out=w.out, rows=rows,
+                     b_layout=getattr(w, "b_layout", "kn"))

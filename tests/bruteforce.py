@@ -30,6 +30,13 @@ def exact_gemm(A: Sequence[Sequence[float]], B: Sequence[Sequence[float]]) -> Li
              for n in range(N)] for m in range(M)]
 
 
+def exact_gemm_nt(A: Sequence[Sequence[float]], Bt: Sequence[Sequence[float]]) -> List[List[Fraction]]:
+    """acc[m][n] = sum_k A[m][k] * Bt[n][k] (B given transposed, [N][K])."""
+    M, K, N = len(A), len(A[0]) if A else 0, len(Bt)
+    return [[sum((Fraction(A[m][k]) * Fraction(Bt[n][k]) for k in range(K)), Fraction(0))
+             for n in range(N)] for m in range(M)]
+
+
 def act(x: float, name: str) -> float:
     if name == "none":
         return x
@@ -42,8 +49,9 @@ def act(x: float, name: str) -> float:
     raise ValueError(name)
 
 
-def run_chain_scalar(chain, A, B, B2=None, bias=None, R=None, alpha=1.0) -> dict:
-    """A: [batch][M][K] floats, B/B2: [batch][K][N]; bias: [N]; R: [batch][M][N].
+def run_chain_scalar(chain, A, B, B2=None, bias=None, R=None, alpha=1.0, b_layout="kn") -> dict:
+    """A: [batch][M][K] floats, B/B2: [batch][K][N] ([batch][N][K] for b_layout "nk");
+    bias: [N]; R: [batch][M][N].
 
     Returns {"y": [batch][M][N] floats (before output encoding), "amax": float|None}.
     """
@@ -51,8 +59,9 @@ def run_chain_scalar(chain, A, B, B2=None, bias=None, R=None, alpha=1.0) -> dict
     ys = []
     amax = 0.0
     for b in range(len(A)):
-        acc = exact_gemm(A[b], B[b])
-        acc2 = exact_gemm(A[b], B2[b]) if "pairwise" in kinds else None
+        mm = exact_gemm_nt if b_layout == "nk" else exact_gemm
+        acc = mm(A[b], B[b])
+        acc2 = mm(A[b], B2[b]) if "pairwise" in kinds else None
         M = len(A[b])
         N = len(acc[0]) if acc else 0
         K = len(A[b][0]) if M else 0

@@ -7,6 +7,7 @@
 * Planted mistakes: plausible bugs are patched into the oracle (on the CPU)
   and at least one pin must then fail.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -36,7 +37,7 @@ def _check_against_bruteforce(w, inp):
     res = oracle.run_workload(w, inp)
     bias = oracle.decode_bf16(inp["bias"]).tolist() if "bias" in inp else None
     ref = run_chain_scalar(w.chain, _as_lists(inp, "A"), _as_lists(inp, "B"), _as_lists(inp, "B2"),
-                           bias, _as_lists(inp, "R"), alpha=w.alpha)
+                           bias, _as_lists(inp, "R"), alpha=w.alpha, b_layout=w.b_layout)
     y_ref = np.array(ref["y"], dtype=np.float64)
     assert res.y.shape == y_ref.shape
     assert np.allclose(res.y, y_ref, rtol=1e-12, atol=1e-13), np.abs(res.y - y_ref).max()
@@ -54,6 +55,15 @@ def _check_against_bruteforce(w, inp):
 @pytest.mark.parametrize("name", workloads.CONFIG_ORDER)
 def test_chain_matches_bruteforce(name):
     w, inp = _tiny(name)
+    _check_against_bruteforce(w, inp)
+
+
+@pytest.mark.parametrize("name", workloads.CONFIG_ORDER + ["f1"])
+def test_nk_layout_matches_bruteforce(name):
+    """B stored [N][K]: the product is A @ B^T (brute force indexes B[n][k] directly)."""
+    w = dataclasses.replace(workloads.WORKLOADS[name], b_layout="nk").with_shape(**TINY)
+    inp = workloads.generate(w)
+    assert inp["B"].shape == (w.batch, w.N, w.K)
     _check_against_bruteforce(w, inp)
 
 

@@ -5,6 +5,7 @@ cases, the fp8 writer over every bf16 value in range, and each of the five
 workloads at full size in the launch configuration the benchmark uses.
 """
 import contextlib
+import dataclasses
 import os
 
 import numpy as np
@@ -72,6 +73,51 @@ def compare(w, inp, prob, what, rows=None):
 
 
 RAGGED = dict(batch=2, M=300, N=264, K=200)
+
+
+@pytest.mark.parametrize("tile", SINGLE_TILES, ids=[TILE_NAMES[t] for t in SINGLE_TILES])
+@pytest.mark.parametrize("name", ["c1", "c2", "c4", "c5"])
+def test_ragged_nk_every_tile(name, tile):
+    """B given as [N][K] (the product A @ B^T), ragged in every dimension."""
+    w = dataclasses.replace(workloads.WORKLOADS[name], b_layout="nk").with_shape(**RAGGED)
+    inp = workloads.generate(w)
+    assert inp["B"].shape == (w.batch, w.N, w.K)
+    compare(w, inp, gpu_run(w, inp, tile), f"{name} nk tile {TILE_NAMES[tile]}")
+
+
+@pytest.mark.parametrize("tile", PAIR_TILES, ids=[TILE_NAMES[t] for t in PAIR_TILES])
+def test_ragged_nk_pairwise_tiles(tile):
+    w = dataclasses.replace(workloads.WORKLOADS["c3"], b_layout="nk").with_shape(**RAGGED)
+    inp = workloads.generate(w)
+    compare(w, inp, gpu_run(w, inp, tile), f"c3 nk tile {TILE_NAMES[tile]}")
+
+
+@pytest.mark.parametrize("K", [0, 8, 56, 64, 72, 136, 1032])
+@pytest.mark.parametrize("tile", [0, 1, 3], ids=["256x256", "256x128p", "64x64"])
+def test_k_edges_nk(K, tile):
+    name = "c3" if tile == 1 else "c2"
+    w = dataclasses.replace(workloads.WORKLOADS[name], b_layout="nk").with_shape(batch=1, M=136, N=264, K=K)
+    inp = workloads.generate(w)
+    compare(w, inp, gpu_run(w, inp, tile), f"{name} nk K={K} tile {TILE_NAMES[tile]}")
+
+
+def test_nk_padded_leading_dimension_and_sensitive_inputs():
+    w = dataclasses.replace(workloads.WORKLOADS["c5"], b_layout="nk").with_shape(batch=1, M=512, N=520, K=1000)
+    inp = workloads.generate(w, sensitive=True)
+    ldb = w.K + 24
+    Bp = np.zeros((1, w.N, ldb), dtype=np.uint16)
+    Bp[:, :, :w.K] = inp["B"]
+    prob = runner.prepare(w, {**inp, "B": Bp})
+    desc = ge.make_desc(1, w.M, w.N, w.K, ge.make_ops(w.chain), y_type=ge.GE_DT_FP8_E4M3,
+                        b_layout=ge.GE_LAYOUT_NK, ldb=ldb)
+    plan = ge.Plan(desc)
+    args = ge.make_args(A=prob.tensors["A"], B=prob.tensors["B"], bias=prob.tensors["bias"], Y=prob.Y,
+                        amax=prob.amax, quant_scale=w.quant_scale)
+    plan.run(args)
+    torch.cuda.synchronize()
+    ref = oracle.run_workload(w, inp)
+    check_fp8(prob.y_host_bits(), ref.codes, "nk padded ldb")
+    check_amax(prob.amax_host(), ref.amax, "nk padded ldb")
 
 
 @pytest.mark.parametrize("tile", SINGLE_TILES, ids=[TILE_NAMES[t] for t in SINGLE_TILES])

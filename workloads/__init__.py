@@ -57,6 +57,7 @@ class Workload:
     bias_var: float = 1.0
     out: str = "bf16"           # "bf16" or "fp8_e4m3"
     description: str = ""
+    b_layout: str = "kn"        # "kn": B stored [K][N]; "nk": B stored [N][K] (product A @ B^T)
 
     @property
     def pairwise(self) -> bool:
@@ -153,10 +154,11 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
-def _fold(w_bits: np.ndarray, g: np.ndarray) -> np.ndarray:
-    """bf16(fp32(W[k, n]) * g[k]) for W [batch, K, N] as bf16 bits."""
+def _fold(w_bits: np.ndarray, g: np.ndarray, layout: str = "kn") -> np.ndarray:
+    """bf16(fp32(W[k, n]) * g[k]) for W stored [batch, K, N] ("kn") or [batch, N, K] ("nk")."""
     w_f32 = (w_bits.astype(np.uint32) << 16).view(np.float32)
-    return f32_to_bf16_bits(w_f32 * g[None, :, None])
+    gk = g[None, :, None] if layout == "kn" else g[None, None, :]
+    return f32_to_bf16_bits(w_f32 * gk)
 
 
 def _normal_bf16(config_id: int, tensor_id: int, shape, var: float) -> np.ndarray:
@@ -173,7 +175,7 @@ def generate(w: Workload, sensitive: bool = False, seed_offset: int = 0) -> Dict
     """Seeded inputs for workload ``w``.
 
     Returns bf16 tensors as uint16 bit arrays (A: [batch, M, K]; B, B2:
-    [batch, K, N]; bias: [N]; R: [batch, M, N]) and float32 arrays for the
+    [batch, K, N], or [batch, N, K] for b_layout "nk"; bias: [N]; R: [batch, M, N]) and float32 arrays for the
     gain ``g`` (RMS workload only).  ``sensitive=True`` draws A from N(0, 1)
     and sets the bias to zero, so the GEMM term dominates the output.
     ``seed_offset`` shifts the config id of every stream (extra seeds for the
@@ -181,6 +183,8 @@ def generate(w: Workload, sensitive: bool = False, seed_offset: int = 0) -> Dict
     """
     cid = w.config_id + 100 * seed_offset
     b, M, N, K = w.batch, w.M, w.N, w.K
+    lay = w.b_layout
+    bshape = (b, K, N) if lay == "kn" else (b, N, K)
     out: Dict[str, np.ndarray] = {}
     a_var = 1.0 if sensitive else _var(w.a_var, K)
     out["A"] = _normal_bf16(cid, T_A, (b, M, K), a_var)
@@ -188,17 +192,17 @@ def generate(w: Workload, sensitive: bool = False, seed_offset: int = 0) -> Dict
     if w.has("row_rms"):
         # gain g[k] ~ U(0.5, 1.5) folded into the base weight(s) along the contraction axis
         g = _rng(cid, T_G).uniform(0.5, 1.5, size=K).astype(np.float32)
-        w_base = _normal_bf16(cid, T_W, (b, K, N), _var(w.b_var, K))
+        w_base = _normal_bf16(cid, T_W, bshape, _var(w.b_var, K))
         out["g"] = g
         out["W_base"] = w_base
-        out["B"] = _fold(w_base, g)
+        out["B"] = _fold(w_base, g, lay)
     else:
-        out["B"] = _normal_bf16(cid, T_B, (b, K, N), _var(w.b_var, K))
+        out["B"] = _normal_bf16(cid, T_B, bshape, _var(w.b_var, K))
     if w.pairwise:
-        out["B2"] = _normal_bf16(cid, T_B2, (b, K, N), _var(w.b_var, K))
+        out["B2"] = _normal_bf16(cid, T_B2, bshape, _var(w.b_var, K))
         if g is not None:            # RMSNorm-MLP: the same gain scales X before both products
             out["W2_base"] = out["B2"]
-            out["B2"] = _fold(out["B2"], g)
+            out["B2"] = _fold(out["B2"], g, lay)
     if w.has("bias"):
         if sensitive:
             out["bias"] = np.zeros(N, dtype=np.uint16)
