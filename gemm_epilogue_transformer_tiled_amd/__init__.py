@@ -21,13 +21,14 @@ GE_DT_BF16, GE_DT_FP8_E4M3, GE_DT_FP32 = range(3)
 GE_ACT_NONE, GE_ACT_RELU, GE_ACT_GELU_TANH, GE_ACT_SILU = range(4)
 GE_LAYOUT_KN, GE_LAYOUT_NK = range(2)
 (GE_OP_SCALE, GE_OP_ROW_RMS, GE_OP_ROW_SCALE, GE_OP_BIAS_COL, GE_OP_ACT, GE_OP_PAIRWISE_ACT_MUL,
- GE_OP_RESIDUAL, GE_OP_AMAX, GE_OP_QUANT_FP8) = range(9)
+ GE_OP_RESIDUAL, GE_OP_AMAX, GE_OP_QUANT_FP8, GE_OP_ACT_GRAD, GE_OP_COL_SUM) = range(11)
 GE_MAX_OPS = 8
 
 ACT_NAMES = {"none": GE_ACT_NONE, "relu": GE_ACT_RELU, "gelu_tanh": GE_ACT_GELU_TANH, "silu": GE_ACT_SILU}
 OP_NAMES = {"scale": GE_OP_SCALE, "row_rms": GE_OP_ROW_RMS, "row_scale": GE_OP_ROW_SCALE,
             "bias": GE_OP_BIAS_COL, "act": GE_OP_ACT, "pairwise": GE_OP_PAIRWISE_ACT_MUL,
-            "residual": GE_OP_RESIDUAL, "amax": GE_OP_AMAX, "quant_fp8": GE_OP_QUANT_FP8}
+            "residual": GE_OP_RESIDUAL, "amax": GE_OP_AMAX, "quant_fp8": GE_OP_QUANT_FP8,
+            "act_grad": GE_OP_ACT_GRAD, "col_sum": GE_OP_COL_SUM}
 
 
 class ge_op_t(ctypes.Structure):
@@ -44,6 +45,7 @@ class ge_desc_t(ctypes.Structure):
         ("n_ops", ctypes.c_int32),
         ("ops", ge_op_t * GE_MAX_OPS),
         ("b_layout", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("ldz", ctypes.c_int64), ("stride_z", ctypes.c_int64),
     ]
 
 
@@ -53,6 +55,7 @@ class ge_args_t(ctypes.Structure):
         ("row_scale", ctypes.c_void_p), ("residual", ctypes.c_void_p), ("Y", ctypes.c_void_p),
         ("amax", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("alpha", ctypes.c_float), ("quant_scale", ctypes.c_float),
+        ("aux", ctypes.c_void_p), ("col_sum", ctypes.c_void_p),
     ]
 
 
@@ -151,7 +154,7 @@ def make_ops(chain: Iterable[tuple]) -> Sequence[Tuple[int, int, float]]:
     for op in chain:
         kind = OP_NAMES[op[0]]
         act, eps = 0, 0.0
-        if op[0] in ("act", "pairwise"):
+        if op[0] in ("act", "pairwise", "act_grad"):
             act = ACT_NAMES[op[1]]
         elif op[0] == "row_rms":
             eps = float(op[1])
@@ -164,7 +167,8 @@ def make_desc(batch: int, M: int, N: int, K: int, ops: Sequence[Tuple[int, int, 
               ldy: Optional[int] = None, ldr: Optional[int] = None, stride_a: Optional[int] = None,
               stride_b: Optional[int] = None, stride_y: Optional[int] = None,
               stride_r: Optional[int] = None, a_type: int = GE_DT_BF16, b_type: int = GE_DT_BF16,
-              b_layout: int = GE_LAYOUT_KN) -> ge_desc_t:
+              b_layout: int = GE_LAYOUT_KN, ldz: Optional[int] = None,
+              stride_z: Optional[int] = None) -> ge_desc_t:
     """Descriptor for packed row-major operands unless leading dims / strides are given.
     b_layout GE_LAYOUT_NK: B (and B2) are [batch][N][K]."""
     d = ge_desc_t()
@@ -178,6 +182,8 @@ def make_desc(batch: int, M: int, N: int, K: int, ops: Sequence[Tuple[int, int, 
     d.stride_b = (N if b_layout == GE_LAYOUT_NK else K) * d.ldb if stride_b is None else stride_b
     d.stride_y = M * d.ldy if stride_y is None else stride_y
     d.stride_r = M * d.ldr if stride_r is None else stride_r
+    d.ldz = N if ldz is None else ldz
+    d.stride_z = M * d.ldz if stride_z is None else stride_z
     d.a_type, d.b_type, d.y_type = a_type, b_type, y_type
     if len(ops) > GE_MAX_OPS:
         raise ValueError("too many epilogue ops")
@@ -192,9 +198,10 @@ def _ptr(t) -> Optional[int]:
 
 
 def make_args(A=None, B=None, B2=None, bias=None, row_scale=None, residual=None, Y=None, amax=None,
-              alpha: float = 1.0, quant_scale: float = 1.0, workspace=None) -> ge_args_t:
+              alpha: float = 1.0, quant_scale: float = 1.0, workspace=None, aux=None, col_sum=None) -> ge_args_t:
     """Variant pack from torch device tensors (or None)."""
     a = ge_args_t()
+    a.aux, a.col_sum = _ptr(aux), _ptr(col_sum)
     a.A, a.B, a.B2, a.bias = _ptr(A), _ptr(B), _ptr(B2), _ptr(bias)
     a.row_scale, a.residual, a.Y, a.amax = _ptr(row_scale), _ptr(residual), _ptr(Y), _ptr(amax)
     a.workspace = _ptr(workspace)

@@ -38,10 +38,12 @@ int op_rank(int kind) {
     case GE_OP_ROW_SCALE: return 1;
     case GE_OP_BIAS_COL: return 2;
     case GE_OP_ACT:
-    case GE_OP_PAIRWISE_ACT_MUL: return 3;
+    case GE_OP_PAIRWISE_ACT_MUL:
+    case GE_OP_ACT_GRAD: return 3;
     case GE_OP_RESIDUAL: return 4;
-    case GE_OP_AMAX: return 5;
-    case GE_OP_QUANT_FP8: return 6;
+    case GE_OP_COL_SUM: return 5;
+    case GE_OP_AMAX: return 6;
+    case GE_OP_QUANT_FP8: return 7;
     default: return -1;
   }
 }
@@ -104,7 +106,7 @@ ge_status_t gemm_epilogue_validate(const ge_desc_t* d) {
     if (r < 0) return GE_ERR_INVALID_ARG;
     if (r <= last_rank) return GE_ERR_INVALID_ARG;
     last_rank = r;
-    if (op.kind == GE_OP_ACT || op.kind == GE_OP_PAIRWISE_ACT_MUL) {
+    if (op.kind == GE_OP_ACT || op.kind == GE_OP_PAIRWISE_ACT_MUL || op.kind == GE_OP_ACT_GRAD) {
       if (op.act < GE_ACT_NONE || op.act > GE_ACT_SILU) return GE_ERR_INVALID_ARG;
     }
     if (op.kind == GE_OP_ROW_RMS) {
@@ -127,9 +129,16 @@ ge_status_t gemm_epilogue_validate(const ge_desc_t* d) {
     return GE_ERR_INVALID_ARG;
   }
   if (pair && has_op(d, GE_OP_BIAS_COL)) return GE_ERR_UNSUPPORTED;
+  // the activation-gradient instances write bf16 and take no in-kernel row statistic
+  if (has_op(d, GE_OP_ACT_GRAD) && (quant || has_op(d, GE_OP_ROW_RMS))) return GE_ERR_UNSUPPORTED;
 
   // layout
   const bool res = has_op(d, GE_OP_RESIDUAL);
+  const bool grad = has_op(d, GE_OP_ACT_GRAD);
+  if (grad && (d->ldz < 0 || d->stride_z < 0)) return GE_ERR_INVALID_ARG;
+  if (grad && d->M > 0 && d->ldz < d->N) return GE_ERR_INVALID_ARG;
+  if (grad && (d->ldz % 8 || d->stride_z % 8)) return GE_ERR_UNSUPPORTED;
+  if (grad && extent_elems(d->M + 256, d->N, d->ldz) * 2 > kMaxExtent) return GE_ERR_UNSUPPORTED;
   if (d->M > 0 && d->lda < d->K) return GE_ERR_INVALID_ARG;
   if (!bnk && d->K > 0 && d->ldb < d->N) return GE_ERR_INVALID_ARG;
   if (bnk && d->N > 0 && d->ldb < d->K) return GE_ERR_INVALID_ARG;
@@ -197,6 +206,11 @@ ge_status_t gemm_epilogue_create(const ge_desc_t* desc, ge_handle_t* out) {
   if (has_op(desc, GE_OP_BIAS_COL)) p->flags |= ge::F_BIAS;
   if (has_op(desc, GE_OP_RESIDUAL)) p->flags |= ge::F_RESIDUAL;
   if (has_op(desc, GE_OP_AMAX)) p->flags |= ge::F_AMAX;
+  if (const ge_op_t* g = find_op(desc, GE_OP_ACT_GRAD)) {
+    p->flags |= ge::F_ACT_GRAD;
+    p->act = g->act;
+  }
+  if (has_op(desc, GE_OP_COL_SUM)) p->flags |= ge::F_COL_SUM;
   if (desc->b_layout == GE_LAYOUT_NK) p->flags |= ge::F_B_NK;
   const ge::TileInfo ti = ge::tile_info(p->tile);
   p->tiles_m = ceil_div(desc->M, ti.bm);
@@ -205,9 +219,19 @@ ge_status_t gemm_epilogue_create(const ge_desc_t* desc, ge_handle_t* out) {
   return GE_OK;
 }
 
+namespace {
+size_t workspace_bytes(const ge_plan* h) {
+  const int64_t wgs = h->tiles_m * h->tiles_n * h->desc.batch;
+  const bool amax = (h->flags & ge::F_AMAX) != 0;
+  if (h->flags & ge::F_COL_SUM)
+    return 4 * (ge::colsum_part_word(amax, wgs, h->tiles_n) + (size_t)(h->desc.batch * h->tiles_m * h->desc.N));
+  return amax ? ge::amax_workspace_bytes(wgs) : 0;
+}
+}  // namespace
+
 ge_status_t gemm_epilogue_workspace_size(ge_handle_t h, size_t* bytes) {
   if (!h || !bytes) return GE_ERR_INVALID_ARG;
-  *bytes = (h->flags & ge::F_AMAX) ? ge::amax_workspace_bytes(h->tiles_m * h->tiles_n * h->desc.batch) : 0;
+  *bytes = workspace_bytes(h);
   return GE_OK;
 }
 
@@ -220,10 +244,13 @@ ge_status_t gemm_epilogue_run(ge_handle_t h, const ge_args_t* a, void* stream) {
 
   if (f & ge::F_AMAX) {
     if (!a->amax || !aligned(a->amax, 4)) return GE_ERR_INVALID_ARG;
-    if (!empty && (!a->workspace || !aligned(a->workspace, 16) ||
-                   a->workspace_bytes < ge::amax_workspace_bytes(h->tiles_m * h->tiles_n * d.batch)))
-      return GE_ERR_INVALID_ARG;
   }
+  if (f & ge::F_COL_SUM) {
+    if (d.N > 0 && (!a->col_sum || !aligned(a->col_sum, 4))) return GE_ERR_INVALID_ARG;
+  }
+  if ((f & (ge::F_AMAX | ge::F_COL_SUM)) && !empty &&
+      (!a->workspace || !aligned(a->workspace, 16) || a->workspace_bytes < workspace_bytes(h)))
+    return GE_ERR_INVALID_ARG;
   if (!empty) {
     if (!a->Y || !aligned(a->Y, 16)) return GE_ERR_INVALID_ARG;
     if (d.K > 0) {
@@ -235,11 +262,16 @@ ge_status_t gemm_epilogue_run(ge_handle_t h, const ge_args_t* a, void* stream) {
     if ((f & ge::F_BIAS) && (!a->bias || !aligned(a->bias, 16))) return GE_ERR_INVALID_ARG;
     if ((f & ge::F_ROW_SCALE) && (!a->row_scale || !aligned(a->row_scale, 4))) return GE_ERR_INVALID_ARG;
     if ((f & ge::F_RESIDUAL) && (!a->residual || !aligned(a->residual, 16))) return GE_ERR_INVALID_ARG;
+    if ((f & ge::F_ACT_GRAD) && (!a->aux || !aligned(a->aux, 16))) return GE_ERR_INVALID_ARG;
   }
 
   if (empty) {
     // nothing to reduce: AMAX of no outputs is 0
     if ((f & ge::F_AMAX) && ge::launch_amax_zero(reinterpret_cast<uint32_t*>(a->amax), s) != hipSuccess)
+      return GE_ERR_HIP;
+    // and the column sums over no rows are 0
+    if ((f & ge::F_COL_SUM) && d.N > 0 &&
+        ge::launch_zero_words(reinterpret_cast<uint32_t*>(a->col_sum), d.N, s) != hipSuccess)
       return GE_ERR_HIP;
     return GE_OK;
   }
@@ -254,6 +286,17 @@ ge_status_t gemm_epilogue_run(ge_handle_t h, const ge_args_t* a, void* stream) {
   p.Y = a->Y;
   p.amax = reinterpret_cast<uint32_t*>(a->amax);
   p.ws = static_cast<uint32_t*>(a->workspace);
+  p.Z = static_cast<const uint16_t*>(a->aux);
+  p.col_sum = a->col_sum;
+  {
+    const int64_t wgs = h->tiles_m * h->tiles_n * d.batch;
+    const bool amax = (f & ge::F_AMAX) != 0;
+    p.cs_ctr = (f & ge::F_COL_SUM) ? p.ws + ge::colsum_ctr_word(amax, wgs) : nullptr;
+    p.cs_part = (f & ge::F_COL_SUM) ? reinterpret_cast<float*>(p.ws + ge::colsum_part_word(amax, wgs, h->tiles_n))
+                                    : nullptr;
+  }
+  p.ldz = d.ldz;
+  p.sz = d.stride_z;
   p.lda = d.lda;
   p.ldb = d.ldb;
   p.ldy = d.ldy;

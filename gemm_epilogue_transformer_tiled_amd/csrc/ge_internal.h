@@ -15,6 +15,8 @@ enum : uint32_t {
   F_RESIDUAL = 1u << 4,
   F_AMAX = 1u << 5,
   F_B_NK = 1u << 6,      // B and B2 given as [batch][N][K] (K contiguous)
+  F_ACT_GRAD = 1u << 7,  // y = t * act'(Z) instead of act(t)
+  F_COL_SUM = 1u << 8,   // column sums of y over rows and batches
 };
 
 enum Act : int { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_TANH = 2, ACT_SILU = 3 };
@@ -39,6 +41,11 @@ struct Params {
   void* Y;
   uint32_t* amax;          // fp32 AMAX viewed as its bit pattern
   uint32_t* ws;            // AMAX workspace (layout below); counters are zero between runs
+  const uint16_t* Z;       // ACT_GRAD: saved pre-activation, bf16
+  float* col_sum;          // COL_SUM output [N]
+  uint32_t* cs_ctr;        // COL_SUM ticket counters, one per column tile (stride kColSumCtrStride)
+  float* cs_part;          // COL_SUM partials [batch * tiles_m][N]
+  int64_t ldz, sz;
   int64_t lda, ldb, ldy, ldr;
   int64_t sa, sb, sy, sr;  // batch strides in elements
   int32_t M, N, K, batch;
@@ -78,12 +85,24 @@ hipError_t launch_fused(TileKind kind, int act, bool fp8_out, const Params& p, h
 // Enqueues a one-thread kernel that writes 0 to *amax (empty problems only).
 hipError_t launch_amax_zero(uint32_t* amax, hipStream_t stream);
 
+// Enqueues a kernel that writes `count` zero words at p (COL_SUM of an empty problem).
+hipError_t launch_zero_words(uint32_t* p, int64_t count, hipStream_t stream);
+
 // AMAX workspace layout (32-bit words): eight dispatch-group ticket counters and one top
 // counter, each on its own 256-byte line, then one partial-maximum slot per workgroup.
 constexpr uint32_t kAmaxGroups = 8;
 constexpr uint32_t kAmaxCounterStride = 64;
 constexpr uint32_t kAmaxSlot0 = 1024;
-constexpr uint32_t kAmaxFlatGrid = 64;   // up to this many workgroups take one ticket each on the top counter
+constexpr uint32_t kAmaxFlatGrid = 64;
+constexpr uint32_t kColSumCtrStride = 16;   // 64 bytes between column-tile counters
+// Workspace words: [AMAX region][COL_SUM counters][COL_SUM partials], each 256-byte aligned.
+inline size_t round64(size_t w) { return (w + 63) / 64 * 64; }
+inline size_t colsum_ctr_word(bool amax, int64_t workgroups) {
+  return amax ? round64((size_t)kAmaxSlot0 + (size_t)workgroups) : 0;
+}
+inline size_t colsum_part_word(bool amax, int64_t workgroups, int64_t tiles_n) {
+  return round64(colsum_ctr_word(amax, workgroups) + (size_t)tiles_n * kColSumCtrStride);
+}   // up to this many workgroups take one ticket each on the top counter
 inline size_t amax_workspace_bytes(int64_t workgroups) { return 4 * ((size_t)kAmaxSlot0 + (size_t)workgroups); }
 
 }  // namespace ge

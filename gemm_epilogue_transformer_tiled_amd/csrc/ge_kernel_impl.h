@@ -36,6 +36,7 @@
 //   * Workgroup ids are remapped so each XCD (own L2) receives a contiguous run of tiles,
 //     which are then walked in groups of 8 tile-rows for L2 reuse.
 #include <type_traits>
+#include <utility>
 
 #include "ge_internal.h"
 
@@ -161,6 +162,24 @@ __device__ __forceinline__ float activate(float t) {
   }
 }
 
+// Derivative of activate<ACT> at z, for the backward activation-gradient epilogue.  With
+// s = sigmoid(2u), u = sqrt(2/pi)(z + 0.044715 z^3): GELU' = s + 2 sqrt(2/pi) z s(1-s)
+// (1 + 3*0.044715 z^2); SiLU' = s(1 + z(1-s)) with s = sigmoid(z); ReLU' = [z > 0].
+template <int ACT>
+__device__ __forceinline__ float activate_grad(float z) {
+  if constexpr (ACT == ACT_RELU) {
+    return z > 0.0f ? 1.0f : 0.0f;
+  } else if constexpr (ACT == ACT_GELU_TANH) {
+    const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(kGeluC * (z + kGeluCubic * z * z * z)));
+    return s + 2.0f * 0.7978845608028654f * z * s * (1.0f - s) * (1.0f + 3.0f * kGeluCubic * z * z);
+  } else if constexpr (ACT == ACT_SILU) {
+    const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * z));
+    return s * (1.0f + z * (1.0f - s));
+  } else {
+    return 1.0f;
+  }
+}
+
 // Workgroup id -> (batch, tile row, tile column).
 __device__ __forceinline__ void tile_coords(int wg, const Params& p, int& b, int& tm, int& tn) {
   const int per_batch = p.tiles_m * p.tiles_n;
@@ -204,7 +223,8 @@ __device__ __forceinline__ void sched_group() {
 // BNK: B (and B2) are given as [N][K] (K contiguous) -- for instance W when the product is
 // dY @ W^T of a backward pass -- and are staged exactly like A: two steps at a time as
 // [BN][64] with 128-byte rows, fragments by plain 16-byte LDS reads.
-template <class T, int ACT, bool FP8, bool ROWSTAT, bool KMASK, bool BNK>
+// GRAD: the activation-gradient epilogue y = t * act'(Z) replaces y = act(t) (non-pairwise).
+template <class T, int ACT, bool GRAD, bool FP8, bool ROWSTAT, bool KMASK, bool BNK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(T::WPE, T::WPE)))
 void fused_gemm_epilogue(Params p) {
   // The LDS stages and slots are distinct arrays, so the compiler can tell that the direct
@@ -590,6 +610,8 @@ void fused_gemm_epilogue(Params p) {
   const uint32_t flags = p.flags;
   const bool has_bias = (flags & F_BIAS) != 0;
   const bool has_res = (flags & F_RESIDUAL) != 0;
+  static_assert(!(GRAD && T::PAIR), "the activation gradient is not a pairwise epilogue");
+  const bool has_cs = (flags & F_COL_SUM) != 0;
   const bool has_rs = (flags & F_ROW_SCALE) != 0;
   const bool has_rms = ROWSTAT && (flags & F_ROW_RMS) != 0;
   const float alpha = (flags & F_SCALE) ? p.alpha : 1.0f;
@@ -621,38 +643,65 @@ void fused_gemm_epilogue(Params p) {
   const __amdgpu_buffer_rsrc_t r_rs =
       has_res ? make_rsrc(p.R + b * p.sr + (int64_t)m0 * p.ldr + n0, ((int64_t)(M - 1 - m0) * p.ldr + (N - n0)) * 2)
               : y_rs;
+  const __amdgpu_buffer_rsrc_t z_rs =
+      GRAD ? make_rsrc(p.Z + b * p.sz + (int64_t)m0 * p.ldz + n0, ((int64_t)(M - 1 - m0) * p.ldz + (N - n0)) * 2)
+               : y_rs;
   const uint32_t ldy_b = (uint32_t)p.ldy * (uint32_t)esize, ldr_b = (uint32_t)p.ldr * 2u;
+  const uint32_t ldz_b = (uint32_t)p.ldz * 2u;
   const uint32_t col_y = col_ok ? (uint32_t)(wn0 + p2_col) * (uint32_t)esize : kOOB;
   const uint32_t col_r = col_ok ? (uint32_t)(wn0 + p2_col) * 2u : kOOB;
 
   uint32_t amax_bits = 0;
-  // Residual rows of a 32-row block, in phase-2 layout.  Two blocks are kept: the loads of
-  // block j+1 are issued before block j is processed, so their latency is hidden.
-  u32x2_t rvb[2][PASSES];
-  auto load_res = [&](int j, u32x2_t* rv) {
+  float csum[4] = {0.0f, 0.0f, 0.0f, 0.0f};    // COL_SUM: this lane's four columns
+  // Residual rows of a 32-row block, in phase-2 layout, loaded at the start of the block so
+  // that phase 1 hides their latency.  (The saved pre-activation of ACT_GRAD is loaded per
+  // chunk inside phase 2: registers.)
+  u32x2_t rvb[1][PASSES];
+  auto load_rows = [&](int j, __amdgpu_buffer_rsrc_t rs, uint32_t ld_b, u32x2_t* rv) {
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
       const int ml = wm0 + 32 * j + ps * RPP + p2_row;
-      const uint32_t off = (m0 + ml < M) ? (uint32_t)ml * ldr_b + col_r : kOOB;
-      rv[ps] = __builtin_amdgcn_raw_buffer_load_b64(r_rs, off | (col_r & kOOB), 0, 0);
+      const uint32_t off = (m0 + ml < M) ? (uint32_t)ml * ld_b + col_r : kOOB;
+      rv[ps] = __builtin_amdgcn_raw_buffer_load_b64(rs, off | (col_r & kOOB), 0, 0);
     }
   };
+  auto prefetch = [&](int j) {
+    if (has_res) load_rows(j, r_rs, ldr_b, rvb[0]);
+  };
+  // Phase 2 in chunks of PCH passes (bounds the registers the batched LDS reads and the
+  // saved pre-activation occupy).
+  constexpr int PCH = PASSES < 8 ? PASSES : 8;
   auto phase2 = [&](int j, auto res_c, const u32x2_t* rv) {
     constexpr bool RES = decltype(res_c)::value;
-    f32x4_t vv[PASSES];
 #pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) vv[ps] = *(const f32x4_t*)(ep + (ps * RPP + p2_row) * EP_LD + p2_col);
+    for (int c0 = 0; c0 < PASSES; c0 += PCH) {
+    u32x2_t zv[GRAD ? PCH : 1];
+    if constexpr (GRAD) {
 #pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
+      for (int q = 0; q < PCH; ++q) {
+        const int ml = wm0 + 32 * j + (c0 + q) * RPP + p2_row;
+        const uint32_t off = (m0 + ml < M) ? (uint32_t)ml * ldz_b + col_r : kOOB;
+        zv[q] = __builtin_amdgcn_raw_buffer_load_b64(z_rs, off | (col_r & kOOB), 0, 0);
+      }
+    }
+    f32x4_t vv[PCH];
+#pragma unroll
+    for (int q = 0; q < PCH; ++q) vv[q] = *(const f32x4_t*)(ep + ((c0 + q) * RPP + p2_row) * EP_LD + p2_col);
+#pragma unroll
+    for (int q = 0; q < PCH; ++q) {
+      const int ps = c0 + q;
       const int r = ps * RPP + p2_row;
       const int ml = wm0 + 32 * j + r;
       const bool ok = (m0 + ml < M) & col_ok;
-      const f32x4_t v = vv[ps];
+      const f32x4_t v = vv[q];
       float y[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if constexpr (T::PAIR) {
           y[e] = v[e];
+        } else if constexpr (GRAD) {
+          const uint32_t zw = zv[q][e >> 1];
+          y[e] = (v[e] + bias4[e]) * activate_grad<ACT>((e & 1) ? bf16_hi(zw) : bf16_lo(zw));
         } else {
           y[e] = activate<ACT>(v[e] + bias4[e]);
         }
@@ -666,6 +715,8 @@ void fused_gemm_epilogue(Params p) {
       const uint32_t m01 = max(__float_as_uint(y[0]) & 0x7FFFFFFFu, __float_as_uint(y[1]) & 0x7FFFFFFFu);
       const uint32_t m23 = max(__float_as_uint(y[2]) & 0x7FFFFFFFu, __float_as_uint(y[3]) & 0x7FFFFFFFu);
       amax_bits = ok ? max(amax_bits, max(m01, m23)) : amax_bits;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) csum[e] += ok ? y[e] : 0.0f;
       const uint32_t yoff = ok ? (uint32_t)ml * ldy_b + col_y : kOOB;
       if constexpr (FP8) {
         const float qs = p.qscale;
@@ -682,12 +733,12 @@ void fused_gemm_epilogue(Params p) {
         __builtin_amdgcn_raw_buffer_store_b64(w, y_rs, yoff, 0, 0);
       }
     }
+    }
   };
 
-  if (has_res) load_res(0, rvb[0]);
 #pragma unroll
   for (int j = 0; j < T::FM; ++j) {
-    if (has_res && j + 1 < T::FM) load_res(j + 1, rvb[(j + 1) & 1]);
+    prefetch(j);
     const int ml = wm0 + 32 * j + lrow;
     float rscale = alpha;
     if constexpr (ROWSTAT) {
@@ -711,11 +762,62 @@ void fused_gemm_epilogue(Params p) {
         *(f32x4_t*)(ep + lrow * EP_LD + 32 * i + 8 * g + 4 * lhalf) = t;
       }
     // phase 2 reads what this wave just wrote; a wave's LDS operations complete in order
-    if (has_res) {
-      phase2(j, std::integral_constant<bool, true>{}, rvb[j & 1]);
-    } else {
+    if (has_res)
+      phase2(j, std::integral_constant<bool, true>{}, rvb[0]);
+    else
       phase2(j, std::integral_constant<bool, false>{}, rvb[0]);
+  }
+
+  // ---- COL_SUM ----
+  // Lanes holding the same four columns (equal lane % LPR) add up their rows; the two waves of
+  // a column half (wave_m = 0, 1) meet in LDS; the workgroup stores its partial column sums
+  // (device scope) in its [batch * tiles_m] row of the workspace and takes a ticket from its
+  // column tile's counter.  The workgroup completing a column tile adds that tile's partials
+  // in row-tile order -- a fixed order, so the result does not depend on which workgroup
+  // finishes last -- writes col_sum and resets the counter.
+  if (has_cs) {
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) csum[e] += __shfl_xor(csum[e], off);
+    __syncthreads();                                    // LDS: epilogue blocks are done with
+    float* cs_lds = (float*)aslot0;
+    if (wave_m == 1 && lane < LPR)
+      *(f32x4_t*)(cs_lds + wn0 + p2_col) = f32x4_t{csum[0], csum[1], csum[2], csum[3]};
+    __syncthreads();
+    const uint32_t prow = (uint32_t)(b * p.tiles_m + tm);
+    if (wave_m == 0 && lane < LPR) {
+      const f32x4_t o = *(const f32x4_t*)(cs_lds + wn0 + p2_col);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (gcol + e < N)
+          __hip_atomic_store(&p.cs_part[(int64_t)prow * N + gcol + e], csum[e] + o[e], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
     }
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);                // partials performed before the ticket
+    __syncthreads();
+    const uint32_t rows_of_tiles = (uint32_t)(p.batch * p.tiles_m);
+    if (tid == 0) {
+      uint32_t* ctr = &p.cs_ctr[(uint32_t)tn * kColSumCtrStride];
+      bool last = false;
+      if (__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == rows_of_tiles - 1u) {
+        __hip_atomic_exchange(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = true;
+      }
+      wave_amax[0] = last ? 1u : 0u;
+    }
+    __syncthreads();
+    if (wave_amax[0]) {                                 // uniform: the tile's last workgroup
+      static_assert(T::BN <= T::NT, "one thread per column");
+      const int n = n0 + tid;
+      if (tid < T::BN && n < N) {
+        float sum = 0.0f;
+        for (uint32_t r = 0; r < rows_of_tiles; ++r)
+          sum += __hip_atomic_load(&p.cs_part[(int64_t)r * N + n], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        p.col_sum[n] = sum;
+      }
+    }
+    __syncthreads();                                    // wave_amax is reused below
   }
 
   // ---- AMAX ----
@@ -790,22 +892,31 @@ constexpr TileInfo info_of() {
   return TileInfo{T::BM, T::BN, T::NT, T::WAVES, T::PAIR, T::LDS};
 }
 
-template <class T, int ACT, bool FP8, bool ROWSTAT, bool BNK>
+template <class T, int ACT, bool GRAD, bool FP8, bool ROWSTAT, bool BNK>
 void launch_k(const Params& p, hipStream_t s, unsigned grid) {
   if (p.K % 64 != 0)
-    hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, FP8, ROWSTAT, true, BNK>), dim3(grid), dim3(T::NT), 0, s, p);
+    hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, GRAD, FP8, ROWSTAT, true, BNK>), dim3(grid), dim3(T::NT), 0, s, p);
   else
-    hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, FP8, ROWSTAT, false, BNK>), dim3(grid), dim3(T::NT), 0, s, p);
+    hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, GRAD, FP8, ROWSTAT, false, BNK>), dim3(grid), dim3(T::NT), 0, s, p);
 }
 
 template <class T, int ACT, bool FP8, bool BNK>
 hipError_t launch_t(const Params& p, hipStream_t s) {
   const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * p.batch;
   if (grid <= 0) return hipSuccess;
-  if (p.flags & F_ROW_RMS)
-    launch_k<T, ACT, FP8, true, BNK>(p, s, (unsigned)grid);
-  else
-    launch_k<T, ACT, FP8, false, BNK>(p, s, (unsigned)grid);
+  if (p.flags & F_ACT_GRAD) {
+    // backward epilogue instances: bf16 output, no in-kernel row statistic (checked on the host)
+    if constexpr (!T::PAIR && !FP8) {
+      if (p.flags & F_ROW_RMS) return hipErrorInvalidValue;
+      launch_k<T, ACT, true, false, false, BNK>(p, s, (unsigned)grid);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else if (p.flags & F_ROW_RMS) {
+    launch_k<T, ACT, false, FP8, true, BNK>(p, s, (unsigned)grid);
+  } else {
+    launch_k<T, ACT, false, FP8, false, BNK>(p, s, (unsigned)grid);
+  }
   return hipGetLastError();
 }
 

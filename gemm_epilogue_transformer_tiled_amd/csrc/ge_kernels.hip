@@ -7,6 +7,11 @@
 namespace ge {
 namespace {
 
+__global__ void zero_words_kernel(uint32_t* p, int64_t count) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
 __global__ void amax_zero_kernel(uint32_t* amax) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *amax = 0u;
 }
@@ -38,6 +43,14 @@ hipError_t launch_fused(TileKind kind, int act, bool fp8_out, const Params& p, h
                                      : launch_tile_128x128_pair_kn(act, fp8_out, p, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_zero_words(uint32_t* p, int64_t count, hipStream_t stream) {
+  if (count <= 0) return hipSuccess;
+  const int64_t blocks = (count + 255) / 256;
+  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)(blocks < 65535 ? blocks : 65535)), dim3(256), 0, stream, p,
+                     count);
+  return hipGetLastError();
 }
 
 hipError_t launch_amax_zero(uint32_t* amax, hipStream_t stream) {

@@ -29,6 +29,7 @@ class DeviceProblem:
     Y: torch.Tensor
     amax: Optional[torch.Tensor]
     args: object
+    col_sum: Optional[torch.Tensor] = None
 
     def run(self, stream: Optional[int] = None) -> None:
         self.plan.run(self.args, stream)
@@ -42,11 +43,14 @@ class DeviceProblem:
     def amax_host(self) -> Optional[float]:
         return None if self.amax is None else float(self.amax.item())
 
+    def col_sum_host(self):
+        return None if self.col_sum is None else self.col_sum.cpu().numpy().astype(np.float64)
+
 
 def prepare(w, inputs: Dict[str, np.ndarray], device="cuda", y_fill: Optional[int] = None) -> DeviceProblem:
     """Uploads inputs, allocates Y (and AMAX), creates the plan for workload ``w``."""
     t = {k: to_device_bf16(v, device) for k, v in inputs.items()
-         if k in ("A", "B", "B2", "bias", "R")}
+         if k in ("A", "B", "B2", "bias", "R", "Z")}
     if "row_scale" in inputs:
         t["row_scale"] = torch.from_numpy(np.ascontiguousarray(inputs["row_scale"], dtype=np.float32)).to(device)
     fp8 = w.out == "fp8_e4m3"
@@ -58,10 +62,12 @@ def prepare(w, inputs: Dict[str, np.ndarray], device="cuda", y_fill: Optional[in
     if y_fill is not None:
         Y.view(torch.uint8).fill_(y_fill)
     amax = torch.full((1,), -1.0, dtype=torch.float32, device=device) if w.has("amax") else None
+    col = torch.full((w.N,), float("nan"), dtype=torch.float32, device=device) if w.has("col_sum") else None
     desc = make_desc(w.batch, w.M, w.N, w.K, make_ops(w.chain),
                      y_type=GE_DT_FP8_E4M3 if fp8 else GE_DT_BF16,
                      b_layout=GE_LAYOUT_NK if getattr(w, "b_layout", "kn") == "nk" else GE_LAYOUT_KN)
     plan = Plan(desc)
     args = make_args(A=t.get("A"), B=t.get("B"), B2=t.get("B2"), bias=t.get("bias"), residual=t.get("R"),
-                     row_scale=t.get("row_scale"), Y=Y, amax=amax, alpha=w.alpha, quant_scale=w.quant_scale)
-    return DeviceProblem(w, plan, t, Y, amax, args)
+                     row_scale=t.get("row_scale"), Y=Y, amax=amax, alpha=w.alpha, quant_scale=w.quant_scale,
+                     aux=t.get("Z"), col_sum=col)
+    return DeviceProblem(w, plan, t, Y, amax, args, col)

@@ -33,6 +33,8 @@
  *   B2 same layout, leading dimension and batch stride as B (pairwise only)
  *   Y  [batch][M][N] bf16 or fp8-e4m3 (OCP "e4m3fn"), at Y + b*stride_y + m*ldy + n
  *   R  [batch][M][N] bf16 residual, at R + b*stride_r + m*ldr + n
+ *   Z  [batch][M][N] bf16 saved pre-activation (ACT_GRAD), at aux + b*stride_z + m*ldz + n
+ *   col_sum [N] fp32 (COL_SUM)
  *   bias [N] bf16, shared by every row and batch
  *   row_scale [batch][M] fp32, at row_scale + b*M + m
  *   amax: one fp32 in device memory
@@ -47,7 +49,15 @@
  *   ACT(act)         y = act(t)
  *   PAIRWISE_ACT_MUL(act)  y = act(t_gate) * t_up, gate from B, up from B2; the
  *                    linear ops above apply to both accumulators (exclusive with ACT)
+ *   ACT_GRAD(act)    y = t * act'(Z[b,m,n]) -- the activation-gradient step of a backward
+ *                    pass, dZ = (dY @ W^T) * act'(Z) (CODA news item, "How CODA works":
+ *                    epilogues for the forward and the backward pass); exclusive with ACT
+ *                    and PAIRWISE_ACT_MUL
  *   RESIDUAL         y = y + R[b,m,n]
+ *   COL_SUM          col_sum[n] = sum over b, m of y[b,m,n] in fp32, before any rounding --
+ *                    the column reduction that gives a bias gradient (same item, the
+ *                    "reductions" primitive); overwritten, not accumulated; needs the
+ *                    workspace; deterministic (fixed summation order)
  *   AMAX             *amax = max |y| over all outputs, before any rounding (needs the workspace)
  *   QUANT_FP8        Y = e4m3(clamp(y * quant_scale, -448, 448)), round to
  *                    nearest even; requires y_type == GE_DT_FP8_E4M3 and must be last
@@ -56,9 +66,10 @@
  *   SILU t / (1 + e^-t).
  *
  * Supported shapes: batch >= 0, M >= 0, N >= 0, K >= 0 (K >= 1 with ROW_RMS);
- * N, K, lda, ldb, ldy (and ldr) multiples of 8; lda >= K, ldb >= N, ldy >= N,
- * ldr >= N; every device pointer 16-byte aligned.  Ragged M, N and K tails
- * (not multiples of the tile) are handled inside the kernels.
+ * N, K, lda, ldb, ldy (and ldr, ldz) multiples of 8; lda >= K, ldb >= N ([K][N] B) or
+ * ldb >= K ([N][K] B), ldy >= N, ldr >= N, ldz >= N; every device pointer 16-byte aligned
+ * (col_sum and amax: 4-byte).  Ragged M, N and K tails (not multiples of the tile) are
+ * handled inside the kernels.
  *
  * Ownership: the caller owns every device buffer and the stream.  The
  * library borrows the pointers until the work enqueued by gemm_epilogue_run
@@ -104,12 +115,14 @@ typedef enum {
   GE_OP_PAIRWISE_ACT_MUL = 5,
   GE_OP_RESIDUAL = 6,
   GE_OP_AMAX = 7,
-  GE_OP_QUANT_FP8 = 8
+  GE_OP_QUANT_FP8 = 8,
+  GE_OP_ACT_GRAD = 9,
+  GE_OP_COL_SUM = 10
 } ge_op_kind_t;
 
 typedef struct {
   int32_t kind;     /* ge_op_kind_t */
-  int32_t act;      /* ge_act_t, for ACT and PAIRWISE_ACT_MUL; else 0 */
+  int32_t act;      /* ge_act_t, for ACT, PAIRWISE_ACT_MUL and ACT_GRAD; else 0 */
   float eps;        /* for ROW_RMS; else 0 */
 } ge_op_t;
 
@@ -122,6 +135,7 @@ typedef struct {
   ge_op_t ops[GE_MAX_OPS];
   int32_t b_layout;                             /* ge_layout_t of B and B2 (0 = [K][N]) */
   int32_t reserved;                             /* must be 0 */
+  int64_t ldz, stride_z;                        /* ACT_GRAD: Z leading dimension and batch stride */
 } ge_desc_t;
 
 /* The per-execution "variant pack": borrowed device pointers plus host scalars.
@@ -135,13 +149,15 @@ typedef struct {
   const void* residual;    /* RESIDUAL */
   void* Y;
   float* amax;             /* AMAX: overwritten with max|y| */
-  void* workspace;         /* AMAX only: device scratch of gemm_epilogue_workspace_size bytes,
+  void* workspace;         /* AMAX, COL_SUM: device scratch of gemm_epilogue_workspace_size bytes,
                               16-byte aligned, ZERO-FILLED before its first use; each run leaves
                               it zeroed again when it completes.  Runs that share a workspace
                               must not overlap (order them on one stream). */
   size_t workspace_bytes;
   float alpha;             /* SCALE */
   float quant_scale;       /* QUANT_FP8 */
+  const void* aux;         /* ACT_GRAD: Z, the saved pre-activation */
+  float* col_sum;          /* COL_SUM: N floats, overwritten */
 } ge_args_t;
 
 typedef struct ge_plan* ge_handle_t;
@@ -155,9 +171,10 @@ ge_status_t gemm_epilogue_validate(const ge_desc_t* desc);
  * plan; on failure *out is set to NULL.  Launches nothing. */
 ge_status_t gemm_epilogue_create(const ge_desc_t* desc, ge_handle_t* out);
 
-/* Device scratch the plan needs from the caller, in bytes: with AMAX in the
- * chain 4 * (1024 + number of workgroups) -- nine ticket counters on their own
- * cache lines plus one partial-maximum slot per workgroup; 0 otherwise. */
+/* Device scratch the plan needs from the caller, in bytes; 0 without AMAX and COL_SUM.
+ * AMAX: nine ticket counters on their own cache lines plus one partial-maximum slot per
+ * workgroup.  COL_SUM: one ticket counter per column tile plus one fp32 partial column sum
+ * per row tile, batch and column.  Zero-filled before first use; counters return to zero. */
 ge_status_t gemm_epilogue_workspace_size(ge_handle_t handle, size_t* bytes);
 
 /* Enqueues the fused GEMM + epilogue on `stream` (a hipStream_t; NULL = the

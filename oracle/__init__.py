@@ -32,7 +32,8 @@ from .codecs import (  # noqa: F401
     BF16_MAX, E4M3_MAX, decode_bf16, decode_e4m3, encode_bf16, encode_e4m3,
 )
 from .ops import (  # noqa: F401
-    act, amax, bias_col, gelu_tanh, gemm, pairwise_act_mul, quant_fp8, relu,
-    residual, row_rms_scale, row_scale, scale, silu, silu_exp2_form,
+    act, act_grad, amax, bias_col, col_sum, gelu_tanh, gelu_tanh_grad, gemm, pairwise_act_mul,
+    quant_fp8, relu, relu_grad, residual, row_rms_scale, row_scale, scale, silu, silu_exp2_form,
+    silu_grad,
 )
 from .chain import OracleResult, run_chain, run_workload  # noqa: F401

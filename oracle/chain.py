@@ -10,8 +10,10 @@ removing the epilogue's memory traffic, not from a different result).  So the
 oracle is that sequence, in the canonical order
 
     t = alpha * acc -> t = s[m] * t -> t = t + bias[n]
-      -> y = act(t)   (or y = act(t_gate) * t_up for the pairwise op)
-      -> y = y + R[m, n] -> amax = max|y| -> encode (bf16, or fp8 of y * scale)
+      -> y = act(t)   (or y = act(t_gate) * t_up for the pairwise op,
+                       or y = t * act'(Z[m, n]) for the backward activation gradient)
+      -> y = y + R[m, n] -> colsum[n] = sum_m y -> amax = max|y|
+      -> encode (bf16, or fp8 of y * scale)
 
 AMAX is taken on the unrounded value ``y`` (before the fp8 scale), the value
 whose maximum sets the next quantisation scale.
@@ -33,19 +35,22 @@ class OracleResult:
     codes: np.ndarray             # uint16 bf16 bits or uint8 e4m3 codes
     amax: Optional[float]         # None when the chain has no AMAX op
     out: str                      # "bf16" or "fp8_e4m3"
+    col_sum: Optional[np.ndarray] = None   # [N] float64, when the chain has COL_SUM
 
 
 def run_chain(chain: Sequence[tuple], A: np.ndarray, B: np.ndarray,
               B2: Optional[np.ndarray] = None, bias: Optional[np.ndarray] = None,
               R: Optional[np.ndarray] = None, row_scale_vec: Optional[np.ndarray] = None,
               alpha: float = 1.0, quant_scale: float = 1.0, out: str = "bf16",
-              rows: Optional[np.ndarray] = None, b_layout: str = "kn") -> OracleResult:
+              rows: Optional[np.ndarray] = None, b_layout: str = "kn",
+              Z: Optional[np.ndarray] = None) -> OracleResult:
     """Evaluate ``chain`` on bf16-bit inputs.
 
     A: uint16 [batch, M, K]; B, B2: uint16 [batch, K, N], or [batch, N, K] with
     ``b_layout="nk"`` -- then the product is A @ B^T, the backward-pass form dY @ W^T
     (CODA news item, "How CODA works": forward and backward); bias: uint16 [N];
-    R: uint16 [batch, M, N]; row_scale_vec: float32 [batch, M].
+    R, Z: uint16 [batch, M, N] (Z: the saved pre-activation of ACT_GRAD); row_scale_vec:
+    float32 [batch, M].
     ``rows`` (optional) restricts the evaluation to those rows of every batch
     (the result then has M = len(rows)); AMAX is then over those rows only.
     """
@@ -54,6 +59,8 @@ def run_chain(chain: Sequence[tuple], A: np.ndarray, B: np.ndarray,
         A = A[:, rows, :]
         if R is not None:
             R = R[:, rows, :]
+        if Z is not None:
+            Z = Z[:, rows, :]
         if row_scale_vec is not None:
             row_scale_vec = np.asarray(row_scale_vec)[:, rows]
     kinds = [op[0] for op in chain]
@@ -79,6 +86,7 @@ def run_chain(chain: Sequence[tuple], A: np.ndarray, B: np.ndarray,
     t = linear_part(acc)
     t2 = linear_part(acc2) if acc2 is not None else None
     result_amax = None
+    result_col = None
     y = t
     for op in chain:
         kind = op[0]
@@ -90,6 +98,10 @@ def run_chain(chain: Sequence[tuple], A: np.ndarray, B: np.ndarray,
             y = ops.act(y, op[1])
         elif kind == "pairwise":
             y = ops.pairwise_act_mul(y, t2, op[1])
+        elif kind == "act_grad":
+            y = ops.act_grad(y, decode_bf16(Z), op[1])
+        elif kind == "col_sum":
+            result_col = ops.col_sum(y)
         elif kind == "residual":
             y = ops.residual(y, decode_bf16(R))
         elif kind == "amax":
@@ -102,7 +114,7 @@ def run_chain(chain: Sequence[tuple], A: np.ndarray, B: np.ndarray,
         codes = ops.quant_fp8(y, quant_scale)
     else:
         codes = encode_bf16(y)
-    return OracleResult(y=y, codes=codes, amax=result_amax, out=out)
+    return OracleResult(y=y, codes=codes, amax=result_amax, out=out, col_sum=result_col)
 
 
 def run_workload(w, inputs: Dict[str, np.ndarray], rows=None) -> OracleResult:
@@ -110,4 +122,4 @@ def run_workload(w, inputs: Dict[str, np.ndarray], rows=None) -> OracleResult:
     return run_chain(w.chain, inputs["A"], inputs["B"], inputs.get("B2"), inputs.get("bias"),
                      inputs.get("R"), inputs.get("row_scale"), alpha=w.alpha,
                      quant_scale=w.quant_scale, out=w.out, rows=rows,
-                     b_layout=getattr(w, "b_layout", "kn"))
+                     b_layout=getattr(w, "b_layout", "kn"), Z=inputs.get("Z"))

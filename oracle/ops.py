@@ -104,6 +104,45 @@ def act(t: np.ndarray, name: str) -> np.ndarray:
     return _ACTS[name](t)
 
 
+def relu_grad(z: np.ndarray) -> np.ndarray:
+    """d relu / dz: 1 where z > 0, else 0 (0 at z = 0)."""
+    return (np.asarray(z, dtype=np.float64) > 0.0).astype(np.float64)
+
+
+def gelu_tanh_grad(z: np.ndarray) -> np.ndarray:
+    """d/dz of 0.5 z (1 + tanh(u)), u = sqrt(2/pi) (z + 0.044715 z^3):
+    0.5 (1 + tanh u) + 0.5 z (1 - tanh^2 u) sqrt(2/pi) (1 + 3 * 0.044715 z^2)."""
+    z = np.asarray(z, dtype=np.float64)
+    th = np.tanh(_SQRT_2_OVER_PI * (z + _GELU_CUBIC * z * z * z))
+    return 0.5 * (1.0 + th) + 0.5 * z * (1.0 - th * th) * _SQRT_2_OVER_PI * (1.0 + 3.0 * _GELU_CUBIC * z * z)
+
+
+def silu_grad(z: np.ndarray) -> np.ndarray:
+    """d/dz of z sigmoid(z): sigmoid(z) (1 + z (1 - sigmoid(z)))."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        sg = 1.0 / (1.0 + np.exp(-z))
+    return sg * (1.0 + z * (1.0 - sg))
+
+
+_ACT_GRADS = {"none": lambda z: np.ones_like(np.asarray(z, dtype=np.float64)), "relu": relu_grad,
+              "gelu_tanh": gelu_tanh_grad, "silu": silu_grad}
+
+
+def act_grad(t: np.ndarray, z: np.ndarray, name: str) -> np.ndarray:
+    """Backward epilogue: t * act'(z), z the saved pre-activation -- the activation-gradient
+    step of a backward pass (CODA news item, "How CODA works": epilogues for the forward
+    and the backward pass), dZ = (dY @ W^T) * act'(Z)."""
+    return np.asarray(t, dtype=np.float64) * _ACT_GRADS[name](z)
+
+
+def col_sum(y: np.ndarray) -> np.ndarray:
+    """s[n] = sum over batches and rows of y[b, m, n] -- the column reduction that gives a
+    bias gradient (CODA news item, "How CODA works": the reductions primitive)."""
+    y = np.asarray(y, dtype=np.float64)
+    return y.reshape(-1, y.shape[-1]).sum(axis=0) if y.size else np.zeros(y.shape[-1])
+
+
 def pairwise_act_mul(t_gate: np.ndarray, t_up: np.ndarray, name: str) -> np.ndarray:
     """out = act(gate) * up: the SwiGLU graph of section 7 (out = up * silu(gate))
     and, with no activation, the RMSNorm-MLP product of section 10."""

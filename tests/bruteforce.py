@@ -49,11 +49,28 @@ def act(x: float, name: str) -> float:
     raise ValueError(name)
 
 
-def run_chain_scalar(chain, A, B, B2=None, bias=None, R=None, alpha=1.0, b_layout="kn") -> dict:
+def act_derivative(z: float, name: str) -> float:
+    """Derivative of ``act`` at z, each written from its textbook closed form."""
+    if name == "none":
+        return 1.0
+    if name == "relu":
+        return 1.0 if z > 0 else 0.0
+    if name == "gelu_tanh":
+        c = math.sqrt(2.0 / math.pi)
+        u = c * (z + 0.044715 * z ** 3)
+        return 0.5 * (1.0 + math.tanh(u)) + 0.5 * z * (1.0 / math.cosh(u)) ** 2 * c * (1.0 + 0.134145 * z * z)
+    if name == "silu":
+        sg = 1.0 / (1.0 + math.exp(-z))
+        return sg + z * sg * (1.0 - sg)
+    raise ValueError(name)
+
+
+def run_chain_scalar(chain, A, B, B2=None, bias=None, R=None, alpha=1.0, b_layout="kn", Z=None) -> dict:
     """A: [batch][M][K] floats, B/B2: [batch][K][N] ([batch][N][K] for b_layout "nk");
     bias: [N]; R: [batch][M][N].
 
-    Returns {"y": [batch][M][N] floats (before output encoding), "amax": float|None}.
+    Z: [batch][M][N] (ACT_GRAD).  Returns {"y": [batch][M][N] floats (before output
+    encoding), "amax": float|None, "col_sum": [N] floats|None}.
     """
     kinds = [op[0] for op in chain]
     ys = []
@@ -87,6 +104,8 @@ def run_chain_scalar(chain, A, B, B2=None, bias=None, R=None, alpha=1.0, b_layou
                         vals = [act(vals[0], op[1])]
                     elif op[0] == "pairwise":
                         vals = [act(vals[0], op[1]) * vals[1]]
+                    elif op[0] == "act_grad":
+                        vals = [vals[0] * act_derivative(Z[b][m][n], op[1])]
                     elif op[0] == "residual":
                         vals = [vals[0] + R[b][m][n]]
                 out = vals[0]
@@ -94,4 +113,8 @@ def run_chain_scalar(chain, A, B, B2=None, bias=None, R=None, alpha=1.0, b_layou
                 row.append(out)
             rows.append(row)
         ys.append(rows)
-    return {"y": ys, "amax": amax if "amax" in kinds else None}
+    col = None
+    if "col_sum" in kinds:
+        N = len(ys[0][0]) if ys and ys[0] else 0
+        col = [math.fsum(ys[b][m][n] for b in range(len(ys)) for m in range(len(ys[b]))) for n in range(N)]
+    return {"y": ys, "amax": amax if "amax" in kinds else None, "col_sum": col}

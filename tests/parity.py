@@ -9,6 +9,9 @@
   monotone order of E4M3 values (+0 and -0 count as the same point).
 * AMAX: relative error <= 2e-3 against the oracle's max |y| taken before
   rounding.
+* COL_SUM: each column sum within a floored relative error of 2e-3 of the
+  oracle's float64 sum of the unrounded y (floor: 1e-3 of the largest |sum|):
+  the kernel adds fp32 values of y whose own error is ~1e-6 relative, in fp32.
 """
 from __future__ import annotations
 
@@ -58,6 +61,24 @@ def check_fp8(codes: np.ndarray, ref_codes: np.ndarray, what: str = "") -> int:
         idx = np.unravel_index(int(np.argmax(d)), d.shape)
         raise AssertionError(f"{what}: fp8 code distance {worst} at {idx}: gpu={codes[idx]:#04x} "
                              f"ref={ref_codes[idx]:#04x}; {int((d > 1).sum())} codes off by more than one")
+    return worst
+
+
+COLSUM_TOL = 2e-3
+
+
+def check_col_sum(got: np.ndarray, ref: np.ndarray, what: str = "") -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    if ref.size == 0:
+        return 0.0
+    floor = max(1e-3 * float(np.max(np.abs(ref))), 1e-30)
+    err = np.abs(got - ref) / np.maximum(np.abs(ref), floor)
+    worst = float(err.max())
+    if not worst <= COLSUM_TOL:
+        i = int(np.argmax(err))
+        raise AssertionError(f"{what}: column sum rel err {worst:.3e} at {i}: gpu={got[i]} ref={ref[i]}")
     return worst
 
 

@@ -37,13 +37,18 @@ def _check_against_bruteforce(w, inp):
     res = oracle.run_workload(w, inp)
     bias = oracle.decode_bf16(inp["bias"]).tolist() if "bias" in inp else None
     ref = run_chain_scalar(w.chain, _as_lists(inp, "A"), _as_lists(inp, "B"), _as_lists(inp, "B2"),
-                           bias, _as_lists(inp, "R"), alpha=w.alpha, b_layout=w.b_layout)
+                           bias, _as_lists(inp, "R"), alpha=w.alpha, b_layout=w.b_layout,
+                           Z=_as_lists(inp, "Z"))
     y_ref = np.array(ref["y"], dtype=np.float64)
     assert res.y.shape == y_ref.shape
     assert np.allclose(res.y, y_ref, rtol=1e-12, atol=1e-13), np.abs(res.y - y_ref).max()
     if w.has("amax"):
         assert math.isclose(res.amax, ref["amax"], rel_tol=1e-12)
         assert res.amax == np.abs(res.y).max()
+    if w.has("col_sum"):
+        assert np.allclose(res.col_sum, np.array(ref["col_sum"]), rtol=1e-12, atol=1e-12)
+    else:
+        assert res.col_sum is None
     if w.out == "fp8_e4m3":
         assert res.codes.dtype == np.uint8
         want = oracle.encode_e4m3(np.clip(y_ref * w.quant_scale, -448, 448))
@@ -181,3 +186,22 @@ def test_planted_e4m3_truncation_is_caught(monkeypatch):
         y = res.y * w.quant_scale
         want = np.array([_brute_force_e4m3(float(v)) for v in y.ravel()], dtype=np.uint8)
         assert np.array_equal(res.codes.ravel(), want)
+
+
+BACKWARD_CHAINS = [
+    (("act_grad", "gelu_tanh"), ("col_sum",)),
+    (("act_grad", "silu"), ("col_sum",)),
+    (("act_grad", "relu"), ("residual",), ("col_sum",), ("amax",)),
+    (("scale",), ("bias",), ("act_grad", "gelu_tanh"), ("col_sum",)),
+    (("act", "relu"), ("col_sum",)),
+]
+
+
+@pytest.mark.parametrize("layout", ["nk", "kn"])
+@pytest.mark.parametrize("chain", BACKWARD_CHAINS, ids=lambda c: "-".join(op[0] for op in c))
+def test_backward_chains_match_bruteforce(chain, layout):
+    w = dataclasses.replace(workloads.WORKLOADS["f2"], chain=chain, b_layout=layout, alpha=0.75,
+                            bias_var=0.3).with_shape(batch=2, M=3, N=5, K=16)
+    inp = workloads.generate(w)
+    assert ("Z" in inp) == w.has("act_grad")
+    _check_against_bruteforce(w, inp)

@@ -178,3 +178,46 @@ def test_quant_fp8_scales_then_clamps():
 def test_bruteforce_bf16_decoder_agrees_with_field_definition():
     for bits in [0x3F80, 0xBF80, 0x0001, 0x7F7F, 0x4049, 0x0080]:
         assert bf16_value(bits) == oracle.decode_bf16(np.array([bits], dtype=np.uint16))[0]
+
+
+@pytest.mark.parametrize("name", ["none", "relu", "gelu_tanh", "silu"])
+def test_act_grad_matches_central_differences_of_the_activation(name):
+    """act'(z) against (act(z+h) - act(z-h)) / 2h of the oracle's own activation (away from
+    ReLU's kink): a dropped term or a wrong sign in the derivative shows up here."""
+    z = np.concatenate([np.linspace(-6.0, -0.05, 60), np.linspace(0.05, 6.0, 60)])
+    h = 1e-5
+    fd = (ops.act(z + h, name) - ops.act(z - h, name)) / (2 * h)
+    got = ops.act_grad(np.ones_like(z), z, name)
+    assert np.allclose(got, fd, rtol=1e-6, atol=1e-9), np.abs(got - fd).max()
+
+
+def test_act_grad_special_values_and_torch_autograd():
+    assert ops.gelu_tanh_grad(np.array([0.0]))[0] == 0.5
+    assert ops.silu_grad(np.array([0.0]))[0] == 0.5
+    assert list(ops.relu_grad(np.array([-1.0, 0.0, 2.0]))) == [0.0, 0.0, 1.0]
+    assert abs(ops.gelu_tanh_grad(np.array([12.0]))[0] - 1.0) < 1e-12
+    assert abs(ops.gelu_tanh_grad(np.array([-12.0]))[0]) < 1e-12
+    assert abs(ops.silu_grad(np.array([40.0]))[0] - 1.0) < 1e-12
+    # torch's float64 autograd of its own GELU (tanh approximation) and SiLU
+    z = torch.linspace(-5, 5, 101, dtype=torch.float64, requires_grad=True)
+    torch.nn.functional.gelu(z, approximate="tanh").sum().backward()
+    assert np.allclose(ops.gelu_tanh_grad(z.detach().numpy()), z.grad.numpy(), rtol=1e-12, atol=1e-14)
+    z.grad = None
+    torch.nn.functional.silu(z).sum().backward()
+    assert np.allclose(ops.silu_grad(z.detach().numpy()), z.grad.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_act_grad_multiplies_the_incoming_gradient():
+    t = np.array([[[2.0, -3.0, 0.5]]])
+    z = np.array([[[1.0, -1.0, 0.0]]])
+    assert np.array_equal(ops.act_grad(t, z, "relu"), np.array([[[2.0, -0.0, 0.0]]]))
+    assert np.array_equal(ops.act_grad(t, z, "none"), t)
+
+
+def test_col_sum_over_rows_and_batches():
+    y = np.arange(2 * 3 * 4, dtype=np.float64).reshape(2, 3, 4)
+    want = [sum(y[b, m, n] for b in range(2) for m in range(3)) for n in range(4)]
+    assert list(ops.col_sum(y)) == want
+    assert list(ops.col_sum(np.zeros((1, 0, 5)))) == [0.0] * 5
+    # a column of ones over M rows and B batches sums to M*B
+    assert ops.col_sum(np.ones((3, 7, 2)))[1] == 21.0

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import workloads
-from tests.parity import check_amax, check_bf16, check_fp8
+from tests.parity import check_amax, check_bf16, check_col_sum, check_fp8
 
 pytestmark = pytest.mark.gpu
 
@@ -69,6 +69,8 @@ def compare(w, inp, prob, what, rows=None):
         check_bf16(y, ref.y, what)
     if w.has("amax") and rows is None:
         check_amax(prob.amax_host(), ref.amax, what)
+    if w.has("col_sum") and rows is None:
+        check_col_sum(prob.col_sum_host(), ref.col_sum, what)
     return ref
 
 
@@ -279,7 +281,7 @@ def test_fp8_writer_over_every_bf16_value_in_range():
 # The five workloads at full size, in the benchmark's launch configuration.
 # ---------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", workloads.CONFIG_ORDER + ["f1"])
+@pytest.mark.parametrize("name", workloads.CONFIG_ORDER + ["f1", "f2"])
 def test_full_workload(name):
     w = workloads.WORKLOADS[name]
     inp = workloads.generate(w)
@@ -354,3 +356,69 @@ def test_graph_replays_match_eager_runs(name):
         prob.run()                                  # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(prob.Y, y_eager)
+
+
+
+# ---------------------------------------------------------------------------------------------
+# Backward-pass epilogues: activation gradient with the saved pre-activation, column sums.
+# ---------------------------------------------------------------------------------------------
+
+BACKWARD_CHAINS = [
+    (("act_grad", "gelu_tanh"), ("col_sum",)),
+    (("act_grad", "silu"), ("col_sum",)),
+    (("act_grad", "relu"), ("residual",), ("col_sum",), ("amax",)),
+    (("scale",), ("bias",), ("act_grad", "gelu_tanh"), ("col_sum",)),
+    (("act_grad", "none"),),
+    (("act", "relu"), ("col_sum",)),
+]
+
+
+@pytest.mark.parametrize("layout", ["nk", "kn"])
+@pytest.mark.parametrize("tile", SINGLE_TILES, ids=[TILE_NAMES[t] for t in SINGLE_TILES])
+@pytest.mark.parametrize("chain", BACKWARD_CHAINS, ids=lambda c: "-".join(op[0] + (op[1] if len(op) > 1 and isinstance(op[1], str) else "") for op in c))
+def test_backward_chains_every_tile(chain, tile, layout):
+    w = dataclasses.replace(workloads.WORKLOADS["f2"], chain=chain, b_layout=layout, alpha=0.75,
+                            bias_var=0.3).with_shape(**RAGGED)
+    inp = workloads.generate(w)
+    compare(w, inp, gpu_run(w, inp, tile), f"backward {chain} tile {TILE_NAMES[tile]} {layout}")
+
+
+@pytest.mark.parametrize("tile", PAIR_TILES, ids=[TILE_NAMES[t] for t in PAIR_TILES])
+def test_col_sum_of_the_pairwise_product(tile):
+    w = dataclasses.replace(workloads.WORKLOADS["c3"], chain=(("pairwise", "silu"), ("col_sum",))).with_shape(**RAGGED)
+    inp = workloads.generate(w)
+    compare(w, inp, gpu_run(w, inp, tile), f"pairwise col_sum tile {TILE_NAMES[tile]}")
+
+
+def test_col_sum_is_deterministic_and_leaves_the_workspace_zeroed():
+    w = dataclasses.replace(workloads.WORKLOADS["f2"]).with_shape(batch=2, M=1000, N=1032, K=512)
+    inp = workloads.generate(w)
+    prob = gpu_run(w, inp)
+    first = prob.col_sum.clone()
+    compare(w, inp, prob, "f2 batch 2")
+    for _ in range(3):
+        prob.run()
+    torch.cuda.synchronize()
+    assert torch.equal(prob.col_sum, first)          # fixed summation order: bit-identical
+    ws = prob.plan.workspace
+    assert int(ws.view(torch.int32)[:1024].count_nonzero()) == 0 or not w.has("amax")
+    # every column-tile counter is back at zero (the partial sums may stay)
+    tiles_n = (w.N + 255) // 256 if "256x256" in prob.plan.describe() else None
+    if tiles_n is not None:
+        ctr = ws.view(torch.int32)[: tiles_n * 16]
+        assert int(ctr.count_nonzero()) == 0
+
+
+def test_col_sum_of_an_empty_problem_is_zero():
+    w = dataclasses.replace(workloads.WORKLOADS["f2"]).with_shape(batch=1, M=0, N=264, K=64)
+    inp = workloads.generate(w)
+    prob = gpu_run(w, inp)
+    assert float(prob.col_sum.abs().max().item()) == 0.0
+
+
+def test_act_grad_rejects_fp8_output_and_row_rms():
+    base = dict(batch=1, M=64, N=64, K=64)
+    bad1 = ge.make_desc(ops=ge.make_ops([("act_grad", "gelu_tanh"), ("quant_fp8",)]), y_type=ge.GE_DT_FP8_E4M3, **base)
+    bad2 = ge.make_desc(ops=ge.make_ops([("row_rms", 1e-6), ("act_grad", "gelu_tanh")]), **base)
+    assert ge.gemm_epilogue_validate(bad1) == ge.GE_ERR_UNSUPPORTED
+    assert ge.gemm_epilogue_validate(bad2) == ge.GE_ERR_UNSUPPORTED

@@ -29,7 +29,7 @@ from typing import Dict, List, Optional, Tuple
 import numpy as np
 
 # Tensor ids of the seeded streams.
-T_A, T_B, T_B2, T_BIAS, T_R, T_G, T_W = 0, 1, 2, 3, 4, 5, 6
+T_A, T_B, T_B2, T_BIAS, T_R, T_G, T_W, T_Z = 0, 1, 2, 3, 4, 5, 6, 7
 
 
 @dataclasses.dataclass(frozen=True)
@@ -38,9 +38,9 @@ class Workload:
 
     ``chain`` lists the epilogue ops in their canonical order as plain tuples:
     ``("scale",)``, ``("row_rms", eps)``, ``("bias",)``, ``("act", name)``,
-    ``("pairwise", act_name)``, ``("residual",)``, ``("amax",)``,
-    ``("quant_fp8",)``.  Activation names: ``none``, ``relu``, ``gelu_tanh``,
-    ``silu``.
+    ``("pairwise", act_name)``, ``("act_grad", act_name)``, ``("residual",)``,
+    ``("col_sum",)``, ``("amax",)``, ``("quant_fp8",)``.  Activation names: ``none``,
+    ``relu``, ``gelu_tanh``, ``silu``.
     """
 
     name: str
@@ -86,6 +86,10 @@ class Workload:
             nbytes += 2 * self.N
         if self.has("residual"):
             nbytes += 2 * b * self.M * self.N
+        if self.has("act_grad"):
+            nbytes += 2 * b * self.M * self.N
+        if self.has("col_sum"):
+            nbytes += 4 * self.N
         nbytes += (1 if self.out == "fp8_e4m3" else 2) * b * self.M * self.N
         if self.has("amax"):
             nbytes += 4
@@ -138,6 +142,18 @@ WORKLOADS["f1"] = Workload(
     a_var="1", b_var="1/K",
     description="RMSNorm-MLP: (S*X@Wg')*(S*X@Wu'), S = 1/rms(X), gain U(0.5,1.5) folded into Wg and Wu, "
                 "X[8192x4096] N(0,1), W[4096x11008] N(0,1/4096), no activation")
+
+# The backward-pass epilogue (CODA news item, "How CODA works": forward and backward): for a
+# GELU MLP layer H = GELU(Z1), Y = H @ W2 with W2 stored [hidden][d], the gradient step
+# dZ1 = (dY @ W2^T) * GELU'(Z1) with the bias gradient db1 = sum over rows of dZ1, in one
+# kernel: A = dY [8192 x 4096], B = W2 stored [N = 11008][K = 4096] (the [N][K] layout),
+# Z = Z1 [8192 x 11008].
+WORKLOADS["f2"] = Workload(
+    name="f2", config_id=7, batch=1, M=8192, N=11008, K=4096,
+    chain=(("act_grad", "gelu_tanh"), ("col_sum",)),
+    a_var="1", b_var="1/K", b_layout="nk",
+    description="MLP backward: dZ1 = (dY@W2^T)*GELU'(Z1), db1 = colsum(dZ1); dY[8192x4096] N(0,1), "
+                "W2 stored [11008x4096] N(0,1/4096), Z1 N(0,1)")
 
 CONFIG_ORDER: List[str] = ["c1", "c2", "c3", "c4", "c5"]
 
@@ -210,4 +226,7 @@ def generate(w: Workload, sensitive: bool = False, seed_offset: int = 0) -> Dict
             out["bias"] = _normal_bf16(cid, T_BIAS, (N,), w.bias_var)
     if w.has("residual"):
         out["R"] = _normal_bf16(cid, T_R, (b, M, N), 1.0)
+    if w.has("act_grad"):
+        # the saved pre-activation of the forward pass, N(0, 1)
+        out["Z"] = _normal_bf16(cid, T_Z, (b, M, N), 1.0)
     return out
