@@ -64,8 +64,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "f1"],
-                    help="c1..c5: the five configurations; f1: the RMSNorm-MLP (row RMS + pairwise product)")
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "f1", "f2"],
+                    help="c1..c5: the five configurations; f1: the RMSNorm-MLP (row RMS + pairwise "
+                         "product); f2: the MLP backward step (activation gradient + column sums, B as [N][K])")
     ap.add_argument("--launch", default="auto", choices=["auto", "eager", "graph"],
                     help="issue the timed steps eagerly or as one HIP-graph replay (auto: the faster on a probe)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle timing sample")

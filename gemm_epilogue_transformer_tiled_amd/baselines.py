@@ -14,7 +14,7 @@ from typing import Dict, List, Optional, Tuple
 
 import torch
 
-from . import GE_DT_BF16, Plan, make_args, make_desc, make_ops
+from . import GE_DT_BF16, GE_LAYOUT_KN, GE_LAYOUT_NK, Plan, make_args, make_desc, make_ops
 from .runner import to_device_bf16
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libge_baselines.so")
 
 EXPORTED = ("ge_unfused_scale", "ge_unfused_bias_col", "ge_unfused_act", "ge_unfused_act_mul",
             "ge_unfused_row_rms", "ge_unfused_row_scale", "ge_unfused_add", "ge_unfused_amax",
-            "ge_unfused_quant_fp8", "ge_probe_mfma", "ge_probe_copy")
+            "ge_unfused_quant_fp8", "ge_unfused_act_grad", "ge_unfused_col_sum", "ge_probe_mfma",
+            "ge_probe_copy")
 ACTS = {"none": 0, "relu": 1, "gelu_tanh": 2, "silu": 3}
 
 _p, _i64, _i, _f = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
@@ -36,6 +37,8 @@ _SIGS = {
     "ge_unfused_add": [_p, _p, _p, _i64, _p],
     "ge_unfused_amax": [_p, _i64, _p, _p],
     "ge_unfused_quant_fp8": [_p, _p, _i64, _f, _p],
+    "ge_unfused_act_grad": [_p, _p, _p, _i64, _i, _p],
+    "ge_unfused_col_sum": [_p, _p, _i64, _i64, _p],
     "ge_probe_mfma": [_p, _i, _i, _p],
     "ge_probe_copy": [_p, _p, _i64, _p],
 }
@@ -73,7 +76,7 @@ class Unfused:
 
     def __init__(self, w, inputs: Dict, device="cuda"):
         self.w = w
-        t = {k: to_device_bf16(v, device) for k, v in inputs.items() if k in ("A", "B", "B2", "bias", "R")}
+        t = {k: to_device_bf16(v, device) for k, v in inputs.items() if k in ("A", "B", "B2", "bias", "R", "Z")}
         if "row_scale" in inputs:
             import numpy as np
             t["row_scale"] = torch.from_numpy(np.ascontiguousarray(inputs["row_scale"], dtype=np.float32)).to(device)
@@ -81,6 +84,7 @@ class Unfused:
         rows, n_out = w.batch * w.M, w.batch * w.M * w.N
         bf = lambda *shape: torch.empty(*shape, dtype=torch.bfloat16, device=device)
         self.amax = torch.zeros(1, dtype=torch.float32, device=device) if w.has("amax") else None
+        self.col_sum = torch.zeros(w.N, dtype=torch.float32, device=device) if w.has("col_sum") else None
         self.plans: List[Plan] = []
         steps: List[Tuple[str, object, int, int]] = []
         A = t["A"]
@@ -112,6 +116,11 @@ class Unfused:
             kind = op[0]
             if kind in ("pairwise", "row_rms"):
                 continue
+            if kind == "col_sum":
+                steps.append(("col_sum", lambda x=cur: call(
+                    "ge_unfused_col_sum", x.data_ptr(), self.col_sum.data_ptr(), rows, w.N, _stream()),
+                    n_out * 2, w.N * 4))
+                continue
             if kind == "amax":
                 steps.append(("amax", lambda x=cur: call(
                     "ge_unfused_amax", x.data_ptr(), n_out, self.amax.data_ptr(), _stream()), n_out * 2, 4))
@@ -142,6 +151,11 @@ class Unfused:
                 fn = lambda x=cur, y=Y, act=act: call("ge_unfused_act", x.data_ptr(), y.data_ptr(), n_out, act,
                                                       _stream())
                 rd = n_out * 2
+            elif kind == "act_grad":
+                act = ACTS[op[1]]
+                fn = lambda x=cur, y=Y, act=act: call("ge_unfused_act_grad", x.data_ptr(), t["Z"].data_ptr(),
+                                                      y.data_ptr(), n_out, act, _stream())
+                rd = 2 * n_out * 2
             elif kind == "residual":
                 fn = lambda x=cur, y=Y: call("ge_unfused_add", x.data_ptr(), t["R"].data_ptr(), y.data_ptr(), n_out,
                                              _stream())
@@ -155,7 +169,8 @@ class Unfused:
 
     def _gemm(self, A, B, C):
         w = self.w
-        plan = Plan(make_desc(w.batch, w.M, w.N, w.K, make_ops([]), y_type=GE_DT_BF16))
+        plan = Plan(make_desc(w.batch, w.M, w.N, w.K, make_ops([]), y_type=GE_DT_BF16,
+                              b_layout=GE_LAYOUT_NK if w.b_layout == "nk" else GE_LAYOUT_KN))
         self.plans.append(plan)
         args = make_args(A=A, B=B, Y=C)
         return lambda: plan.run(args)
@@ -169,6 +184,9 @@ class Unfused:
 
     def kernels(self) -> List[str]:
         return [s[0] for s in self.steps]
+
+    def col_sum_host(self):
+        return None if self.col_sum is None else self.col_sum.cpu().numpy().astype("float64")
 
     def amax_host(self) -> Optional[float]:
         return None if self.amax is None else float(self.amax.item())

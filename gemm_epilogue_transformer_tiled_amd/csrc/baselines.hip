@@ -46,6 +46,23 @@ __device__ __forceinline__ float act_fn(int act, float t) {
   }
 }
 
+// Derivatives of the activations above at z.
+__device__ __forceinline__ float act_grad_fn(int act, float z) {
+  switch (act) {
+    case 1: return z > 0.0f ? 1.0f : 0.0f;
+    case 2: {
+      const float c = 0.7978845608028654f;
+      const float th = tanhf(c * (z + 0.044715f * z * z * z));
+      return 0.5f * (1.0f + th) + 0.5f * z * (1.0f - th * th) * c * (1.0f + 3.0f * 0.044715f * z * z);
+    }
+    case 3: {
+      const float sg = 1.0f / (1.0f + expf(-z));
+      return sg * (1.0f + z * (1.0f - sg));
+    }
+    default: return 1.0f;
+  }
+}
+
 int64_t blocks_for(int64_t items) {
   int64_t b = (items + kThreads - 1) / kThreads;
   return b < 1 ? 1 : (b > kMaxBlocks ? kMaxBlocks : b);
@@ -103,6 +120,10 @@ struct ActMul {
   int act;
   __device__ float operator()(float g, float u) const { return act_fn(act, g) * u; }
 };
+struct ActGrad {
+  int act;
+  __device__ float operator()(float x, float z) const { return x * act_grad_fn(act, z); }
+};
 struct Add {
   __device__ float operator()(float a, float b) const { return a + b; }
 };
@@ -134,6 +155,16 @@ __global__ __launch_bounds__(kThreads) void row_scale_kernel(const uint16_t* __r
     for (int j = 0; j < 4; ++j) o[j] = pack(lo(w[j]) * r, hi(w[j]) * r);
     *(u32x4_t*)(y + 8 * (int64_t)v) = o;
   }
+}
+
+// ---- column sums: one thread per column, rows added in order ----
+__global__ __launch_bounds__(kThreads) void col_sum_kernel(const uint16_t* __restrict__ x, float* __restrict__ out,
+                                                           int64_t rows, int64_t cols) {
+  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (c >= cols) return;
+  float acc = 0.0f;
+  for (int64_t r = 0; r < rows; ++r) acc += bf(x[r * cols + c]);
+  out[c] = acc;
 }
 
 // ---- row statistic: one workgroup per row ----
@@ -291,6 +322,18 @@ int ge_unfused_row_scale(const uint16_t* x, const float* s, uint16_t* y, int64_t
   if (nv == 0) return 0;
   return launch(row_scale_kernel, blocks_for(nv), (hipStream_t)stream, x, s, y, (uint32_t)nv,
                 (uint32_t)(cols / 8));
+}
+
+int ge_unfused_act_grad(const uint16_t* x, const uint16_t* z, uint16_t* y, int64_t n, int act, void* stream) {
+  if (n < 0 || act < 0 || act > 3 || (n > 0 && (!x || !z || !y))) return 1;
+  if (n == 0) return 0;
+  return launch(map2<ActGrad>, blocks_for(n / 8 + 1), (hipStream_t)stream, x, z, y, n, ActGrad{act});
+}
+
+int ge_unfused_col_sum(const uint16_t* x, float* out, int64_t rows, int64_t cols, void* stream) {
+  if (rows < 0 || cols < 0 || (cols > 0 && !out) || (rows * cols > 0 && !x)) return 1;
+  if (cols == 0) return 0;
+  return launch(col_sum_kernel, (cols + kThreads - 1) / kThreads, (hipStream_t)stream, x, out, rows, cols);
 }
 
 int ge_unfused_add(const uint16_t* x, const uint16_t* r, uint16_t* y, int64_t n, void* stream) {

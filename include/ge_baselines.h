@@ -55,6 +55,14 @@ int ge_unfused_row_rms(const uint16_t* x, float* s, int64_t rows, int64_t cols, 
 int ge_unfused_row_scale(const uint16_t* x, const float* s, uint16_t* y, int64_t rows, int64_t cols,
                          void* stream);
 
+/* y[i] = bf16(x[i] * act'(z[i])) -- the backward activation gradient with the saved
+ * pre-activation z; act as in ge_unfused_act. */
+int ge_unfused_act_grad(const uint16_t* x, const uint16_t* z, uint16_t* y, int64_t n, int act, void* stream);
+
+/* out[c] = sum over r of x[r][c] in fp32 (rows x cols bf16 x; rows summed in order) -- the
+ * bias-gradient column reduction. */
+int ge_unfused_col_sum(const uint16_t* x, float* out, int64_t rows, int64_t cols, void* stream);
+
 /* y[i] = bf16(x[i] + r[i]) -- residual add. */
 int ge_unfused_add(const uint16_t* x, const uint16_t* r, uint16_t* y, int64_t n, void* stream);
 
