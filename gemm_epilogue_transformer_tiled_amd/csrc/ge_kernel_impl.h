@@ -653,10 +653,11 @@ void fused_gemm_epilogue(Params p) {
 
   uint32_t amax_bits = 0;
   float csum[4] = {0.0f, 0.0f, 0.0f, 0.0f};    // COL_SUM: this lane's four columns
-  // Residual rows of a 32-row block, in phase-2 layout, loaded at the start of the block so
-  // that phase 1 hides their latency.  (The saved pre-activation of ACT_GRAD is loaded per
-  // chunk inside phase 2: registers.)
+  // Residual rows (and, for the activation gradient, saved pre-activation rows) of a 32-row
+  // block, in phase-2 layout, loaded at the start of the block so that phase 1 hides their
+  // latency.
   u32x2_t rvb[1][PASSES];
+  u32x2_t zvb[GRAD ? PASSES : 1];
   auto load_rows = [&](int j, __amdgpu_buffer_rsrc_t rs, uint32_t ld_b, u32x2_t* rv) {
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
@@ -667,6 +668,7 @@ void fused_gemm_epilogue(Params p) {
   };
   auto prefetch = [&](int j) {
     if (has_res) load_rows(j, r_rs, ldr_b, rvb[0]);
+    if constexpr (GRAD) load_rows(j, z_rs, ldz_b, zvb);
   };
   // Phase 2 in chunks of PCH passes (bounds the registers the batched LDS reads and the
   // saved pre-activation occupy).
@@ -675,15 +677,6 @@ void fused_gemm_epilogue(Params p) {
     constexpr bool RES = decltype(res_c)::value;
 #pragma unroll
     for (int c0 = 0; c0 < PASSES; c0 += PCH) {
-    u32x2_t zv[GRAD ? PCH : 1];
-    if constexpr (GRAD) {
-#pragma unroll
-      for (int q = 0; q < PCH; ++q) {
-        const int ml = wm0 + 32 * j + (c0 + q) * RPP + p2_row;
-        const uint32_t off = (m0 + ml < M) ? (uint32_t)ml * ldz_b + col_r : kOOB;
-        zv[q] = __builtin_amdgcn_raw_buffer_load_b64(z_rs, off | (col_r & kOOB), 0, 0);
-      }
-    }
     f32x4_t vv[PCH];
 #pragma unroll
     for (int q = 0; q < PCH; ++q) vv[q] = *(const f32x4_t*)(ep + ((c0 + q) * RPP + p2_row) * EP_LD + p2_col);
@@ -700,7 +693,7 @@ void fused_gemm_epilogue(Params p) {
         if constexpr (T::PAIR) {
           y[e] = v[e];
         } else if constexpr (GRAD) {
-          const uint32_t zw = zv[q][e >> 1];
+          const uint32_t zw = zvb[c0 + q][e >> 1];
           y[e] = (v[e] + bias4[e]) * activate_grad<ACT>((e & 1) ? bf16_hi(zw) : bf16_lo(zw));
         } else {
           y[e] = activate<ACT>(v[e] + bias4[e]);
