@@ -44,8 +44,9 @@ METRIC = "fused GEMM-epilogue TFLOP/s (% of MI355X bf16 MFMA peak) per config"
 # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE (x2.0) + WRITE_SIZE (x1.0) of the fused
 # kernel at each workload; the factors scale the counters to the bytes of a plain 1 GiB device
 # copy.  Valid only for the kernel source they were taken on (sha256 prefix below).
-MEASURED_TRAFFIC_SOURCE = "0a4fc6489d185a05"
-MEASURED_TRAFFIC = {"c1": 1043223, "c2": 101168759, "c3": 3053782077, "c4": 537491895, "c5": 1833042778}
+MEASURED_TRAFFIC_SOURCE = "c3cc0fce483d0c9a"
+MEASURED_TRAFFIC = {"c1": 1062063, "c2": 101278629, "c3": 2717362921, "c4": 537505063, "c5": 1870328884,
+                    "f1": 3316143244, "f2": 1806596797}
 
 
 def kernel_source_hash():
