@@ -14,8 +14,8 @@ from typing import Dict, List, Optional, Tuple
 
 import torch
 
-from . import GE_DT_BF16, GE_LAYOUT_KN, GE_LAYOUT_NK, Plan, make_args, make_desc, make_ops
-from .runner import to_device_bf16
+from . import GE_DT_BF16, GE_DT_FP8_E4M3, GE_LAYOUT_KN, GE_LAYOUT_NK, Plan, make_args, make_desc, make_ops
+from .runner import to_device
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libge_baselines.so")
@@ -76,7 +76,7 @@ class Unfused:
 
     def __init__(self, w, inputs: Dict, device="cuda"):
         self.w = w
-        t = {k: to_device_bf16(v, device) for k, v in inputs.items() if k in ("A", "B", "B2", "bias", "R", "Z")}
+        t = {k: to_device(v, device) for k, v in inputs.items() if k in ("A", "B", "B2", "bias", "R", "Z")}
         if "row_scale" in inputs:
             import numpy as np
             t["row_scale"] = torch.from_numpy(np.ascontiguousarray(inputs["row_scale"], dtype=np.float32)).to(device)
@@ -88,7 +88,7 @@ class Unfused:
         self.plans: List[Plan] = []
         steps: List[Tuple[str, object, int, int]] = []
         A = t["A"]
-        a_bytes = A.numel() * 2
+        a_bytes = A.numel() * A.element_size()      # fp8 operands: one byte per element
         # RMS: statistic kernel, normalisation kernel, then the GEMM on the normalised rows
         if w.has("row_rms"):
             S = torch.empty(rows, dtype=torch.float32, device=device)
@@ -101,11 +101,12 @@ class Unfused:
                 a_bytes + rows * 4, a_bytes))
             A = Xn
         C = bf(w.batch, w.M, w.N)
-        steps.append(("gemm", self._gemm(A, t["B"], C), A.numel() * 2 + t["B"].numel() * 2, n_out * 2))
+        nb = lambda x: x.numel() * x.element_size()
+        steps.append(("gemm", self._gemm(A, t["B"], C), nb(A) + nb(t["B"]), n_out * 2))
         cur = C
         if w.pairwise:
             U = bf(w.batch, w.M, w.N)
-            steps.append(("gemm_up", self._gemm(A, t["B2"], U), A.numel() * 2 + t["B2"].numel() * 2, n_out * 2))
+            steps.append(("gemm_up", self._gemm(A, t["B2"], U), nb(A) + nb(t["B2"]), n_out * 2))
             Y = bf(w.batch, w.M, w.N)
             act = ACTS[w.op("pairwise")[1]]
             steps.append(("act_mul", lambda g=cur, u=U, y=Y, act=act: call(
@@ -169,7 +170,8 @@ class Unfused:
 
     def _gemm(self, A, B, C):
         w = self.w
-        plan = Plan(make_desc(w.batch, w.M, w.N, w.K, make_ops([]), y_type=GE_DT_BF16,
+        in_t = GE_DT_FP8_E4M3 if A.dtype == torch.uint8 else GE_DT_BF16
+        plan = Plan(make_desc(w.batch, w.M, w.N, w.K, make_ops([]), y_type=GE_DT_BF16, a_type=in_t, b_type=in_t,
                               b_layout=GE_LAYOUT_NK if w.b_layout == "nk" else GE_LAYOUT_KN))
         self.plans.append(plan)
         args = make_args(A=A, B=B, Y=C)

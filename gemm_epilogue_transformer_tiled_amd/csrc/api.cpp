@@ -117,8 +117,17 @@ ge_status_t gemm_epilogue_validate(const ge_desc_t* d) {
   const bool quant = has_op(d, GE_OP_QUANT_FP8);
   if (has_op(d, GE_OP_ROW_RMS) && d->K < 1) return GE_ERR_INVALID_ARG;
 
-  // dtypes
-  if (d->a_type != GE_DT_BF16 || d->b_type != GE_DT_BF16) return GE_ERR_UNSUPPORTED;
+  // dtypes: bf16 operands, or fp8-e4m3 operands with B given [N][K]
+  auto known = [](int32_t t) { return t == GE_DT_BF16 || t == GE_DT_FP8_E4M3 || t == GE_DT_FP32; };
+  if (!known(d->a_type) || !known(d->b_type)) return GE_ERR_INVALID_ARG;
+  const bool f8in = d->a_type == GE_DT_FP8_E4M3;
+  if (f8in) {
+    if (d->b_type != GE_DT_FP8_E4M3 || !bnk) return GE_ERR_UNSUPPORTED;
+    // the fp8 instances run forward epilogues without the in-kernel row statistic
+    if (has_op(d, GE_OP_ROW_RMS) || has_op(d, GE_OP_ACT_GRAD)) return GE_ERR_UNSUPPORTED;
+  } else if (d->a_type != GE_DT_BF16 || d->b_type != GE_DT_BF16) {
+    return GE_ERR_UNSUPPORTED;
+  }
   if (d->y_type == GE_DT_FP8_E4M3) {
     if (!quant) return GE_ERR_INVALID_ARG;
   } else if (d->y_type == GE_DT_BF16) {
@@ -146,8 +155,10 @@ ge_status_t gemm_epilogue_validate(const ge_desc_t* d) {
   if (res && d->M > 0 && d->ldr < d->N) return GE_ERR_INVALID_ARG;
   if (d->batch > 1 && d->stride_y == 0 && d->M > 0 && d->N > 0) return GE_ERR_INVALID_ARG;  // batches would race
 
-  // supported set: 16-byte vector access everywhere
+  // supported set: 16-byte vector access everywhere (16 fp8 operand values per 16 bytes)
   if (d->N % 8 || d->K % 8) return GE_ERR_UNSUPPORTED;
+  if (f8in && (d->K % 16 || d->lda % 16 || d->ldb % 16 || d->stride_a % 16 || d->stride_b % 16))
+    return GE_ERR_UNSUPPORTED;
   if (d->lda % 8 || d->ldb % 8 || d->ldy % 8 || (res && d->ldr % 8)) return GE_ERR_UNSUPPORTED;
   if (d->stride_a % 8 || d->stride_b % 8 || d->stride_y % 8 || (res && d->stride_r % 8))
     return GE_ERR_UNSUPPORTED;
@@ -157,9 +168,11 @@ ge_status_t gemm_epilogue_validate(const ge_desc_t* d) {
   // Kernels address each operand with 32-bit byte offsets from a per-tile base and mark
   // masked accesses with an offset of 2^31; every offset a tile can form (one tile and one
   // K step past the end included) must therefore stay below 2^31.
-  if (extent_elems(d->M + 256, d->K + 64, d->lda) * 2 > kMaxExtent) return GE_ERR_UNSUPPORTED;
+  // (operand element size ae; one A slot spans slot_k K values)
+  const int64_t ae = f8in ? 1 : 2, slot_k = f8in ? 128 : 64;
+  if (extent_elems(d->M + 256, d->K + slot_k, d->lda) * ae > kMaxExtent) return GE_ERR_UNSUPPORTED;
   if (!bnk && extent_elems(d->K + 128, d->N, d->ldb) * 2 > kMaxExtent) return GE_ERR_UNSUPPORTED;
-  if (bnk && extent_elems(d->N + 256, d->K + 64, d->ldb) * 2 > kMaxExtent) return GE_ERR_UNSUPPORTED;
+  if (bnk && extent_elems(d->N + 256, d->K + slot_k, d->ldb) * ae > kMaxExtent) return GE_ERR_UNSUPPORTED;
   if (extent_elems(d->M + 256, d->N, d->ldy) * esize > kMaxExtent) return GE_ERR_UNSUPPORTED;
   if (res && extent_elems(d->M + 256, d->N, d->ldr) * 2 > kMaxExtent) return GE_ERR_UNSUPPORTED;
   // grid: one workgroup per 64x64 tile at most
@@ -212,6 +225,7 @@ ge_status_t gemm_epilogue_create(const ge_desc_t* desc, ge_handle_t* out) {
   }
   if (has_op(desc, GE_OP_COL_SUM)) p->flags |= ge::F_COL_SUM;
   if (desc->b_layout == GE_LAYOUT_NK) p->flags |= ge::F_B_NK;
+  if (desc->a_type == GE_DT_FP8_E4M3) p->flags |= ge::F_IN_FP8;
   const ge::TileInfo ti = ge::tile_info(p->tile);
   p->tiles_m = ceil_div(desc->M, ti.bm);
   p->tiles_n = ceil_div(desc->N, ti.bn);
@@ -335,8 +349,9 @@ const char* gemm_epilogue_status_string(ge_status_t s) {
 ge_status_t gemm_epilogue_describe(ge_handle_t h, char* buf, size_t len) {
   if (!h || !buf || len == 0) return GE_ERR_INVALID_ARG;
   const ge::TileInfo ti = ge::tile_info(h->tile);
-  std::snprintf(buf, len, "tile=%dx%dx64 pair=%d b=%s threads=%d lds=%d grid=%lld act=%d fp8=%d flags=0x%x",
-                ti.bm, ti.bn, ti.pair ? 1 : 0, (h->flags & ge::F_B_NK) ? "NK" : "KN", ti.threads, ti.lds_bytes,
+  std::snprintf(buf, len, "tile=%dx%dx64 pair=%d in=%s b=%s threads=%d lds=%d grid=%lld act=%d fp8=%d flags=0x%x",
+                ti.bm, ti.bn, ti.pair ? 1 : 0, (h->flags & ge::F_IN_FP8) ? "fp8" : "bf16",
+                (h->flags & ge::F_B_NK) ? "NK" : "KN", ti.threads, ti.lds_bytes,
                 (long long)(h->tiles_m * h->tiles_n * h->desc.batch), h->act, h->fp8_out ? 1 : 0,
                 (unsigned)h->flags);
   return GE_OK;

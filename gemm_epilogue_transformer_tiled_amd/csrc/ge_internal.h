@@ -17,6 +17,7 @@ enum : uint32_t {
   F_B_NK = 1u << 6,      // B and B2 given as [batch][N][K] (K contiguous)
   F_ACT_GRAD = 1u << 7,  // y = t * act'(Z) instead of act(t)
   F_COL_SUM = 1u << 8,   // column sums of y over rows and batches
+  F_IN_FP8 = 1u << 9,    // A and B hold fp8-e4m3 codes (B given [N][K])
 };
 
 enum Act : int { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_TANH = 2, ACT_SILU = 3 };
@@ -32,7 +33,7 @@ enum TileKind : int {
 };
 
 struct Params {
-  const uint16_t* A;
+  const uint16_t* A;       // bf16 elements, or fp8 codes (bytes) with F_IN_FP8
   const uint16_t* B;
   const uint16_t* B2;
   const uint16_t* bias;
@@ -78,6 +79,12 @@ TileInfo tile_info_64x64();
 hipError_t launch_tile_128x128_pair_kn(int act, bool fp8_out, const Params& p, hipStream_t stream);
 hipError_t launch_tile_128x128_pair_nk(int act, bool fp8_out, const Params& p, hipStream_t stream);
 TileInfo tile_info_128x128_pair();
+// fp8-e4m3 operands, B laid out [N][K]
+hipError_t launch_tile_256x256_f8(int act, bool fp8_out, const Params& p, hipStream_t stream);
+hipError_t launch_tile_256x128_pair_f8(int act, bool fp8_out, const Params& p, hipStream_t stream);
+hipError_t launch_tile_128x128_f8(int act, bool fp8_out, const Params& p, hipStream_t stream);
+hipError_t launch_tile_64x64_f8(int act, bool fp8_out, const Params& p, hipStream_t stream);
+hipError_t launch_tile_128x128_pair_f8(int act, bool fp8_out, const Params& p, hipStream_t stream);
 
 // Enqueues the fused kernel.  `act` in Act, `fp8_out` selects the E4M3 writer.
 hipError_t launch_fused(TileKind kind, int act, bool fp8_out, const Params& p, hipStream_t stream);

@@ -219,14 +219,42 @@ __device__ __forceinline__ void sched_group() {
   }
 }
 
-// KMASK: K is not a multiple of 64, so one A slot straddles K and needs per-lane masking.
+// The same for the fp8 mainloop, whose fragment reads outnumber its MFMAs: after MFMA m come
+// ceil(NL / MF) loads and ceil(RD / MF) fragment reads while any remain.
+template <int MF, int NL, int RD, int M = 0>
+__device__ __forceinline__ void sched_group8() {
+  if constexpr (M < MF) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int per = (NL + MF - 1) / MF;
+    constexpr int left = NL - M * per;
+    constexpr int n = left < per ? left : per;
+    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x010, n, 0);
+    constexpr int rper = (RD + MF - 1) / MF;
+    constexpr int rleft = RD - M * rper;
+    constexpr int rn = rleft < rper ? rleft : rper;
+    if constexpr (rn > 0) __builtin_amdgcn_sched_group_barrier(0x100, rn, 0);
+    sched_group8<MF, NL, RD, M + 1>();
+  }
+}
+
+// KMASK: K is not a multiple of two steps (64 bf16 or 128 fp8 values), so one A slot straddles
+// K and needs per-lane masking.
 // BNK: B (and B2) are given as [N][K] (K contiguous) -- for instance W when the product is
 // dY @ W^T of a backward pass -- and are staged exactly like A: two steps at a time as
 // [BN][64] with 128-byte rows, fragments by plain 16-byte LDS reads.
 // GRAD: the activation-gradient epilogue y = t * act'(Z) replaces y = act(t) (non-pairwise).
-template <class T, int ACT, bool GRAD, bool FP8, bool ROWSTAT, bool KMASK, bool BNK>
+// F8IN: A and B hold OCP fp8-e4m3 codes (B given [N][K]); the mainloop runs
+// v_mfma_f32_32x32x64_f8f6f4, K advancing 64 values (64 bytes) per step, so the same LDS
+// slots of 128-byte rows hold two steps and every byte offset is what it is for bf16.  The
+// dequantisation factors of delayed scaling (1 / (scale_A * scale_B)) are the epilogue's
+// alpha; everything after the accumulator is shared with the bf16 path.
+template <class T, int ACT, bool GRAD, bool FP8, bool ROWSTAT, bool KMASK, bool BNK, bool F8IN = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(T::WPE, T::WPE)))
 void fused_gemm_epilogue(Params p) {
+  constexpr int ES = F8IN ? 1 : 2;                // bytes per operand element
+  constexpr int BKE = F8IN ? 64 : T::BK;          // K values per step (64 bytes of a row)
+  constexpr uint32_t EPC = 16 / ES;               // K values per 16-byte chunk
+  static_assert(!F8IN || (BNK && !ROWSTAT && !GRAD), "fp8 operands: B given [N][K], no row statistic");
   // The LDS stages and slots are distinct arrays, so the compiler can tell that the direct
   // loads filling one never alias the fragment reads of another.
   __shared__ __attribute__((aligned(1024))) unsigned char aslot0[T::A_ALLOC];
@@ -284,13 +312,13 @@ void fused_gemm_epilogue(Params p) {
   // (B) k0 and its extent shrinks by the same amount, so per-lane offsets stay fixed for the
   // whole loop (no vector instructions for addressing).  A step entirely outside [0, K) gets
   // an empty resource, which reads zeros.
-  const uint16_t* a_base = p.A + b * p.sa + (int64_t)m0 * p.lda;
-  const int64_t a_ext = ((int64_t)(M - 1 - m0) * p.lda + K) * 2;
+  const unsigned char* a_base = (const unsigned char*)p.A + (b * p.sa + (int64_t)m0 * p.lda) * ES;
+  const int64_t a_ext = ((int64_t)(M - 1 - m0) * p.lda + K) * ES;
   // [K][N]: the tile's columns start at n0; [N][K]: its rows start at n0 (like A's at m0)
   const int64_t b_ofs = BNK ? (int64_t)n0 * p.ldb : (int64_t)n0;
-  const uint16_t* b_base = p.B + b * p.sb + b_ofs;
-  const uint16_t* b2_base = T::PAIR ? p.B2 + b * p.sb + b_ofs : b_base;
-  const int64_t b_ext = BNK ? ((int64_t)(N - 1 - n0) * p.ldb + K) * 2
+  const unsigned char* b_base = (const unsigned char*)p.B + (b * p.sb + b_ofs) * ES;
+  const unsigned char* b2_base = T::PAIR ? (const unsigned char*)p.B2 + (b * p.sb + b_ofs) * ES : b_base;
+  const int64_t b_ext = BNK ? ((int64_t)(N - 1 - n0) * p.ldb + K) * ES
                             : (K > 0 ? ((int64_t)(K - 1) * p.ldb + (N - n0)) * 2 : 0);
   __amdgpu_buffer_rsrc_t b_rs0 = make_rsrc(b_base, b_ext), b2_rs0 = b_rs0;   // ragged K, [N][K]
   if constexpr (T::PAIR) b2_rs0 = make_rsrc(b2_base, b_ext);
@@ -304,7 +332,7 @@ void fused_gemm_epilogue(Params p) {
   // slot is wholly inside or outside [0, K); otherwise chunks outside [0, K) get the
   // out-of-range offset, per lane, with k0 added to the offset instead of the resource.
   static_assert(T::A_ROWS_PER_LOAD == 8 && T::A_CHUNKS == 8, "one 128-byte row per 8 lanes");
-  const uint32_t lda2 = (uint32_t)p.lda * 2u, ldb2 = (uint32_t)p.ldb * 2u;
+  const uint32_t lda2 = (uint32_t)p.lda * (uint32_t)ES, ldb2 = (uint32_t)p.ldb * (uint32_t)ES;   // row pitch, bytes
   const uint32_t a_x = (uint32_t)((lane & 7) ^ (lane >> 3));
   const uint32_t a_row = (uint32_t)(lane >> 3) * lda2;
   uint32_t a_voff[T::A_LOADS];
@@ -333,16 +361,17 @@ void fused_gemm_epilogue(Params p) {
     }
   }
 
-  // Resources of the step starting at K column/row k0 (a multiple of 32, so a B step -- and,
-  // with K a multiple of 64, an A slot -- is wholly inside or outside [0, K)): the base is
+  // Resources of the step starting at K column/row k0 (a multiple of the step, so a B step --
+  // and, with K a multiple of two steps, an A slot -- is wholly inside or outside [0, K)): the base is
   // clamped into range and an out-of-range step gets extent 0.  Byte offsets fit 32 bits:
   // every extent is checked below 2^31 on the host.  Scalar, branch-free code.
 #define GE_KCLAMP(k0) ((k0) < 0 ? 0 : ((k0) > K ? K : (k0)))
 #define GE_KLIVE(k0) (((k0) >= 0) & ((k0) < K))
-#define GE_A_RS(k0) make_rsrc(a_base + GE_KCLAMP(k0), GE_KLIVE(k0) ? a_ext - 2 * (int64_t)GE_KCLAMP(k0) : 0)
+#define GE_A_RS(k0) \
+  make_rsrc(a_base + (uint32_t)GE_KCLAMP(k0) * (uint32_t)ES, GE_KLIVE(k0) ? a_ext - ES * (int64_t)GE_KCLAMP(k0) : 0)
 #define GE_B_RS(base, k0) \
-  make_rsrc((const unsigned char*)(base) + (uint32_t)GE_KCLAMP(k0) * (BNK ? 2u : ldb2), \
-            GE_KLIVE(k0) ? b_ext - (int64_t)((uint32_t)GE_KCLAMP(k0) * (BNK ? 2u : ldb2)) : 0)
+  make_rsrc((base) + (uint32_t)GE_KCLAMP(k0) * (BNK ? (uint32_t)ES : ldb2), \
+            GE_KLIVE(k0) ? b_ext - (int64_t)((uint32_t)GE_KCLAMP(k0) * (BNK ? (uint32_t)ES : ldb2)) : 0)
 
   // A slot for steps k0/BK and k0/BK + 1; k0 may be negative (leading all-zero steps).
   // K a multiple of 64: `rs` is the step's resource and the offsets are fixed.  Otherwise the
@@ -356,7 +385,7 @@ void fused_gemm_epilogue(Params p) {
       if constexpr (KMASK) {
         const uint32_t u = (uint32_t)(wave * T::A_LOADS + t);          // wave-uniform
         const uint32_t c = a_x ^ (u & 3u);
-        off = ((uint32_t)(k0 + (int)(c * 8u)) < (uint32_t)K) ? off + (uint32_t)k0 * 2u : kOOB;
+        off = ((uint32_t)(k0 + (int)(c * EPC)) < (uint32_t)K) ? off + (uint32_t)k0 * (uint32_t)ES : kOOB;
       }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           ars, (__attribute__((address_space(3))) void*)(slot + (wave * T::A_LOADS + t) * 1024), 16, off, 0, 0, 0);
@@ -372,7 +401,7 @@ void fused_gemm_epilogue(Params p) {
         uint32_t off = b_voff[t];
         if constexpr (KMASK) {
           const uint32_t c = a_x ^ (r & 3u);
-          off = ((uint32_t)(k0 + (int)(c * 8u)) < (uint32_t)K) ? off + (uint32_t)k0 * 2u : kOOB;
+          off = ((uint32_t)(k0 + (int)(c * EPC)) < (uint32_t)K) ? off + (uint32_t)k0 * (uint32_t)ES : kOOB;
         }
         unsigned char* dst = st + op * (T::BN * T::A_ROWB) + r * 1024;
         if (T::PAIR && op == 1)
@@ -526,8 +555,8 @@ void fused_gemm_epilogue(Params p) {
     using Fill = std::integral_constant<int, S + 2>;
     // [K][N]: B every step; [N][K]: B with A, on even steps only
     constexpr int B_NOW = BNK ? (EVEN ? BL : 0) : BL;
-    if constexpr (!BNK || EVEN) issue_b(bstage(Fill{}), (kt + 2) * T::BK);
-    if constexpr (EVEN) issue_a((kt + 2) * T::BK, aslot(Fill{}));
+    if constexpr (!BNK || EVEN) issue_b(bstage(Fill{}), (kt + 2) * BKE);
+    if constexpr (EVEN) issue_a((kt + 2) * BKE, aslot(Fill{}));
     static_assert(T::GROUPS == 2, "two groups per step");
     read_frags(aslot(Cur{}), bstage(Cur{}), S % 2, 1, f1);
     mfmas(f0);
@@ -543,10 +572,94 @@ void fused_gemm_epilogue(Params p) {
     sched_group<MFMAS_PER_GROUP, 0, READS_PER_GROUP>();
   };
 
+  // ---- fp8 operands (F8IN) ----
+  // One v_mfma_f32_32x32x64_f8f6f4 per 32x32 block and step takes 32 bytes per lane from each
+  // operand.  A dot product does not depend on which K position a (lane half, byte) pair
+  // stands for, as long as both operands use the same assignment, so each lane reads the two
+  // 16-byte chunks that the bf16 path reads for its two 16-deep groups (chunks 4h + lhalf and
+  // 4h + 2 + lhalf of the slot row): the same conflict-free LDS pattern.  The step's MFMAs are
+  // split into two halves over the B fragments (operand, column block): the first half runs
+  // before the barrier while the rest of this step's B fragments are read, the second half
+  // after it while the next step's A fragments and first B fragments are read.  A fragments
+  // alternate between two register sets by step parity.
+  typedef int i32x4_t __attribute__((ext_vector_type(4)));
+  typedef int i32x8_t __attribute__((ext_vector_type(8)));
+  constexpr int NQ = T::NB * T::FN;                    // B fragments per step
+  constexpr int NQ0 = NQ / 2;                          // consumed before the barrier
+  i32x8_t fa8[2][F8IN ? T::FM : 1];
+  i32x8_t fb8[F8IN ? NQ : 1];
+  auto frag8 = [&](const unsigned char* base, int h) -> i32x8_t {
+    const i32x4_t lo = *(const i32x4_t*)(base + a_frag[2 * h]);
+    const i32x4_t hi = *(const i32x4_t*)(base + a_frag[2 * h + 1]);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto read_a8 = [&](const unsigned char* as, int h, i32x8_t* fa) {
+#pragma unroll
+    for (int j = 0; j < T::FM; ++j) fa[j] = frag8(as + j * 32 * T::A_ROWB, h);
+  };
+  // B rows start at wn0 + 32i of operand op; bnk_frag equals a_frag shifted by wn0 - wm0 rows
+  auto read_b8 = [&](const unsigned char* bs, int h, auto q0_c, auto q1_c) {
+    constexpr int Q0 = decltype(q0_c)::value, Q1 = decltype(q1_c)::value;
+#pragma unroll
+    for (int q = Q0; q < Q1; ++q) {
+      const int op = q / T::FN, i = q % T::FN;
+      const unsigned char* base = bs + op * T::BN * T::A_ROWB + i * 32 * T::A_ROWB;
+      const i32x4_t lo = *(const i32x4_t*)(base + bnk_frag[2 * h]);
+      const i32x4_t hi = *(const i32x4_t*)(base + bnk_frag[2 * h + 1]);
+      fb8[q] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+  auto mfma8 = [&](const i32x8_t* fa, auto q0_c, auto q1_c) {
+    constexpr int Q0 = decltype(q0_c)::value, Q1 = decltype(q1_c)::value;
+#pragma unroll
+    for (int q = Q0; q < Q1; ++q) {
+      const int op = q / T::FN, i = q % T::FN;
+#pragma unroll
+      for (int j = 0; j < T::FM; ++j) {
+        // format 0 = fp8 e4m3 for both sources; zero scale operands select the unscaled form
+        if (!T::PAIR || op == 0) {
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb8[q], fa[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+        } else {
+          constexpr int P = T::PAIR ? 1 : 0;      // acc2 is [1][1] without the pairwise op
+          acc2[P * i][P * j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb8[q], fa[j], acc2[P * i][P * j],
+                                                                                0, 0, 0, 0, 0, 0);
+        }
+      }
+    }
+  };
+  using Q0c = std::integral_constant<int, 0>;
+  using QHc = std::integral_constant<int, NQ0>;
+  using QNc = std::integral_constant<int, NQ>;
+  // One fp8 step; the loads, waits and barrier are those of k_step ([N][K] B).
+  auto k_step8 = [&](auto s_c, int kt) {
+    constexpr int S = decltype(s_c)::value;
+    constexpr bool EVEN = S % 2 == 0;
+    using Cur = std::integral_constant<int, S>;
+    using Next = std::integral_constant<int, S + 1>;
+    using Fill = std::integral_constant<int, S + 2>;
+    constexpr int B_NOW = EVEN ? BL : 0;
+    if constexpr (EVEN) {
+      issue_b(bstage(Fill{}), (kt + 2) * BKE);
+      issue_a((kt + 2) * BKE, aslot(Fill{}));
+    }
+    read_b8(bstage(Cur{}), S % 2, QHc{}, QNc{});
+    mfma8(fa8[S % 2], Q0c{}, QHc{});
+    sched_group8<T::FM * NQ0, EVEN ? T::A_LOADS + B_NOW : 0, 2 * (NQ - NQ0)>();
+    if constexpr (EVEN)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(T::A_LOADS + B_NOW));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(B_NOW));
+    __builtin_amdgcn_s_barrier();
+    read_a8(aslot(Next{}), (S + 1) % 2, fa8[(S + 1) % 2]);
+    read_b8(bstage(Next{}), (S + 1) % 2, Q0c{}, QHc{});
+    mfma8(fa8[S % 2], QHc{}, QNc{});
+    sched_group8<T::FM * (NQ - NQ0), 0, 2 * (T::FM + NQ0)>();
+  };
+
   // Step count rounded up to a multiple of NS with leading all-zero steps, so the loop
   // always runs whole stage rings, A slots pair steps (0,1) and (2,3) of each ring, and the
   // accumulators have one exit path.
-  const int nk = (K + T::BK - 1) / T::BK;
+  const int nk = (K + BKE - 1) / BKE;
   const int nsteps = (nk + T::NS - 1) / T::NS * T::NS;
   int kt = nk - nsteps;
   // [N][K] B follows A: slot resources at the slot's first step, fixed ones for ragged K
@@ -561,26 +674,35 @@ void fused_gemm_epilogue(Params p) {
       if constexpr (T::PAIR) b2rs = GE_B_RS(b2_base, BNK ? (ka) : (kb));       \
     }                                                                          \
   } while (0)
-  GE_SET_RS(kt * T::BK, kt * T::BK);
-  issue_a(kt * T::BK, aslot(S0{}));
-  issue_b(bstage(S0{}), kt * T::BK);
+  GE_SET_RS(kt * BKE, kt * BKE);
+  issue_a(kt * BKE, aslot(S0{}));
+  issue_b(bstage(S0{}), kt * BKE);
   if constexpr (!BNK) {
-    GE_SET_RS(kt * T::BK, (kt + 1) * T::BK);
-    issue_b(bstage(S1{}), (kt + 1) * T::BK);
+    GE_SET_RS(kt * BKE, (kt + 1) * BKE);
+    issue_b(bstage(S1{}), (kt + 1) * BKE);
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(BNK ? 0 : T::B_LOADS));
   __builtin_amdgcn_s_barrier();
-  read_frags(aslot(S0{}), bstage(S0{}), 0, 0, f0);
+  if constexpr (F8IN) {
+    read_a8(aslot(S0{}), 0, fa8[0]);
+    read_b8(bstage(S0{}), 0, Q0c{}, QHc{});
+  } else {
+    read_frags(aslot(S0{}), bstage(S0{}), 0, 0, f0);
+  }
+  auto step = [&](auto s_c, int k) {
+    if constexpr (F8IN) k_step8(s_c, k);
+    else k_step(s_c, k);
+  };
   for (; kt < nk; kt += T::NS) {
     // each step fills the stages of step + 2 (A: on even steps, the slot of steps + 2, + 3)
-    GE_SET_RS((kt + 2) * T::BK, (kt + 2) * T::BK);
-    k_step(S0{}, kt);
-    GE_SET_RS((kt + 2) * T::BK, (kt + 3) * T::BK);
-    k_step(S1{}, kt + 1);
-    GE_SET_RS((kt + 4) * T::BK, (kt + 4) * T::BK);
-    k_step(S2{}, kt + 2);
-    GE_SET_RS((kt + 4) * T::BK, (kt + 5) * T::BK);
-    k_step(S3{}, kt + 3);
+    GE_SET_RS((kt + 2) * BKE, (kt + 2) * BKE);
+    step(S0{}, kt);
+    GE_SET_RS((kt + 2) * BKE, (kt + 3) * BKE);
+    step(S1{}, kt + 1);
+    GE_SET_RS((kt + 4) * BKE, (kt + 4) * BKE);
+    step(S2{}, kt + 2);
+    GE_SET_RS((kt + 4) * BKE, (kt + 5) * BKE);
+    step(S3{}, kt + 3);
   }
 #undef GE_SET_RS
 #undef GE_B_RS
@@ -911,6 +1033,34 @@ hipError_t launch_t(const Params& p, hipStream_t s) {
     launch_k<T, ACT, false, FP8, false, BNK>(p, s, (unsigned)grid);
   }
   return hipGetLastError();
+}
+
+// fp8 operands (B given [N][K]): forward epilogues only, no in-kernel row statistic (checked
+// on the host).  One A slot holds 128 K values, so K % 128 decides the per-lane masking.
+template <class T, int ACT, bool FP8>
+hipError_t launch_t8(const Params& p, hipStream_t s) {
+  const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * p.batch;
+  if (grid <= 0) return hipSuccess;
+  if (p.flags & (F_ACT_GRAD | F_ROW_RMS)) return hipErrorInvalidValue;
+  if (p.K % 128 != 0)
+    hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, false, FP8, false, true, true, true>), dim3((unsigned)grid),
+                       dim3(T::NT), 0, s, p);
+  else
+    hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, false, FP8, false, false, true, true>), dim3((unsigned)grid),
+                       dim3(T::NT), 0, s, p);
+  return hipGetLastError();
+}
+
+template <class T>
+hipError_t launch_tile_f8(int act, bool fp8, const Params& p, hipStream_t s) {
+  switch (act) {
+    case ACT_NONE: return fp8 ? launch_t8<T, ACT_NONE, true>(p, s) : launch_t8<T, ACT_NONE, false>(p, s);
+    case ACT_RELU: return fp8 ? launch_t8<T, ACT_RELU, true>(p, s) : launch_t8<T, ACT_RELU, false>(p, s);
+    case ACT_GELU_TANH:
+      return fp8 ? launch_t8<T, ACT_GELU_TANH, true>(p, s) : launch_t8<T, ACT_GELU_TANH, false>(p, s);
+    case ACT_SILU: return fp8 ? launch_t8<T, ACT_SILU, true>(p, s) : launch_t8<T, ACT_SILU, false>(p, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // The instances of one tile shape and one B layout (one translation unit each).

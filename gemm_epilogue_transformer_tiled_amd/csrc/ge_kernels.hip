@@ -30,6 +30,16 @@ TileInfo tile_info(TileKind kind) {
 }
 
 hipError_t launch_fused(TileKind kind, int act, bool fp8_out, const Params& p, hipStream_t stream) {
+  if (p.flags & F_IN_FP8) {
+    switch (kind) {
+      case TILE_256x256: return launch_tile_256x256_f8(act, fp8_out, p, stream);
+      case TILE_256x128_PAIR: return launch_tile_256x128_pair_f8(act, fp8_out, p, stream);
+      case TILE_128x128: return launch_tile_128x128_f8(act, fp8_out, p, stream);
+      case TILE_64x64: return launch_tile_64x64_f8(act, fp8_out, p, stream);
+      case TILE_128x128_PAIR: return launch_tile_128x128_pair_f8(act, fp8_out, p, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (kind) {
     case TILE_256x256: return (p.flags & F_B_NK) ? launch_tile_256x256_nk(act, fp8_out, p, stream)
                                      : launch_tile_256x256_kn(act, fp8_out, p, stream);

@@ -1,0 +1,10 @@
+// Instances of the fused kernel for the 128x128 tile with fp8-e4m3 operands (B laid out [N][K]).
+#include "ge_kernel_impl.h"
+
+namespace ge {
+
+hipError_t launch_tile_128x128_f8(int act, bool fp8_out, const Params& p, hipStream_t stream) {
+  return launch_tile_f8<T128>(act, fp8_out, p, stream);
+}
+
+}  // namespace ge

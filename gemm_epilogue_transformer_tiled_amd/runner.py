@@ -21,6 +21,13 @@ def to_device_bf16(bits: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
 
 
+def to_device(bits: np.ndarray, device) -> torch.Tensor:
+    """uint16 bf16 bits -> torch.bfloat16; uint8 e4m3 codes -> torch.uint8 (same bytes)."""
+    if bits.dtype == np.uint8:
+        return torch.from_numpy(np.ascontiguousarray(bits)).to(device)
+    return to_device_bf16(bits, device)
+
+
 @dataclasses.dataclass
 class DeviceProblem:
     workload: object
@@ -49,7 +56,7 @@ class DeviceProblem:
 
 def prepare(w, inputs: Dict[str, np.ndarray], device="cuda", y_fill: Optional[int] = None) -> DeviceProblem:
     """Uploads inputs, allocates Y (and AMAX), creates the plan for workload ``w``."""
-    t = {k: to_device_bf16(v, device) for k, v in inputs.items()
+    t = {k: to_device(v, device) for k, v in inputs.items()
          if k in ("A", "B", "B2", "bias", "R", "Z")}
     if "row_scale" in inputs:
         t["row_scale"] = torch.from_numpy(np.ascontiguousarray(inputs["row_scale"], dtype=np.float32)).to(device)
@@ -63,8 +70,9 @@ def prepare(w, inputs: Dict[str, np.ndarray], device="cuda", y_fill: Optional[in
         Y.view(torch.uint8).fill_(y_fill)
     amax = torch.full((1,), -1.0, dtype=torch.float32, device=device) if w.has("amax") else None
     col = torch.full((w.N,), float("nan"), dtype=torch.float32, device=device) if w.has("col_sum") else None
+    in_t = GE_DT_FP8_E4M3 if getattr(w, "in_dtype", "bf16") == "fp8_e4m3" else GE_DT_BF16
     desc = make_desc(w.batch, w.M, w.N, w.K, make_ops(w.chain),
-                     y_type=GE_DT_FP8_E4M3 if fp8 else GE_DT_BF16,
+                     y_type=GE_DT_FP8_E4M3 if fp8 else GE_DT_BF16, a_type=in_t, b_type=in_t,
                      b_layout=GE_LAYOUT_NK if getattr(w, "b_layout", "kn") == "nk" else GE_LAYOUT_KN)
     plan = Plan(desc)
     args = make_args(A=t.get("A"), B=t.get("B"), B2=t.get("B2"), bias=t.get("bias"), residual=t.get("R"),

@@ -26,7 +26,7 @@ from typing import Dict, Optional, Sequence
 import numpy as np
 
 from . import ops
-from .codecs import decode_bf16, encode_bf16
+from .codecs import decode_bf16, decode_e4m3, encode_bf16
 
 
 @dataclasses.dataclass
@@ -38,6 +38,15 @@ class OracleResult:
     col_sum: Optional[np.ndarray] = None   # [N] float64, when the chain has COL_SUM
 
 
+def decode_operand(x: np.ndarray) -> np.ndarray:
+    """GEMM operand bits -> float64, exactly: uint16 arrays are bf16 bit patterns, uint8
+    arrays OCP e4m3 codes (the fp8 operands of delayed scaling; the cuDNN tutorial's
+    batched-matmul paragraph feeds fp8 scaling from AMAX)."""
+    if x.dtype == np.uint8:
+        return decode_e4m3(x)
+    return decode_bf16(x)
+
+
 def run_chain(chain: Sequence[tuple], A: np.ndarray, B: np.ndarray,
               B2: Optional[np.ndarray] = None, bias: Optional[np.ndarray] = None,
               R: Optional[np.ndarray] = None, row_scale_vec: Optional[np.ndarray] = None,
@@ -46,7 +55,7 @@ def run_chain(chain: Sequence[tuple], A: np.ndarray, B: np.ndarray,
               Z: Optional[np.ndarray] = None) -> OracleResult:
     """Evaluate ``chain`` on bf16-bit inputs.
 
-    A: uint16 [batch, M, K]; B, B2: uint16 [batch, K, N], or [batch, N, K] with
+    A: uint16 [batch, M, K] (or uint8 e4m3 codes, then B and B2 too); B, B2: uint16 [batch, K, N], or [batch, N, K] with
     ``b_layout="nk"`` -- then the product is A @ B^T, the backward-pass form dY @ W^T
     (CODA news item, "How CODA works": forward and backward); bias: uint16 [N];
     R, Z: uint16 [batch, M, N] (Z: the saved pre-activation of ACT_GRAD); row_scale_vec:
@@ -64,10 +73,10 @@ def run_chain(chain: Sequence[tuple], A: np.ndarray, B: np.ndarray,
         if row_scale_vec is not None:
             row_scale_vec = np.asarray(row_scale_vec)[:, rows]
     kinds = [op[0] for op in chain]
-    Af = decode_bf16(A)
+    Af = decode_operand(A)
 
     def as_kn(W: np.ndarray) -> np.ndarray:
-        W = decode_bf16(W)
+        W = decode_operand(W)
         return np.swapaxes(W, -1, -2) if b_layout == "nk" else W
 
     acc = ops.gemm(Af, as_kn(B))

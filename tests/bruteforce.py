@@ -24,6 +24,19 @@ def bf16_value(bits: int) -> float:
     return s * (1.0 + m / 128.0) * 2.0 ** (e - 127)
 
 
+def e4m3_value(code: int) -> float:
+    """Value of an OCP e4m3 ("e4m3fn") code from its fields: sign, 4 exponent bits (bias 7),
+    3 mantissa bits; exponent 0 is subnormal (step 2^-9); S.1111.111 is NaN, no infinities."""
+    s = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0:
+        return s * m * 2.0 ** -9
+    if e == 0xF and m == 0x7:
+        return math.nan
+    return s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
 def exact_gemm(A: Sequence[Sequence[float]], B: Sequence[Sequence[float]]) -> List[List[Fraction]]:
     M, K, N = len(A), len(A[0]) if A else 0, len(B[0]) if B else 0
     return [[sum((Fraction(A[m][k]) * Fraction(B[k][n]) for k in range(K)), Fraction(0))

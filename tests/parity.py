@@ -7,6 +7,13 @@
   alone contributes up to 2**-8 = 3.9e-3.
 * fp8 outputs: each code within one step of the oracle's code along the
   monotone order of E4M3 values (+0 and -0 count as the same point).
+* fp8 outputs of a GEMM with fp8 operands: the matrix core's fp8 instruction
+  sums its 64 products less exactly than fp32 (measured by cancellation:
+  worst |error| 4.7e-6 * sum_k |a_k b_k| at K = 1024, 1.3e-6 at K = 8192, about
+  1.5e-4 / sqrt(K) of it), so each code must lie within one step of the codes
+  the oracle's value takes anywhere in y_ref +- L * E, with
+  E = FP8_ACC_REL / sqrt(max(K, 64)) * alpha * sum_k |a_k b_k| (four times the
+  measured worst case) and L >= the activation's largest slope.
 * AMAX: relative error <= 2e-3 against the oracle's max |y| taken before
   rounding.
 * COL_SUM: each column sum within a floored relative error of 2e-3 of the
@@ -62,6 +69,25 @@ def check_fp8(codes: np.ndarray, ref_codes: np.ndarray, what: str = "") -> int:
         raise AssertionError(f"{what}: fp8 code distance {worst} at {idx}: gpu={codes[idx]:#04x} "
                              f"ref={ref_codes[idx]:#04x}; {int((d > 1).sum())} codes off by more than one")
     return worst
+
+
+FP8_ACC_REL = 6e-4      # E / (alpha * sum |a b|) * sqrt(K): 4x the worst measured 1.5e-4
+
+
+def check_fp8_interval(codes: np.ndarray, y_lo: np.ndarray, y_hi: np.ndarray, scale: float,
+                       what: str = "") -> int:
+    """Each code within one step of [e4m3(y_lo * scale), e4m3(y_hi * scale)] (the oracle's
+    encoder, clamped to +-448; e4m3 rounding is monotone, so those are the extreme codes of the
+    interval).  Returns the summed interval widths, in codes."""
+    lo = e4m3_index(oracle.encode_e4m3(np.clip(np.asarray(y_lo) * scale, -448.0, 448.0)))
+    hi = e4m3_index(oracle.encode_e4m3(np.clip(np.asarray(y_hi) * scale, -448.0, 448.0)))
+    g = e4m3_index(codes)
+    bad = (g < lo - 1) | (g > hi + 1)
+    if bad.any():
+        idx = np.unravel_index(int(np.argmax(bad)), bad.shape)
+        raise AssertionError(f"{what}: fp8 code {int(codes[idx]):#04x} at {idx} outside one step of "
+                             f"[{int(lo[idx])}, {int(hi[idx])}] (monotone index); {int(bad.sum())} such codes")
+    return int(np.sum(hi - lo))
 
 
 COLSUM_TOL = 2e-3

@@ -63,8 +63,11 @@ def _desc(**kw):
 def test_validate_accepts_every_workload_chain():
     import workloads
     for w in workloads.WORKLOADS.values():
+        in_t = ge.GE_DT_FP8_E4M3 if w.in_dtype == "fp8_e4m3" else ge.GE_DT_BF16
         d = ge.make_desc(w.batch, w.M, w.N, w.K, ge.make_ops(w.chain),
-                         y_type=ge.GE_DT_FP8_E4M3 if w.out == "fp8_e4m3" else ge.GE_DT_BF16)
+                         y_type=ge.GE_DT_FP8_E4M3 if w.out == "fp8_e4m3" else ge.GE_DT_BF16,
+                         a_type=in_t, b_type=in_t,
+                         b_layout=ge.GE_LAYOUT_NK if w.b_layout == "nk" else ge.GE_LAYOUT_KN)
         assert ge.gemm_epilogue_validate(d) == ge.GE_OK, w.name
 
 
@@ -148,3 +151,29 @@ def test_create_without_a_gfx950_device_reports_device_error():
     st = ge.lib.gemm_epilogue_create(ctypes.byref(_desc()), ctypes.byref(h))
     assert st == ge.GE_ERR_DEVICE
     assert not h.value
+
+
+FP8_OPS = dict(a_type=ge.GE_DT_FP8_E4M3, b_type=ge.GE_DT_FP8_E4M3, b_layout=ge.GE_LAYOUT_NK)
+
+
+@pytest.mark.parametrize("kw,chain,want", [
+    (dict(), [("scale",), ("bias",), ("act", "relu"), ("amax",)], ge.GE_OK),
+    (dict(), [("scale",), ("pairwise", "silu")], ge.GE_OK),
+    (dict(b_layout=ge.GE_LAYOUT_KN), [("scale",)], ge.GE_ERR_UNSUPPORTED),     # fp8 B must be [N][K]
+    (dict(b_type=ge.GE_DT_BF16), [("scale",)], ge.GE_ERR_UNSUPPORTED),         # mixed operand types
+    (dict(K=24, lda=32, ldb=32), [("scale",)], ge.GE_ERR_UNSUPPORTED),         # K not a multiple of 16
+    (dict(K=48, lda=56, ldb=48), [("scale",)], ge.GE_ERR_UNSUPPORTED),         # lda not a multiple of 16
+    (dict(K=48), [("scale",)], ge.GE_OK),
+    (dict(), [("row_rms", 1e-6)], ge.GE_ERR_UNSUPPORTED),                      # no in-kernel row statistic
+    (dict(), [("act_grad", "gelu_tanh")], ge.GE_ERR_UNSUPPORTED),
+    (dict(a_type=7, b_type=7), [("scale",)], ge.GE_ERR_INVALID_ARG),           # unknown dtype
+    # extents count bytes: an A of just under 2 GiB fits as fp8 and not as bf16
+    (dict(M=(1 << 19) - 4096, K=4096), [("scale",)], ge.GE_OK),
+    (dict(M=(1 << 19) - 4096, K=4096, a_type=ge.GE_DT_BF16, b_type=ge.GE_DT_BF16), [("scale",)],
+     ge.GE_ERR_UNSUPPORTED),
+    (dict(M=1 << 19, K=4096), [("scale",)], ge.GE_ERR_UNSUPPORTED),
+])
+def test_validate_fp8_operands(kw, chain, want):
+    args = dict(batch=1, M=64, N=64, K=64, ops=ge.make_ops(chain), **FP8_OPS)
+    args.update(kw)
+    assert ge.gemm_epilogue_validate(ge.make_desc(**args)) == want

@@ -17,7 +17,7 @@ import oracle
 import workloads
 from oracle import chain as oracle_chain
 from oracle import ops
-from tests.bruteforce import run_chain_scalar
+from tests.bruteforce import e4m3_value, run_chain_scalar
 
 TINY = dict(batch=2, M=3, N=5, K=16)
 
@@ -30,7 +30,11 @@ def _tiny(name, **kw):
 
 
 def _as_lists(inp, key):
-    return oracle.decode_bf16(inp[key]).tolist() if key in inp else None
+    if key not in inp:
+        return None
+    if inp[key].dtype == np.uint8:          # fp8 operands: decoded from the code fields
+        return np.vectorize(e4m3_value, otypes=[np.float64])(inp[key]).tolist()
+    return oracle.decode_bf16(inp[key]).tolist()
 
 
 def _check_against_bruteforce(w, inp):
@@ -205,3 +209,56 @@ def test_backward_chains_match_bruteforce(chain, layout):
     inp = workloads.generate(w)
     assert ("Z" in inp) == w.has("act_grad")
     _check_against_bruteforce(w, inp)
+
+
+# ---- fp8 operands (delayed scaling) ----
+
+FP8_TINY = dict(batch=2, M=3, N=5, K=32)
+
+
+@pytest.mark.parametrize("out", ["fp8_e4m3", "bf16"])
+def test_fp8_operands_match_bruteforce(out):
+    """e4m3 operand codes decoded from their fields by the brute force; the chain of the
+    fp8-operand workload (alpha dequantises, then bias, GELU, AMAX, output)."""
+    w = dataclasses.replace(workloads.WORKLOADS["f3"], out=out,
+                            chain=tuple(op for op in workloads.WORKLOADS["f3"].chain
+                                        if out == "fp8_e4m3" or op[0] != "quant_fp8")).with_shape(**FP8_TINY)
+    inp = workloads.generate(w)
+    assert inp["A"].dtype == np.uint8 and inp["B"].dtype == np.uint8
+    assert inp["B"].shape == (w.batch, w.N, w.K)
+    _check_against_bruteforce(w, inp)
+
+
+def test_fp8_operands_pairwise_and_residual_match_bruteforce():
+    base = workloads.WORKLOADS["f3"]
+    for chain in ((("scale",), ("pairwise", "silu")), (("scale",), ("act", "relu"), ("residual",), ("amax",))):
+        w = dataclasses.replace(base, chain=chain, out="bf16").with_shape(**FP8_TINY)
+        _check_against_bruteforce(w, workloads.generate(w))
+
+
+def test_fp8_operand_generator_codes():
+    """Codes are finite e4m3 values (no NaN code) and decode to the clamped, scaled draws
+    within half an e4m3 step (relative 2^-4, or the subnormal step 2^-10 absolute)."""
+    w = workloads.WORKLOADS["f3"].with_shape(batch=1, M=64, N=48, K=256)
+    inp = workloads.generate(w)
+    for key, var, qs, shape in (("A", 1.0, w.a_qscale, (1, 64, 256)), ("B", 1.0 / 256, w.b_qscale, (1, 48, 256))):
+        codes = inp[key]
+        assert codes.dtype == np.uint8 and codes.shape == shape
+        assert not np.any((codes & 0x7F) == 0x7F)
+        tid = workloads.T_A if key == "A" else workloads.T_B
+        z = workloads._rng(w.config_id, tid).standard_normal(size=shape, dtype=np.float32)
+        x = np.clip((z * np.float32(math.sqrt(var))).astype(np.float64) * qs, -448, 448)
+        got = np.vectorize(e4m3_value, otypes=[np.float64])(codes)
+        assert np.all(np.abs(got - x) <= np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10) + 1e-12)
+
+
+def test_planted_fp8_operand_misdecode_is_caught(monkeypatch):
+    """Reading fp8 operand codes as if they were the high byte of a bf16 value must fail."""
+    w = dataclasses.replace(workloads.WORKLOADS["f3"], out="bf16",
+                            chain=(("scale",), ("bias",), ("act", "gelu_tanh"), ("amax",))).with_shape(**FP8_TINY)
+    inp = workloads.generate(w)
+    monkeypatch.setattr(oracle_chain, "decode_operand",
+                        lambda x: oracle.decode_bf16(x.astype(np.uint16) << 8) if x.dtype == np.uint8
+                        else oracle.decode_bf16(x))
+    with pytest.raises(AssertionError):
+        _check_against_bruteforce(w, inp)

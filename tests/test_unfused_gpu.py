@@ -32,6 +32,7 @@ SHAPES = {
     "c5": dict(M=512, N=1024, K=512),
     "f1": dict(M=512, N=704, K=512),
     "f2": dict(M=512, N=704, K=512),
+    "f3": dict(M=512, N=1024, K=512),
 }
 
 

@@ -14,6 +14,11 @@ Recipe (one independent stream per tensor):
   normals, multiplied by ``sqrt(v)`` in float32 and cast to bf16 with
   round-to-nearest-even (torch's float32 -> bfloat16 cast).
 
+fp8 operands (``in_dtype="fp8_e4m3"``): the same float32 draws are multiplied by the
+operand's quantisation scale, clamped to +-448 and cast to OCP e4m3 ("e4m3fn") codes with
+round-to-nearest-even (torch's float32 -> float8_e4m3fn cast); the codes are the inputs.
+The dequantisation factor 1 / (scale_A * scale_B) is the workload's alpha.
+
 The RMS workload folds a per-channel gain ``g[k]`` into the weight before
 anything runs: ``W'[k, n] = bf16(g[k] * W[k, n])`` with the product taken in
 float32 (a row scaling over the contraction axis, the only fold for which
@@ -58,6 +63,9 @@ class Workload:
     out: str = "bf16"           # "bf16" or "fp8_e4m3"
     description: str = ""
     b_layout: str = "kn"        # "kn": B stored [K][N]; "nk": B stored [N][K] (product A @ B^T)
+    in_dtype: str = "bf16"      # operand type: "bf16" or "fp8_e4m3" (codes, B stored [N][K])
+    a_qscale: float = 1.0       # fp8 operands: quantisation scales of A and B
+    b_qscale: float = 1.0
 
     @property
     def pairwise(self) -> bool:
@@ -76,12 +84,18 @@ class Workload:
         """2*M*N*K per GEMM, times batch, times two for the pairwise (gate, up) pair."""
         return 2.0 * self.batch * self.M * self.N * self.K * (2 if self.pairwise else 1)
 
+    @property
+    def operand_bytes(self) -> int:
+        """Bytes per A / B element."""
+        return 1 if self.in_dtype == "fp8_e4m3" else 2
+
     def algorithmic_bytes(self) -> int:
         """Each operand read once, the output written once, plus the 4-byte AMAX."""
         b = self.batch
-        nbytes = 2 * b * self.M * self.K + 2 * b * self.K * self.N
+        ob = self.operand_bytes
+        nbytes = ob * b * self.M * self.K + ob * b * self.K * self.N
         if self.pairwise:
-            nbytes += 2 * b * self.K * self.N
+            nbytes += ob * b * self.K * self.N
         if self.has("bias"):
             nbytes += 2 * self.N
         if self.has("residual"):
@@ -155,6 +169,20 @@ WORKLOADS["f2"] = Workload(
     description="MLP backward: dZ1 = (dY@W2^T)*GELU'(Z1), db1 = colsum(dZ1); dY[8192x4096] N(0,1), "
                 "W2 stored [11008x4096] N(0,1/4096), Z1 N(0,1)")
 
+# fp8 operands with delayed scaling (cuDNN tutorial, batched-matmul paragraph: the AMAX of
+# one pass sets the fp8 scale of the next): the large fp8-output GEMM of c5 fed with fp8
+# operands, X ~ N(0, 1) quantised with the scale 448/4 = 112 that c5's output uses, W ~
+# N(0, 1/K) stored [N][K] and quantised with 4096; alpha = 1/(112*4096) dequantises the
+# accumulator, then bias, GELU-tanh, AMAX and the fp8 output with scale 112.
+WORKLOADS["f3"] = Workload(
+    name="f3", config_id=8, batch=1, M=8192, N=8192, K=8192,
+    chain=(("scale",), ("bias",), ("act", "gelu_tanh"), ("amax",), ("quant_fp8",)),
+    alpha=1.0 / (112.0 * 4096.0), quant_scale=448.0 / 4.0, bias_var=0.1, out="fp8_e4m3",
+    a_var="1", b_var="1/K", b_layout="nk", in_dtype="fp8_e4m3", a_qscale=112.0, b_qscale=4096.0,
+    description="fp8 operands: X[8192x8192] N(0,1) as e4m3 with scale 112, W stored [8192x8192] "
+                "N(0,1/8192) as e4m3 with scale 4096; alpha=1/(112*4096), bias N(0,0.1), GELU_tanh, "
+                "fp8 e4m3 output with scale 112 and fp32 AMAX")
+
 CONFIG_ORDER: List[str] = ["c1", "c2", "c3", "c4", "c5"]
 
 
@@ -168,6 +196,21 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def f32_to_e4m3_codes(x: np.ndarray, qscale: float) -> np.ndarray:
+    """OCP e4m3 codes of clamp(x * qscale, -448, 448), round-to-nearest-even (torch's
+    float32 -> float8_e4m3fn cast; the clamp keeps the cast away from its NaN overflow)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)) * float(qscale)
+    return t.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _normal_e4m3(config_id: int, tensor_id: int, shape, var: float, qscale: float) -> np.ndarray:
+    z = _rng(config_id, tensor_id).standard_normal(size=shape, dtype=np.float32)
+    z *= np.float32(math.sqrt(var))
+    return f32_to_e4m3_codes(z, qscale)
 
 
 def _fold(w_bits: np.ndarray, g: np.ndarray, layout: str = "kn") -> np.ndarray:
@@ -190,7 +233,7 @@ def _var(spec: str, K: int) -> float:
 def generate(w: Workload, sensitive: bool = False, seed_offset: int = 0) -> Dict[str, np.ndarray]:
     """Seeded inputs for workload ``w``.
 
-    Returns bf16 tensors as uint16 bit arrays (A: [batch, M, K]; B, B2:
+    Returns bf16 tensors as uint16 bit arrays, fp8 operands as uint8 e4m3 codes (A: [batch, M, K]; B, B2:
     [batch, K, N], or [batch, N, K] for b_layout "nk"; bias: [N]; R: [batch, M, N]) and float32 arrays for the
     gain ``g`` (RMS workload only).  ``sensitive=True`` draws A from N(0, 1)
     and sets the bias to zero, so the GEMM term dominates the output.
@@ -203,6 +246,18 @@ def generate(w: Workload, sensitive: bool = False, seed_offset: int = 0) -> Dict
     bshape = (b, K, N) if lay == "kn" else (b, N, K)
     out: Dict[str, np.ndarray] = {}
     a_var = 1.0 if sensitive else _var(w.a_var, K)
+    if w.in_dtype == "fp8_e4m3":
+        # fp8 operands: uint8 codes; no gain fold, no pairwise (not defined for these workloads)
+        out["A"] = _normal_e4m3(cid, T_A, (b, M, K), a_var, w.a_qscale)
+        out["B"] = _normal_e4m3(cid, T_B, bshape, _var(w.b_var, K), w.b_qscale)
+        if w.pairwise:
+            out["B2"] = _normal_e4m3(cid, T_B2, bshape, _var(w.b_var, K), w.b_qscale)
+        if w.has("bias"):
+            out["bias"] = (np.zeros(N, dtype=np.uint16) if sensitive
+                           else _normal_bf16(cid, T_BIAS, (N,), w.bias_var))
+        if w.has("residual"):
+            out["R"] = _normal_bf16(cid, T_R, (b, M, N), 1.0)
+        return out
     out["A"] = _normal_bf16(cid, T_A, (b, M, K), a_var)
     g = None
     if w.has("row_rms"):
