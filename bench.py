@@ -45,9 +45,9 @@ METRIC = "fused GEMM-epilogue TFLOP/s (% of MI355X bf16 MFMA peak) per config"
 # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE (x2.0) + WRITE_SIZE (x1.0) of the fused
 # kernel at each workload; the factors scale the counters to the bytes of a plain 1 GiB device
 # copy.  Valid only for the kernel source they were taken on (sha256 prefix below).
-MEASURED_TRAFFIC_SOURCE = "c3cc0fce483d0c9a"
-MEASURED_TRAFFIC = {"c1": 1062063, "c2": 101278629, "c3": 2717362921, "c4": 537505063, "c5": 1870328884,
-                    "f1": 3316143244, "f2": 1806596797}
+MEASURED_TRAFFIC_SOURCE = "aec1b252370a36bd"
+MEASURED_TRAFFIC = {"c1": 1068230, "c2": 101242441, "c3": 2545613168, "c4": 537517353, "c5": 1925895337,
+                    "f1": 3171490838, "f2": 1807169248, "f3": 875357753}
 
 
 def kernel_source_hash():
