@@ -22,6 +22,10 @@
  *     superoptimizer write-up, section 7 (SwiGLU).
  *   - The per-row RMS scale 1/sqrt(mean(x^2) + eps) applied after the GEMM via
  *     (X*S)@W == (X@W)*S: superoptimizer write-up, section 9 (RMSNorm).
+ *   - fp8 operands with delayed scaling: the AMAX of one pass sets the fp8 scale
+ *     of the next (cuDNN tutorial, batched-matmul paragraph); a GEMM that
+ *     consumes such fp8 tensors multiplies their e4m3 codes and dequantises the
+ *     accumulator with alpha = 1 / (scale_A * scale_B).
  *
  * Layout (all row-major, leading dimensions and batch strides in ELEMENTS):
  *   A  [batch][M][K] bf16, element (b,m,k) at A + b*stride_a + m*lda + k
@@ -39,6 +43,11 @@
  *   row_scale [batch][M] fp32, at row_scale + b*M + m
  *   amax: one fp32 in device memory
  *   A batch stride of 0 broadcasts that operand over the batch.
+ *   fp8 operands: a_type == b_type == GE_DT_FP8_E4M3 makes A, B (and B2) one-byte OCP e4m3
+ *   ("e4m3fn") codes in the same element layout; B must then be GE_LAYOUT_NK, K, lda, ldb
+ *   and the A/B batch strides multiples of 16, and ROW_RMS and ACT_GRAD are unsupported.
+ *   The products are summed by the fp8 matrix-core instruction into fp32 accumulators
+ *   (its own summation of each 64 products is less exact than fp32).
  *
  * Epilogue chain (descriptor order must be this canonical order; each op at
  * most once):
@@ -130,7 +139,8 @@ typedef struct {
   int64_t batch, M, N, K;
   int64_t lda, ldb, ldy, ldr;                   /* leading dimensions, elements */
   int64_t stride_a, stride_b, stride_y, stride_r; /* batch strides, elements (0 = broadcast) */
-  int32_t a_type, b_type, y_type;               /* ge_dtype_t: bf16, bf16, bf16 | fp8_e4m3 */
+  int32_t a_type, b_type, y_type;               /* ge_dtype_t: A and B both bf16 or both fp8_e4m3;
+                                                   Y bf16 | fp8_e4m3 */
   int32_t n_ops;
   ge_op_t ops[GE_MAX_OPS];
   int32_t b_layout;                             /* ge_layout_t of B and B2 (0 = [K][N]) */

@@ -25,8 +25,8 @@ Sources (pages as titled):
     scalar alpha, bias, activation, AMAX on the result feeding fp8 scaling).
 
 Every function is pinned by ``tests/test_oracle_*.py`` (brute force on tiny
-inputs, closed forms, invariants, library special cases).  Parity pinned for
-all functions here; see the design doc's oracle table.
+inputs, closed forms, invariants, library special cases); no function here is
+left unpinned.
 """
 from .codecs import (  # noqa: F401
     BF16_MAX, E4M3_MAX, decode_bf16, decode_e4m3, encode_bf16, encode_e4m3,
