@@ -73,6 +73,12 @@ def parse():
     ap.add_argument("--launch", default="auto", choices=["auto", "eager", "graph"],
                     help="issue the timed steps eagerly or as one HIP-graph replay (auto: the faster on a probe)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle timing sample")
+    ap.add_argument("--tile-cache", default=None, metavar="JSON",
+                    help="tile-config cache: plan the workload with the instance it holds (and, with --tune, "
+                         "record the sweep there)")
+    ap.add_argument("--tune", action="store_true",
+                    help="time every admissible kernel instance on the workload first (untimed), then run "
+                         "the fastest")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bare", action="store_true", help="skip the bare-GEMM comparison")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache single-launch timing")
@@ -241,7 +247,20 @@ def main():
         sys.exit(1)
     w = workloads.WORKLOADS[args.config]
     inputs = workloads.generate(w)
-    prob = runner.prepare(w, inputs)
+    from gemm_epilogue_transformer_tiled_amd import tuning
+
+    cache = tuning.TileCache.load(args.tile_cache) if args.tile_cache else None
+    prob = runner.prepare(w, inputs, cache=cache)
+    tuned = None
+    if args.tune:
+        default_kernel = prob.plan.describe()
+        cache = cache or tuning.TileCache(path="")
+        best, timings = runner.tune(prob, cache, steps=min(args.steps, 20))
+        if args.tile_cache:
+            cache.save()
+        prob = prob.with_tile(best)
+        tuned = {"ms_per_launch": {str(t): round(v, 6) for t, v in timings.items()}, "chosen": best,
+                 "default_kernel": default_kernel}
     ms_step, mode, probe = time_launches(prob, args.steps, args.warmup, args.launch)
     flops = w.flops()
     value = flops / (ms_step * 1e-3) / 1e12
@@ -272,6 +291,7 @@ def main():
             "kernel": prob.plan.describe(),
         },
         "launch": {"mode": mode, "probe_ms_per_step": probe},
+        "tile_sweep": tuned,
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 3),

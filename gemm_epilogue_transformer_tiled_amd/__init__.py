@@ -20,6 +20,7 @@ GE_OK, GE_ERR_INVALID_ARG, GE_ERR_UNSUPPORTED, GE_ERR_DEVICE, GE_ERR_HIP = range
 GE_DT_BF16, GE_DT_FP8_E4M3, GE_DT_FP32 = range(3)
 GE_ACT_NONE, GE_ACT_RELU, GE_ACT_GELU_TANH, GE_ACT_SILU = range(4)
 GE_LAYOUT_KN, GE_LAYOUT_NK = range(2)
+GE_TILE_256x256, GE_TILE_256x128_PAIR, GE_TILE_128x128, GE_TILE_64x64, GE_TILE_128x128_PAIR, GE_TILE_COUNT = range(6)
 (GE_OP_SCALE, GE_OP_ROW_RMS, GE_OP_ROW_SCALE, GE_OP_BIAS_COL, GE_OP_ACT, GE_OP_PAIRWISE_ACT_MUL,
  GE_OP_RESIDUAL, GE_OP_AMAX, GE_OP_QUANT_FP8, GE_OP_ACT_GRAD, GE_OP_COL_SUM) = range(11)
 GE_MAX_OPS = 8
@@ -44,9 +45,14 @@ class ge_desc_t(ctypes.Structure):
         ("a_type", ctypes.c_int32), ("b_type", ctypes.c_int32), ("y_type", ctypes.c_int32),
         ("n_ops", ctypes.c_int32),
         ("ops", ge_op_t * GE_MAX_OPS),
-        ("b_layout", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("b_layout", ctypes.c_int32), ("tile", ctypes.c_int32),
         ("ldz", ctypes.c_int64), ("stride_z", ctypes.c_int64),
     ]
+
+
+class ge_tile_info_t(ctypes.Structure):
+    _fields_ = [("bm", ctypes.c_int32), ("bn", ctypes.c_int32), ("pairwise", ctypes.c_int32),
+                ("threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32)]
 
 
 class ge_args_t(ctypes.Structure):
@@ -63,7 +69,7 @@ ge_handle_t = ctypes.c_void_p
 
 EXPORTED = ("gemm_epilogue_validate", "gemm_epilogue_create", "gemm_epilogue_workspace_size",
             "gemm_epilogue_run", "gemm_epilogue_destroy", "gemm_epilogue_status_string",
-            "gemm_epilogue_describe")
+            "gemm_epilogue_describe", "gemm_epilogue_tile_info")
 
 
 def _load() -> ctypes.CDLL:
@@ -91,6 +97,8 @@ def _load() -> ctypes.CDLL:
     lib.gemm_epilogue_status_string.restype = ctypes.c_char_p
     lib.gemm_epilogue_describe.argtypes = [ge_handle_t, ctypes.c_char_p, ctypes.c_size_t]
     lib.gemm_epilogue_describe.restype = ctypes.c_int
+    lib.gemm_epilogue_tile_info.argtypes = [ctypes.c_int32, ctypes.POINTER(ge_tile_info_t)]
+    lib.gemm_epilogue_tile_info.restype = ctypes.c_int
     return lib
 
 
@@ -146,6 +154,14 @@ def gemm_epilogue_describe(handle: int) -> str:
     return buf.value.decode()
 
 
+def gemm_epilogue_tile_info(tile: int) -> ge_tile_info_t:
+    info = ge_tile_info_t()
+    st = lib.gemm_epilogue_tile_info(tile, ctypes.byref(info))
+    if st != GE_OK:
+        raise GemmEpilogueError(st, "gemm_epilogue_tile_info")
+    return info
+
+
 # ---- marshalling helpers ----
 
 def make_ops(chain: Iterable[tuple]) -> Sequence[Tuple[int, int, float]]:
@@ -168,10 +184,12 @@ def make_desc(batch: int, M: int, N: int, K: int, ops: Sequence[Tuple[int, int, 
               stride_b: Optional[int] = None, stride_y: Optional[int] = None,
               stride_r: Optional[int] = None, a_type: int = GE_DT_BF16, b_type: int = GE_DT_BF16,
               b_layout: int = GE_LAYOUT_KN, ldz: Optional[int] = None,
-              stride_z: Optional[int] = None) -> ge_desc_t:
+              stride_z: Optional[int] = None, tile: Optional[int] = None) -> ge_desc_t:
     """Descriptor for packed row-major operands unless leading dims / strides are given.
-    b_layout GE_LAYOUT_NK: B (and B2) are [batch][N][K]."""
+    b_layout GE_LAYOUT_NK: B (and B2) are [batch][N][K].  tile: a ge_tile_t to request that
+    kernel instance (None: create chooses)."""
     d = ge_desc_t()
+    d.tile = 0 if tile is None else tile + 1
     d.batch, d.M, d.N, d.K = batch, M, N, K
     d.b_layout = b_layout
     d.lda = K if lda is None else lda

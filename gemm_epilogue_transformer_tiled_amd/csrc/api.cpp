@@ -29,6 +29,11 @@ struct ge_plan {
 
 namespace {
 
+static_assert(GE_TILE_256x256 == ge::TILE_256x256 && GE_TILE_256x128_PAIR == ge::TILE_256x128_PAIR &&
+                  GE_TILE_128x128 == ge::TILE_128x128 && GE_TILE_64x64 == ge::TILE_64x64 &&
+                  GE_TILE_128x128_PAIR == ge::TILE_128x128_PAIR && GE_TILE_COUNT == ge::TILE_KIND_COUNT,
+              "public tile ids mirror the kernel instances");
+
 constexpr int64_t kMaxExtent = 0x7FFFFFF0;   // buffer extents are 31-bit byte counts
 
 int op_rank(int kind) {
@@ -69,6 +74,7 @@ int64_t extent_elems(int64_t rows, int64_t cols, int64_t ld) {
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 ge::TileKind pick_tile(const ge_desc_t* d, bool pair) {
+  if (d->tile > 0) return (ge::TileKind)(d->tile - 1);        // validated: matches the chain
   const char* force = std::getenv("GE_FORCE_TILE");
   if (force && *force) {
     const int k = std::atoi(force);
@@ -95,7 +101,7 @@ ge_status_t gemm_epilogue_validate(const ge_desc_t* d) {
   if (d->lda < 0 || d->ldb < 0 || d->ldy < 0 || d->ldr < 0) return GE_ERR_INVALID_ARG;
   if (d->stride_a < 0 || d->stride_b < 0 || d->stride_y < 0 || d->stride_r < 0) return GE_ERR_INVALID_ARG;
   if (d->b_layout != GE_LAYOUT_KN && d->b_layout != GE_LAYOUT_NK) return GE_ERR_INVALID_ARG;
-  if (d->reserved != 0) return GE_ERR_INVALID_ARG;
+  if (d->tile < 0 || d->tile > GE_TILE_COUNT) return GE_ERR_INVALID_ARG;
   const bool bnk = d->b_layout == GE_LAYOUT_NK;
 
   // op chain: known kinds, canonical order, each at most once, exclusive pairs
@@ -116,6 +122,8 @@ ge_status_t gemm_epilogue_validate(const ge_desc_t* d) {
   const bool pair = has_op(d, GE_OP_PAIRWISE_ACT_MUL);
   const bool quant = has_op(d, GE_OP_QUANT_FP8);
   if (has_op(d, GE_OP_ROW_RMS) && d->K < 1) return GE_ERR_INVALID_ARG;
+  // a requested instance must be a pairwise one exactly when the chain is pairwise
+  if (d->tile > 0 && ge::tile_info((ge::TileKind)(d->tile - 1)).pair != pair) return GE_ERR_INVALID_ARG;
 
   // dtypes: bf16 operands, or fp8-e4m3 operands with B given [N][K]
   auto known = [](int32_t t) { return t == GE_DT_BF16 || t == GE_DT_FP8_E4M3 || t == GE_DT_FP32; };
@@ -344,6 +352,17 @@ const char* gemm_epilogue_status_string(ge_status_t s) {
     case GE_ERR_HIP: return "GE_ERR_HIP: a HIP call or kernel launch failed";
     default: return "unknown status";
   }
+}
+
+ge_status_t gemm_epilogue_tile_info(int32_t tile, ge_tile_info_t* info) {
+  if (!info || tile < 0 || tile >= GE_TILE_COUNT) return GE_ERR_INVALID_ARG;
+  const ge::TileInfo ti = ge::tile_info((ge::TileKind)tile);
+  info->bm = ti.bm;
+  info->bn = ti.bn;
+  info->pairwise = ti.pair ? 1 : 0;
+  info->threads = ti.threads;
+  info->lds_bytes = ti.lds_bytes;
+  return GE_OK;
 }
 
 ge_status_t gemm_epilogue_describe(ge_handle_t h, char* buf, size_t len) {

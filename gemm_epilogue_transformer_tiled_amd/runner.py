@@ -6,14 +6,15 @@ torch stream.
 """
 from __future__ import annotations
 
+import ctypes
 import dataclasses
-from typing import Dict, Optional
+from typing import Dict, Optional, Tuple
 
 import numpy as np
 import torch
 
-from . import (GE_DT_BF16, GE_DT_FP8_E4M3, GE_LAYOUT_KN, GE_LAYOUT_NK, Plan, make_args, make_desc,
-               make_ops)
+from . import (GE_DT_BF16, GE_DT_FP8_E4M3, GE_LAYOUT_KN, GE_LAYOUT_NK, Plan, ge_args_t, ge_desc_t, make_args,
+               make_desc, make_ops, tuning)
 
 
 def to_device_bf16(bits: np.ndarray, device) -> torch.Tensor:
@@ -53,9 +54,20 @@ class DeviceProblem:
     def col_sum_host(self):
         return None if self.col_sum is None else self.col_sum.cpu().numpy().astype(np.float64)
 
+    def with_tile(self, tile: int) -> "DeviceProblem":
+        """The same problem (same device tensors and outputs) planned on kernel instance `tile`."""
+        desc = ge_desc_t.from_buffer_copy(self.plan.desc)
+        desc.tile = tile + 1
+        args = ge_args_t.from_buffer_copy(self.args)
+        args.workspace, args.workspace_bytes = None, 0        # the new plan brings its own
+        return dataclasses.replace(self, plan=Plan(desc), args=args)
 
-def prepare(w, inputs: Dict[str, np.ndarray], device="cuda", y_fill: Optional[int] = None) -> DeviceProblem:
-    """Uploads inputs, allocates Y (and AMAX), creates the plan for workload ``w``."""
+
+def prepare(w, inputs: Dict[str, np.ndarray], device="cuda", y_fill: Optional[int] = None,
+            tile: Optional[int] = None, cache: Optional[tuning.TileCache] = None) -> DeviceProblem:
+    """Uploads inputs, allocates Y (and AMAX), creates the plan for workload ``w``.  The kernel
+    instance is `tile` if given, else the one `cache` holds for this problem, else create's
+    own choice."""
     t = {k: to_device(v, device) for k, v in inputs.items()
          if k in ("A", "B", "B2", "bias", "R", "Z")}
     if "row_scale" in inputs:
@@ -74,8 +86,22 @@ def prepare(w, inputs: Dict[str, np.ndarray], device="cuda", y_fill: Optional[in
     desc = make_desc(w.batch, w.M, w.N, w.K, make_ops(w.chain),
                      y_type=GE_DT_FP8_E4M3 if fp8 else GE_DT_BF16, a_type=in_t, b_type=in_t,
                      b_layout=GE_LAYOUT_NK if getattr(w, "b_layout", "kn") == "nk" else GE_LAYOUT_KN)
+    if tile is None and cache is not None:
+        tile = cache.lookup(desc)
+    if tile is not None:
+        desc.tile = tile + 1
     plan = Plan(desc)
     args = make_args(A=t.get("A"), B=t.get("B"), B2=t.get("B2"), bias=t.get("bias"), residual=t.get("R"),
                      row_scale=t.get("row_scale"), Y=Y, amax=amax, alpha=w.alpha, quant_scale=w.quant_scale,
                      aux=t.get("Z"), col_sum=col)
     return DeviceProblem(w, plan, t, Y, amax, args, col)
+
+
+def tune(prob: DeviceProblem, cache: tuning.TileCache, steps: int = 20) -> Tuple[int, Dict[int, float]]:
+    """Sweeps every admissible kernel instance on `prob`'s tensors, records the fastest in
+    `cache` (not saved) and returns (best tile, {tile: ms per launch})."""
+    def make_run(t):
+        p = prob.with_tile(t)
+        return lambda: p.run()
+    timings = tuning.sweep(prob.plan.desc, make_run, steps=steps)
+    return cache.record(prob.plan.desc, timings), timings

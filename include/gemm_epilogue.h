@@ -115,6 +115,25 @@ typedef enum { GE_ACT_NONE = 0, GE_ACT_RELU = 1, GE_ACT_GELU_TANH = 2, GE_ACT_SI
 
 typedef enum { GE_LAYOUT_KN = 0, GE_LAYOUT_NK = 1 } ge_layout_t;
 
+/* Kernel instances (output tile shapes).  Every instance runs 4 waves of 64 lanes (2 x 2 over
+ * the tile); the pairwise ones hold two accumulators (gate and up). */
+typedef enum {
+  GE_TILE_256x256 = 0,
+  GE_TILE_256x128_PAIR = 1,
+  GE_TILE_128x128 = 2,
+  GE_TILE_64x64 = 3,
+  GE_TILE_128x128_PAIR = 4,
+  GE_TILE_COUNT = 5
+} ge_tile_t;
+
+/* Static facts of one instance: tile rows and columns, whether it is a pairwise instance,
+ * workgroup size, and the LDS bytes one workgroup allocates with B given [K][N] (the [N][K]
+ * and fp8-operand variants allocate within 32 bytes of it); a tile-config search filters
+ * candidates by this against the 160 KiB of LDS per compute unit. */
+typedef struct {
+  int32_t bm, bn, pairwise, threads, lds_bytes;
+} ge_tile_info_t;
+
 typedef enum {
   GE_OP_SCALE = 0,
   GE_OP_ROW_RMS = 1,
@@ -144,7 +163,11 @@ typedef struct {
   int32_t n_ops;
   ge_op_t ops[GE_MAX_OPS];
   int32_t b_layout;                             /* ge_layout_t of B and B2 (0 = [K][N]) */
-  int32_t reserved;                             /* must be 0 */
+  int32_t tile;                                 /* kernel instance: 0 = chosen by create (the
+                                                   largest tile that still gives >= 256
+                                                   workgroups), 1 + ge_tile_t = that instance
+                                                   (a tuned choice, e.g. from a tile-config
+                                                   sweep); its pairwise-ness must match the chain */
   int64_t ldz, stride_z;                        /* ACT_GRAD: Z leading dimension and batch stride */
 } ge_desc_t;
 
@@ -201,6 +224,10 @@ void gemm_epilogue_destroy(ge_handle_t handle);
 
 /* Static description of a status code. */
 const char* gemm_epilogue_status_string(ge_status_t status);
+
+/* Fills *info for instance `tile` (a ge_tile_t).  GE_ERR_INVALID_ARG for an unknown tile or a
+ * NULL info.  Pure host, no device needed. */
+ge_status_t gemm_epilogue_tile_info(int32_t tile, ge_tile_info_t* info);
 
 /* Writes a one-line description of the plan's kernel instance (tile shape,
  * waves, grid) into buf (NUL-terminated, truncated to len). */
