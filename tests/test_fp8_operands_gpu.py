@@ -157,3 +157,42 @@ def test_accumulation_error_bound(K):
     print(f"\nK={K}: max |error| / (alpha sum|ab|) = {float((d / S).max()):.3e}, "
           f"bound {FP8_ACC_REL / np.sqrt(max(K, 64)):.3e}", flush=True)
     assert np.all(d <= (1 + 2.0 ** -8) * E + 2.0 ** -8 * np.abs(exact)), float((d / S).max())
+
+
+def test_batched_with_broadcast_weight():
+    """batch 3 with B's batch stride 0 (one weight for every batch), fp8 output and AMAX over
+    all batches."""
+    w = F3.with_shape(batch=3, M=200, N=136, K=272)
+    inp = workloads.generate(w)
+    inp = {**inp, "B": np.ascontiguousarray(np.broadcast_to(inp["B"][:1], inp["B"].shape))}
+    prob = runner.prepare(w, {**inp, "B": inp["B"][:1]})
+    desc = ge.make_desc(w.batch, w.M, w.N, w.K, ge.make_ops(w.chain), y_type=ge.GE_DT_FP8_E4M3,
+                        a_type=ge.GE_DT_FP8_E4M3, b_type=ge.GE_DT_FP8_E4M3, b_layout=ge.GE_LAYOUT_NK,
+                        stride_b=0)
+    plan = ge.Plan(desc)
+    args = ge.make_args(A=prob.tensors["A"], B=prob.tensors["B"], bias=prob.tensors["bias"], Y=prob.Y,
+                        amax=prob.amax, alpha=w.alpha, quant_scale=w.quant_scale)
+    plan.run(args)
+    torch.cuda.synchronize()
+    compare(w, inp, prob, "fp8 operands, broadcast B over 3 batches")
+
+
+@pytest.mark.parametrize("shape", [dict(M=0), dict(N=0), dict(batch=0)], ids=["M0", "N0", "batch0"])
+def test_empty_problem_zeroes_amax(shape):
+    w = F3.with_shape(**{**dict(batch=1, M=64, N=64, K=128), **shape})
+    inp = workloads.generate(w)
+    prob = runner.prepare(w, inp)
+    prob.run()
+    torch.cuda.synchronize()
+    assert prob.amax_host() == 0.0
+
+
+@pytest.mark.parametrize("tile", [0, 2, 3], ids=["256x256", "128x128", "64x64"])
+def test_requested_tile(tile):
+    w = F3.with_shape(batch=1, M=264, N=200, K=336)
+    inp = workloads.generate(w)
+    prob = runner.prepare(w, inp, tile=tile)
+    assert f"tile={TILE_NAMES[tile]}" in prob.plan.describe()
+    prob.run()
+    torch.cuda.synchronize()
+    compare(w, inp, prob, f"fp8 operands requested tile {TILE_NAMES[tile]}")
