@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import workloads
-from tests.parity import check_amax, check_bf16, check_col_sum, check_fp8
+from tests.parity import check_amax, check_bf16, check_col_sum, check_fp8, fp8_acc_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -422,3 +422,50 @@ def test_act_grad_rejects_fp8_output_and_row_rms():
     bad2 = ge.make_desc(ops=ge.make_ops([("row_rms", 1e-6), ("act_grad", "gelu_tanh")]), **base)
     assert ge.gemm_epilogue_validate(bad1) == ge.GE_ERR_UNSUPPORTED
     assert ge.gemm_epilogue_validate(bad2) == ge.GE_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------------------------
+# Largest supported operand: A's byte extent just under the 2**31 limit of the kernels' 32-bit
+# buffer offsets, so the offsets of the last rows come closest to it (and the last row tile is
+# ragged).  A is drawn on the GPU by torch's seeded generator (not by the HIP path); the sampled
+# rows are copied back and checked against the oracle.
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("in_dtype", ["bf16", "fp8_e4m3"])
+def test_largest_supported_operand_extent(in_dtype):
+    K, N = 4096, 256
+    fp8 = in_dtype == "fp8_e4m3"
+    # validate() admits (M + 255) * K + K + slot <= 2**31 - 16 elements times the element size
+    M = 524024 if fp8 else 261880
+    base = workloads.WORKLOADS["f3" if fp8 else "c2"]
+    w = dataclasses.replace(base, chain=(("scale",), ("bias",), ("act", "relu")), out="bf16",
+                            alpha=base.alpha if fp8 else 1.25).with_shape(batch=1, M=M, N=N, K=K)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20261203)
+    A = torch.randn((1, M, K), generator=g, device="cuda", dtype=torch.float32)
+    if fp8:
+        A = (A * w.a_qscale).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    else:
+        A = A.to(torch.bfloat16)
+    small = workloads.generate(w.with_shape(M=8))                 # B and bias from the generator
+    prob = runner.prepare(w.with_shape(M=8), small)                # uploads B and bias
+    desc = ge.make_desc(1, M, N, K, ge.make_ops(w.chain), a_type=ge.GE_DT_FP8_E4M3 if fp8 else ge.GE_DT_BF16,
+                        b_type=ge.GE_DT_FP8_E4M3 if fp8 else ge.GE_DT_BF16,
+                        b_layout=ge.GE_LAYOUT_NK if fp8 else ge.GE_LAYOUT_KN)
+    assert ge.gemm_epilogue_validate(desc) == ge.GE_OK
+    desc_big = ge.make_desc(1, M + 8, N, K, ge.make_ops(w.chain),
+                            a_type=desc.a_type, b_type=desc.b_type, b_layout=desc.b_layout)
+    assert ge.gemm_epilogue_validate(desc_big) == ge.GE_ERR_UNSUPPORTED   # the limit is where it says
+    Y = torch.empty((1, M, N), dtype=torch.bfloat16, device="cuda")
+    plan = ge.Plan(desc)
+    print(f"\nlargest extent {in_dtype}: M={M} K={K}: {plan.describe()}", flush=True)
+    plan.run(ge.make_args(A=A, B=prob.tensors["B"], bias=prob.tensors["bias"], Y=Y, alpha=w.alpha))
+    torch.cuda.synchronize()
+    rows = np.r_[0:64, M // 2:M // 2 + 64, M - 264:M]            # head, middle, ragged tail
+    a_rows = A[0, torch.from_numpy(rows).cuda()].cpu()
+    a_bits = a_rows.numpy() if fp8 else a_rows.view(torch.int16).numpy().view(np.uint16)
+    ref = oracle.run_workload(w.with_shape(M=len(rows)), {**small, "A": a_bits[None]})
+    y = Y[0, torch.from_numpy(rows).cuda()].cpu().view(torch.int16).numpy().view(np.uint16)
+    # fp8 operands: allow the fp8 instruction's accumulation error (ReLU's slope is 1)
+    allow = fp8_acc_bound(a_bits[None], small["B"], w.alpha, K) if fp8 else None
+    check_bf16(y[None], ref.y, f"largest extent {in_dtype}", allow=allow)
