@@ -222,8 +222,26 @@ def cpu_baseline(w, inputs, seconds):
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 1000:
             break
+    # the split: the oracle's GEMM step alone on the same sample (operands decoded untimed)
+    from oracle.chain import decode_operand
+    a = decode_operand(sub["A"] if rows is None else sub["A"][:, rows, :])
+    bs = [decode_operand(sub[k]) for k in ("B", "B2") if k in sub and (k == "B" or w.pairwise)]
+    if w.b_layout == "nk":
+        bs = [np.swapaxes(b, -1, -2) for b in bs]
+    t1 = time.perf_counter()
+    for b in bs:
+        oracle.gemm(a, b)
+    gemm_s = time.perf_counter() - t1
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(flops_per * reps / el / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle", "sample": sample_desc + f" x{reps} in {el:.1f} s (float64 GEMM + unfused epilogue + encode)"}
+            "kind": "oracle", "sample": sample_desc + f" x{reps} in {el:.1f} s (float64 GEMM + unfused epilogue + encode)",
+            "gemm_s_per_sample": round(gemm_s, 6), "rest_s_per_sample": round(el / reps - gemm_s, 6),
+            "cpu_model": cpu_model}
 
 
 def main():
