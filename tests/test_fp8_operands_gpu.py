@@ -197,3 +197,28 @@ def test_requested_tile(tile):
     prob.run()
     torch.cuda.synchronize()
     compare(w, inp, prob, f"fp8 operands requested tile {TILE_NAMES[tile]}")
+
+
+def test_graph_replays_match_eager_runs():
+    """fp8 operands replayed from a HIP graph (as the benchmark may): every replay, with eager
+    work between replays, reproduces the eager output and AMAX bit for bit."""
+    w = F3.with_shape(M=1024, N=2048, K=1024)
+    inp = workloads.generate(w)
+    prob = gpu_run(w, inp)
+    compare(w, inp, prob, "f3 eager")
+    y_eager, a_eager = prob.Y.clone(), prob.amax_host()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(3):
+            prob.run()
+    for rep in range(3):
+        prob.Y.zero_()
+        prob.amax.fill_(-1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(prob.Y, y_eager), f"replay {rep}"
+        assert prob.amax_host() == a_eager, f"replay {rep}"
+        prob.run()
+        torch.cuda.synchronize()
+        assert torch.equal(prob.Y, y_eager)

@@ -328,17 +328,20 @@ def test_repeated_runs_are_identical_and_amax_is_overwritten():
     assert prob.amax_host() == a1
 
 
-@pytest.mark.parametrize("name", ["c2", "c5"])
+@pytest.mark.parametrize("name", ["c2", "c5", "f2"])
 def test_graph_replays_match_eager_runs(name):
     """The benchmark replays the launches from a HIP graph: every replay, with eager work and
-    synchronisation between replays, gives the eager output and AMAX, and leaves the AMAX
-    ticket counters at zero."""
+    synchronisation between replays, gives the eager output, AMAX and column sums, and leaves
+    the ticket counters at zero."""
     w = workloads.WORKLOADS[name]
     if name == "c5":
         w = w.with_shape(M=1024, N=2048, K=1024)
+    if name == "f2":
+        w = w.with_shape(M=1024, N=1376, K=512)
     inp = workloads.generate(w)
     prob = gpu_run(w, inp)
     y_eager, a_eager = prob.Y.clone(), prob.amax_host()
+    cs_eager = None if prob.col_sum is None else prob.col_sum.clone()
     compare(w, inp, prob, f"{name} eager")
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
@@ -346,13 +349,23 @@ def test_graph_replays_match_eager_runs(name):
             prob.run()
     for rep in range(3):
         prob.Y.zero_()
-        prob.amax.fill_(-1.0)
+        if prob.amax is not None:
+            prob.amax.fill_(-1.0)
+        if prob.col_sum is not None:
+            prob.col_sum.fill_(float("nan"))
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(prob.Y, y_eager), f"replay {rep}"
         assert prob.amax_host() == a_eager, f"replay {rep}"
-        assert int(prob.plan.workspace[:4096].count_nonzero()) == 0, f"replay {rep}"
+        ws = prob.plan.workspace.view(torch.int32)
+        if cs_eager is None:
+            assert int(ws[:1024].count_nonzero()) == 0, f"replay {rep}"      # AMAX counters
+        else:
+            assert torch.equal(prob.col_sum, cs_eager), f"replay {rep}"      # bit-identical
+            bn = int(prob.plan.describe().split("tile=")[1].split("x")[1])   # the plan's tile width
+            tiles_n = (w.N + bn - 1) // bn
+            assert int(ws[: tiles_n * 16].count_nonzero()) == 0, f"replay {rep}"  # column-tile counters
         prob.run()                                  # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(prob.Y, y_eager)
