@@ -226,7 +226,10 @@ void gemm_epilogue_destroy(ge_handle_t handle);
 const char* gemm_epilogue_status_string(ge_status_t status);
 
 /* Fills *info for instance `tile` (a ge_tile_t).  GE_ERR_INVALID_ARG for an unknown tile or a
- * NULL info.  Pure host, no device needed. */
+ * NULL info.  Pure host, no device needed.  For a tile-config search: the TileLang tutorial's
+ * schedule-exploration paragraph autotunes over tile sizes and drops candidates beyond the
+ * shared-memory budget; the cuDNN tutorial's engine-autotuning paragraph times every candidate
+ * plan instead of trusting the heuristic.  The chosen instance goes in ge_desc_t.tile. */
 ge_status_t gemm_epilogue_tile_info(int32_t tile, ge_tile_info_t* info);
 
 /* Writes a one-line description of the plan's kernel instance (tile shape,
