@@ -222,3 +222,25 @@ def test_graph_replays_match_eager_runs():
         prob.run()
         torch.cuda.synchronize()
         assert torch.equal(prob.Y, y_eager)
+
+
+def test_fp8_output_feeds_the_next_layer():
+    """Delayed scaling end to end: layer 1 (bf16 operands, c5's chain) writes e4m3 codes of
+    y * 112 and its AMAX; layer 2 consumes such codes as its fp8 A operand, dequantised by
+    alpha = 1 / (112 * scale_B).  Layer 1 is checked against the oracle; layer 2 runs on the
+    oracle's layer-1 codes (oracle inputs never come from the kernel) and is checked against
+    the oracle too, and the kernel's own layer-1 codes are the same codes within one step."""
+    l1 = workloads.WORKLOADS["c5"].with_shape(batch=1, M=512, N=768, K=1024)
+    in1 = workloads.generate(l1)
+    p1 = gpu_run(l1, in1)
+    ref1 = oracle.run_workload(l1, in1)
+    from tests.parity import check_fp8
+    check_fp8(p1.y_host_bits(), ref1.codes, "layer 1")
+    check_amax(p1.amax_host(), ref1.amax, "layer 1")
+    assert 448.0 / ref1.amax > 0                      # the next scale delayed scaling would use
+    l2 = dataclasses.replace(F3, alpha=1.0 / (l1.quant_scale * F3.b_qscale)).with_shape(batch=1, M=512, N=640, K=768)
+    in2 = workloads.generate(l2)
+    in2 = {**in2, "A": ref1.codes}                    # layer 1's output, as the oracle encoded it
+    assert in2["A"].shape == (1, l2.M, l2.K) and in2["A"].dtype == np.uint8
+    p2 = gpu_run(l2, in2)
+    compare(l2, in2, p2, "layer 2 on layer-1 codes")
