@@ -482,3 +482,44 @@ def test_largest_supported_operand_extent(in_dtype):
     # fp8 operands: allow the fp8 instruction's accumulation error (ReLU's slope is 1)
     allow = fp8_acc_bound(a_bits[None], small["B"], w.alpha, K) if fp8 else None
     check_bf16(y[None], ref.y, f"largest extent {in_dtype}", allow=allow)
+
+
+def test_run_rejects_bad_arguments_without_launching():
+    """run() returns GE_ERR_INVALID_ARG, and enqueues nothing, for a pointer the chain needs
+    that is NULL or misaligned, and for a too-small workspace; the output stays untouched."""
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def expect_invalid(prob, **changes):
+        args = ge.ge_args_t.from_buffer_copy(prob.args)
+        if prob.plan.workspace is not None:
+            args.workspace, args.workspace_bytes = prob.plan.workspace.data_ptr(), prob.plan.workspace.numel()
+        for k, v in changes.items():
+            setattr(args, k, v)
+        before = prob.Y.clone()
+        assert ge.gemm_epilogue_run(prob.plan.handle, args, stream) == ge.GE_ERR_INVALID_ARG, changes
+        torch.cuda.synchronize()
+        assert torch.equal(prob.Y, before), changes
+
+    fwd = workloads.WORKLOADS["c5"].with_shape(M=128, N=128, K=128)
+    p = runner.prepare(fwd, workloads.generate(fwd))
+    for ptr in ("A", "B", "Y", "bias", "amax"):
+        expect_invalid(p, **{ptr: None})
+    expect_invalid(p, Y=p.Y.data_ptr() + 2)                     # 16-byte alignment
+    expect_invalid(p, A=p.tensors["A"].data_ptr() + 8)
+    expect_invalid(p, bias=p.tensors["bias"].data_ptr() + 4)
+    expect_invalid(p, amax=p.amax.data_ptr() + 2)               # 4-byte alignment
+    expect_invalid(p, workspace_bytes=p.plan.workspace.numel() - 4)
+    expect_invalid(p, workspace=None, workspace_bytes=0)
+
+    pair = workloads.WORKLOADS["c3"].with_shape(M=128, N=128, K=128)
+    pp = runner.prepare(pair, workloads.generate(pair))
+    expect_invalid(pp, B2=None)
+
+    bwd = workloads.WORKLOADS["f2"].with_shape(M=128, N=128, K=128)
+    pb = runner.prepare(bwd, workloads.generate(bwd))
+    expect_invalid(pb, aux=None)                                 # the saved pre-activation Z
+    expect_invalid(pb, col_sum=None)
+
+    rms = workloads.WORKLOADS["c4"].with_shape(M=128, N=128, K=128)
+    pr = runner.prepare(rms, workloads.generate(rms))
+    expect_invalid(pr, residual=None)
