@@ -45,9 +45,9 @@ METRIC = "fused GEMM-epilogue TFLOP/s (% of MI355X bf16 MFMA peak) per config"
 # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE (x2.0) + WRITE_SIZE (x1.0) of the fused
 # kernel at each workload; the factors scale the counters to the bytes of a plain 1 GiB device
 # copy.  Valid only for the kernel source they were taken on (sha256 prefix below).
-MEASURED_TRAFFIC_SOURCE = "9004fcad84ffc380"
-MEASURED_TRAFFIC = {"c1": 1074373, "c2": 101285833, "c3": 2378705484, "c4": 537492622, "c5": 1756519655,
-                    "f1": 2380060623, "f2": 1689800397, "f3": 874892888}
+MEASURED_TRAFFIC_SOURCE = "aec1b252370a36bd"
+MEASURED_TRAFFIC = {"c1": 1068230, "c2": 101242441, "c3": 2545613168, "c4": 537517353, "c5": 1925895337,
+                    "f1": 3171490838, "f2": 1807169248, "f3": 875357753}
 
 
 def kernel_source_hash():
