@@ -45,9 +45,9 @@ METRIC = "fused GEMM-epilogue TFLOP/s (% of MI355X bf16 MFMA peak) per config"
 # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE (x2.0) + WRITE_SIZE (x1.0) of the fused
 # kernel at each workload; the factors scale the counters to the bytes of a plain 1 GiB device
 # copy.  Valid only for the kernel source they were taken on (sha256 prefix below).
-MEASURED_TRAFFIC_SOURCE = "aec1b252370a36bd"
-MEASURED_TRAFFIC = {"c1": 1068230, "c2": 101242441, "c3": 2545613168, "c4": 537517353, "c5": 1925895337,
-                    "f1": 3171490838, "f2": 1807169248, "f3": 875357753}
+MEASURED_TRAFFIC_SOURCE = "883464c901c3d681"
+MEASURED_TRAFFIC = {"c1": 1068229, "c2": 101242438, "c3": 2642114460, "c4": 537512242, "c5": 1909662468,
+                    "f1": 3308458054, "f2": 1687832879, "f3": 875346280}
 
 
 def kernel_source_hash():
