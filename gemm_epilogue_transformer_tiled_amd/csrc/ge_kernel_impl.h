@@ -875,6 +875,8 @@ void fused_gemm_epilogue(Params p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) csum[e] += ok ? y[e] : 0.0f;
       const uint32_t yoff = ok ? (uint32_t)ml * ldy_b + col_y : kOOB;
+      // Y is written once and not read back here: non-temporal stores (cache policy bit 1, "nt")
+      // measured +1 to +4 % over plain stores across the workloads.
       if constexpr (FP8) {
         const float qs = p.qscale;
         float z[4];
@@ -882,12 +884,12 @@ void fused_gemm_epilogue(Params p) {
         for (int e = 0; e < 4; ++e) z[e] = fminf(fmaxf(y[e] * qs, -448.0f), 448.0f);
         int w = __builtin_amdgcn_cvt_pk_fp8_f32(z[0], z[1], 0, false);
         w = __builtin_amdgcn_cvt_pk_fp8_f32(z[2], z[3], w, true);
-        __builtin_amdgcn_raw_buffer_store_b32((unsigned)w, y_rs, yoff, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32((unsigned)w, y_rs, yoff, 0, 2);
       } else {
         u32x2_t w;
         w[0] = pack_bf16x2(y[0], y[1]);
         w[1] = pack_bf16x2(y[2], y[3]);
-        __builtin_amdgcn_raw_buffer_store_b64(w, y_rs, yoff, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(w, y_rs, yoff, 0, 2);
       }
     }
     }
