@@ -45,9 +45,9 @@ METRIC = "fused GEMM-epilogue TFLOP/s (% of MI355X bf16 MFMA peak) per config"
 # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE (x2.0) + WRITE_SIZE (x1.0) of the fused
 # kernel at each workload; the factors scale the counters to the bytes of a plain 1 GiB device
 # copy.  Valid only for the kernel source they were taken on (sha256 prefix below).
-MEASURED_TRAFFIC_SOURCE = "883464c901c3d681"
-MEASURED_TRAFFIC = {"c1": 1068229, "c2": 101242438, "c3": 2642114460, "c4": 537512242, "c5": 1909662468,
-                    "f1": 3308458054, "f2": 1687832879, "f3": 875346280}
+MEASURED_TRAFFIC_SOURCE = "11d757d1383956d1"
+MEASURED_TRAFFIC = {"c1": 1068231, "c2": 101242480, "c3": 2435716402, "c4": 537602138, "c5": 1687017830,
+                    "f1": 2611940408, "f2": 1727955033, "f3": 874128325}
 
 
 def kernel_source_hash():
