@@ -1,21 +1,30 @@
 #!/usr/bin/env python3
 """Throughput of the fused GEMM-epilogue path on one MI355X.
 
-One step = one ``gemm_epilogue_run`` (a single fused kernel launch) over the
-workload's seeded synthetic inputs, already resident in HBM.  The default
-workload is the batched one (batch 16 x 1024^3, alpha 1.25, column bias, ReLU,
-AMAX over all outputs, bf16 output); ``--config c1..c5`` selects another.
+One step = one ``gemm_epilogue_run`` (a single fused kernel launch) over a
+workload's seeded synthetic inputs, already resident in HBM.
+
+Without ``--config`` the benchmark runs the whole suite: the SwiGLU
+up-projection c3 (8192x4096 -> 2x11008, the largest configuration, and the
+headline), then c1, c2, c4, c5 and the three further workloads f1 (RMSNorm-MLP),
+f2 (MLP backward) and f3 (fp8 operands).  Each configuration runs in a child
+process of its own (``--config X``); this parent process never touches the GPU.
+A configuration that fails is recorded with its status and the suite carries
+on; one that ends abnormally (a signal, an abort, a time limit) stops the suite,
+and the remaining configurations are recorded as skipped.
 
 The K timed steps run back to back on one stream, issued either eagerly or as one
 replay of a HIP graph holding the K launches (``--launch``; by default the faster
 on an untimed probe, named in the output).
 
-Prints ONE JSON line:
+Prints ONE JSON line (the headline configuration's fields, plus ``per_config``):
   value      whole-job TFLOP/s = 2*M*N*K*batch (x2 pairwise) / (timed wall time / steps)
-  roofline   the fused kernel's achieved TFLOP/s over its average launch duration (HIP
-             events on its stream around the back-to-back steps) against the MI355X dense
-             bf16 MFMA peak (2.5 PFLOP/s); traffic = HBM bytes per launch from the
-             FETCH_SIZE / WRITE_SIZE counters, when they were taken on this kernel source
+  roofline   the fused kernel's achieved rate over its average launch duration (HIP
+             events on its stream around the back-to-back steps) against the MI355X peak
+             of its bound: dense bf16 MFMA 2.5 PFLOP/s (fp8 operands: 5.0) when the
+             workload's ideal time at that peak exceeds its ideal time at 8 TB/s of HBM,
+             else HBM; traffic = HBM bytes per launch from the FETCH_SIZE / WRITE_SIZE
+             counters, when they were taken on this kernel source
   cpu_baseline  the float64 oracle on this host's cores over a bounded sample
   epilogue_overhead_pct  fused kernel time over the same kernel instance with the
              chain reduced to a plain bf16 store (pairwise: the bare product g*u)
@@ -23,6 +32,8 @@ Prints ONE JSON line:
   unfused    the same chain run unfused (GEMM writes bf16 C, one kernel per operation):
              its time, kernels and algorithmic HBM bytes, and the bytes the fusion saves
   measured_peaks  what the MFMA and streaming-copy probes sustain on this GPU
+  per_config  for every configuration of the suite: status, TFLOP/s, GB/s, roofline
+             fractions, epilogue overhead, unfused bytes saved and a short oracle baseline
 """
 from __future__ import annotations
 
@@ -30,6 +41,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -41,6 +53,11 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published (the fp8-operand workload)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 METRIC = "fused GEMM-epilogue TFLOP/s (% of MI355X bf16 MFMA peak) per config"
+# The suite, headline first: c3 is the largest configuration (1.48 TFLOP per step).
+SUITE = ["c3", "c1", "c2", "c4", "c5", "f1", "f2", "f3"]
+# Exit statuses of a child that ended abnormally (signal, abort, segmentation fault, time
+# limit): after one of these nothing more is started on the GPU.
+ABNORMAL_RC = {-6, -9, -11, -15, 124, 134, 137, 139}
 
 # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE (x2.0) + WRITE_SIZE (x1.0) of the fused
 # kernel at each workload; the factors scale the counters to the bytes of a plain 1 GiB device
@@ -66,10 +83,17 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "f1", "f2", "f3"],
-                    help="c1..c5: the five configurations; f1: the RMSNorm-MLP (row RMS + pairwise "
-                         "product); f2: the MLP backward step (activation gradient + column sums, B as [N][K]); "
-                         "f3: fp8-e4m3 operands (delayed scaling) into the c5 epilogue")
+    ap.add_argument("--config", default=None, choices=SUITE,
+                    help="run one workload in this process (default: the whole suite, each configuration in "
+                         "a child process).  c1..c5: the five configurations; f1: the RMSNorm-MLP (row RMS + "
+                         "pairwise product); f2: the MLP backward step (activation gradient + column sums, B as "
+                         "[N][K]); f3: fp8-e4m3 operands (delayed scaling) into the c5 epilogue")
+    ap.add_argument("--suite", default=",".join(SUITE),
+                    help="comma-separated configurations of the suite, the headline first")
+    ap.add_argument("--suite-cpu-seconds", type=float, default=2.5,
+                    help="oracle sample budget of each non-headline configuration of the suite")
+    ap.add_argument("--child-timeout", type=float, default=300.0,
+                    help="seconds one configuration of the suite may take before it is stopped")
     ap.add_argument("--launch", default="auto", choices=["auto", "eager", "graph"],
                     help="issue the timed steps eagerly or as one HIP-graph replay (auto: the faster on a probe)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle timing sample")
@@ -244,18 +268,18 @@ def cpu_baseline(w, inputs, seconds):
             "cpu_model": cpu_model}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: the fused GEMM-epilogue path has no multi-GPU leg "
-              f"(asked for --gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
+def roofline_bound(w, peak_tflops):
+    """("mfma" | "hbm", ideal µs at the MFMA peak, ideal µs at the HBM peak): the bound is the
+    larger of the two ideal times (flops at the matrix-core peak of the operand type, the
+    algorithmic bytes at 8 TB/s)."""
+    t_mfma = w.flops() / (peak_tflops * 1e12) * 1e6
+    t_hbm = w.algorithmic_bytes() / (PEAK_HBM_GBS * 1e9) * 1e6
+    return ("mfma" if t_mfma >= t_hbm else "hbm"), t_mfma, t_hbm
 
+
+def run_one(args):
+    """Measures one workload in this process and prints its JSON line."""
     import torch
-
-    if args.calibrate_copy:
-        calibrate_copy(args.calibrate_copy)
-        return
 
     import workloads
     from gemm_epilogue_transformer_tiled_amd import runner
@@ -285,9 +309,12 @@ def main():
     # The steps run back to back, so the kernel's average launch duration is the step time.
     launch_ms = ms_step
     achieved = value
-    # a contraction is priced against the matrix-core peak of its own operand type
+    # a contraction is priced against the matrix-core peak of its own operand type; a workload
+    # whose ideal time at 8 TB/s exceeds its ideal time at that peak is priced against HBM
     fp8_in = w.in_dtype == "fp8_e4m3"
     peak = PEAK_FP8_TFLOPS if fp8_in else PEAK_BF16_TFLOPS
+    bound, t_mfma_us, t_hbm_us = roofline_bound(w, peak)
+    gbs = w.algorithmic_bytes() / (launch_ms * 1e-3) / 1e9
     result = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -311,20 +338,26 @@ def main():
         "launch": {"mode": mode, "probe_ms_per_step": probe},
         "tile_sweep": tuned,
         "roofline": {
-            "bound": "mfma",
-            "achieved": round(achieved, 3),
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4),
+            "bound": bound,
+            "achieved": round(achieved, 3) if bound == "mfma" else round(gbs, 1),
+            "peak": peak if bound == "mfma" else PEAK_HBM_GBS,
+            "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+            "frac": round(achieved / peak, 4) if bound == "mfma" else round(gbs / PEAK_HBM_GBS, 4),
+            "frac_mfma": round(achieved / peak, 4),
+            "ideal_us_at_mfma_peak": round(t_mfma_us, 3),
+            "ideal_us_at_hbm_peak": round(t_hbm_us, 3),
             "traffic": MEASURED_TRAFFIC.get(w.name) if kernel_source_hash() == MEASURED_TRAFFIC_SOURCE else None,
             "kernel": "fused_gemm_epilogue",
             "launch_ms_mean": round(launch_ms, 6),
             "algorithmic_flops_per_launch": flops,
             "algorithmic_bytes_per_launch": w.algorithmic_bytes(),
-            "hbm_gbs_at_algorithmic_bytes": round(w.algorithmic_bytes() / (launch_ms * 1e-3) / 1e9, 1),
-            "hbm_frac": round(w.algorithmic_bytes() / (launch_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "hbm_gbs_at_algorithmic_bytes": round(gbs, 1),
+            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         },
     }
+    if max(t_mfma_us, t_hbm_us) < 1.0:
+        result["roofline"]["note"] = ("launch-latency bound: the ideal time at either peak is under 1 us, "
+                                      "so the fraction measures launch and synchronisation cost")
     if not args.no_bare:
         # fused, bare, fused again: the overhead compares the bare kernel with the mean of the
         # fused runs on either side of it, so slow clock drift cancels
@@ -361,9 +394,119 @@ def main():
                                     "copy_gbs": cp["gbs"]}
         if not fp8_in:      # the probe runs the bf16 instruction
             result["roofline"]["frac_of_measured_mfma_peak"] = round(achieved / mf["tflops"], 4)
+        result["roofline"]["frac_of_measured_copy_gbs"] = round(gbs / cp["gbs"], 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def _summary(d):
+    """The per-configuration record of a child's JSON line."""
+    rf = d.get("roofline", {})
+    out = {
+        "status": "ok",
+        "workload": d["config"]["workload"],
+        "kernel": d["config"].get("kernel"),
+        "dtype": d.get("dtype"),
+        "value": d["value"],
+        "unit": d["unit"],
+        "ms_per_step": d["ms_per_step"],
+        "launch_mode": d.get("launch", {}).get("mode"),
+        "bound": rf.get("bound"),
+        "frac": rf.get("frac"),
+        "frac_mfma": rf.get("frac_mfma"),
+        "gbs": rf.get("hbm_gbs_at_algorithmic_bytes"),
+        "frac_hbm": rf.get("hbm_frac"),
+        "traffic": rf.get("traffic"),
+        "algorithmic_bytes_per_launch": rf.get("algorithmic_bytes_per_launch"),
+        "epilogue_overhead_pct": d.get("epilogue_overhead_pct"),
+        "bare_gemm_ms": d.get("bare_gemm_ms"),
+    }
+    if "note" in rf:
+        out["note"] = rf["note"]
+    if "unfused" in d:
+        u = d["unfused"]
+        out["unfused"] = {k: u[k] for k in ("ms_per_step", "fused_speedup", "algorithmic_bytes", "bytes_saved",
+                                            "bytes_ratio") if k in u}
+    if "cold" in d:
+        out["cold_ms_median"] = d["cold"]["ms_median"]
+    if "cpu_baseline" in d:
+        out["cpu_baseline"] = d["cpu_baseline"]
+    return out
+
+
+def run_suite(args):
+    """Runs every configuration of the suite in a child process (this process never touches
+    the GPU) and prints one JSON line: the headline configuration's fields plus per_config."""
+    names = [n for n in args.suite.split(",") if n]
+    for n in names:
+        if n not in SUITE:
+            print(f"unknown configuration {n!r} in --suite", file=sys.stderr)
+            sys.exit(2)
+    headline = names[0]
+    per, lines, stop = {}, {}, None
+    t_suite = time.perf_counter()
+    for n in names:
+        if stop is not None:
+            per[n] = {"status": "skipped", "reason": f"{stop} ended abnormally; nothing more was started on the GPU"}
+            continue
+        cmd = [sys.executable, "-u", os.path.abspath(__file__), "--config", n, "--steps", str(args.steps),
+               "--warmup", str(args.warmup), "--launch", args.launch,
+               "--cpu-seconds", str(args.cpu_seconds if n == headline else args.suite_cpu_seconds)]
+        for flag in ("no_cpu_baseline", "no_bare", "no_cold", "no_unfused", "no_probes"):
+            if getattr(args, flag):
+                cmd.append("--" + flag.replace("_", "-"))
+        print(f"[bench] {n}: start", file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=args.child_timeout)
+            rc, out, err = r.returncode, r.stdout, r.stderr
+        except subprocess.TimeoutExpired as e:
+            rc, out, err = 124, (e.stdout or b""), (e.stderr or b"")
+            out = out.decode(errors="replace") if isinstance(out, bytes) else out
+            err = err.decode(errors="replace") if isinstance(err, bytes) else err
+        el = time.perf_counter() - t0
+        line = next((l for l in reversed(out.splitlines()) if l.startswith("{")), None)
+        if rc == 0 and line is not None:
+            d = json.loads(line)
+            lines[n] = d
+            per[n] = _summary(d)
+            per[n]["wall_s"] = round(el, 1)
+            print(f"[bench] {n}: ok, {d['value']} TFLOP/s, {d['ms_per_step'] * 1e3:.2f} us/step ({el:.1f} s)",
+                  file=sys.stderr, flush=True)
+        else:
+            per[n] = {"status": "failed", "rc": rc, "wall_s": round(el, 1),
+                      "stderr_tail": "\n".join(err.strip().splitlines()[-6:])}
+            print(f"[bench] {n}: FAILED rc={rc} ({el:.1f} s)\n{per[n]['stderr_tail']}", file=sys.stderr, flush=True)
+            if rc in ABNORMAL_RC:
+                stop = n
+    if headline in lines:
+        result = dict(lines[headline])
+    else:
+        result = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+                  "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+                  "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                  "config": {"workload": headline}, "status": per[headline]}
+    result["per_config"] = per
+    result["suite_wall_s"] = round(time.perf_counter() - t_suite, 1)
+    print(json.dumps(result), flush=True)
+    if headline not in lines:
+        sys.exit(1)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the fused GEMM-epilogue path has no multi-GPU leg "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+    if args.config is None:
+        run_suite(args)
+    else:
+        run_one(args)
 
 
 if __name__ == "__main__":

@@ -67,10 +67,14 @@
  *                    the column reduction that gives a bias gradient (same item, the
  *                    "reductions" primitive); overwritten, not accumulated; needs the
  *                    workspace; deterministic (fixed summation order)
- *   AMAX             *amax = max |y| over all outputs, before any rounding (needs the workspace)
+ *   AMAX             *amax = max |y| over all outputs, before any rounding (needs the workspace);
+ *                    the maximum is taken on the bit patterns of |y|, so a NaN y gives a NaN
  *   QUANT_FP8        Y = e4m3(clamp(y * quant_scale, -448, 448)), round to
- *                    nearest even; requires y_type == GE_DT_FP8_E4M3 and must be last
- *   Without QUANT_FP8, Y = bf16(y), round to nearest even (y_type == GE_DT_BF16).
+ *                    nearest even; requires y_type == GE_DT_FP8_E4M3 and must be last.
+ *                    Overflow saturates to +-448; a NaN y * quant_scale is written as the
+ *                    e4m3 NaN code 0x7F (OCP: S.1111.111, no infinities)
+ *   Without QUANT_FP8, Y = bf16(y), round to nearest even (y_type == GE_DT_BF16); NaN
+ *   stays NaN and overflow becomes +-inf.
  *   Activations: RELU max(t,0); GELU_TANH 0.5 t (1 + tanh(sqrt(2/pi)(t + 0.044715 t^3)));
  *   SILU t / (1 + e^-t).
  *
@@ -195,34 +199,72 @@ typedef struct {
 
 typedef struct ge_plan* ge_handle_t;
 
-/* Checks a descriptor without touching any device.  Returns GE_OK,
- * GE_ERR_INVALID_ARG (malformed) or GE_ERR_UNSUPPORTED (outside the supported set). */
+/* Checks a descriptor without touching any device: the validation step of the cuDNN
+ * tutorial's five-step build (opening paragraph: validate, build the operation graph, create
+ * execution plans, check support, build the plan; then execute over a variant pack of
+ * pointers); the op set and its order are the CODA news item's epilogue primitives ("How
+ * CODA works").
+ *   desc: host pointer, read only, not retained.
+ * Returns GE_OK, GE_ERR_INVALID_ARG (NULL desc, negative size or stride, a leading dimension
+ * below the row length, unknown op or dtype, ops out of the canonical order or repeated) or
+ * GE_ERR_UNSUPPORTED (well formed but outside the supported set: alignment, extents beyond
+ * 31-bit byte offsets, fp8 operands with B given [K][N], ...).  Never aborts. */
 ge_status_t gemm_epilogue_validate(const ge_desc_t* desc);
 
-/* Validates, checks that the current HIP device is gfx950, and picks a kernel
- * instance (tile shape) for the descriptor.  On success *out owns a host-side
- * plan; on failure *out is set to NULL.  Launches nothing. */
+/* Builds a plan: validation, the support check against the current device and the choice
+ * of a kernel instance -- the support-check and plan-building steps of the cuDNN tutorial's
+ * five-step build (opening paragraph), done once so that execution only binds pointers.
+ *   desc: host pointer, copied into the plan (the caller may free it afterwards).
+ *   out:  receives the handle; set to NULL on any failure.
+ * Returns the status of gemm_epilogue_validate, GE_ERR_DEVICE when no HIP device is current or
+ * it is not gfx950, GE_ERR_HIP when host memory for the plan cannot be had.  Launches nothing
+ * and allocates no device memory; the handle owns host memory only. */
 ge_status_t gemm_epilogue_create(const ge_desc_t* desc, ge_handle_t* out);
 
-/* Device scratch the plan needs from the caller, in bytes; 0 without AMAX and COL_SUM.
+/* Device scratch the plan needs from the caller, in bytes -- the plan-specific workspace of
+ * the cuDNN tutorial (set-up paragraph: a helper allocates the workspace; engine-autotuning
+ * paragraph: each candidate plan is built, given a workspace of the size it reports, and
+ * timed); 0 without AMAX and COL_SUM.
  * AMAX: nine ticket counters on their own cache lines plus one partial-maximum slot per
  * workgroup.  COL_SUM: one ticket counter per column tile plus one fp32 partial column sum
- * per row tile, batch and column.  Zero-filled before first use; counters return to zero. */
+ * per row tile, batch and column.
+ * The workspace must be zero-filled before its first use, and every run that completes leaves
+ * its counters at zero again.  HAZARD: a workspace whose counters are not zero -- never
+ * cleared, or shared by two runs that overlap in time (two streams, or a run that did not
+ * complete) -- makes AMAX and COL_SUM silently wrong: a counter holding d > 0 elects a "last"
+ * workgroup d arrivals early.  Clear it again (e.g. hipMemset) after any such event, and give
+ * concurrent runs separate workspaces.  Returns GE_ERR_INVALID_ARG for a NULL handle or bytes. */
 ge_status_t gemm_epilogue_workspace_size(ge_handle_t handle, size_t* bytes);
 
-/* Enqueues the fused GEMM + epilogue on `stream` (a hipStream_t; NULL = the
- * null stream) as ONE kernel launch and returns without waiting.  With AMAX
- * in the chain, *amax is overwritten with max|y| when the kernel completes
- * (the last workgroup to finish reduces the per-workgroup maxima and publishes it).  Returns GE_ERR_INVALID_ARG for
- * a pointer an op needs that is NULL or misaligned (or a too-small AMAX
- * workspace), GE_ERR_HIP if the launch fails.  An empty problem (batch, M or
- * N zero) launches only a one-thread kernel that writes *amax = 0. */
+/* Executes a plan against a "variant pack" of borrowed device pointers and host scalars --
+ * the execution step of the cuDNN tutorial's build-then-execute model (opening paragraph:
+ * execution over a variant pack; batched-matmul paragraph: alpha is a host scalar and AMAX is
+ * reduced on the result in the same kernel; closing paragraph: the stream is set per
+ * execution, e.g. to a graph-capturing stream).  Computes the operation of the header
+ * comment: the tiled GEMM with its output tile kept on chip while the epilogue runs, then one
+ * store (TileLang tutorial, tiled-matmul and fused-epilogue paragraphs; CODA news item, "How
+ * CODA works").
+ *   handle: from gemm_epilogue_create; read only, so concurrent runs of one handle are safe
+ *           when they use separate outputs and workspaces.
+ *   args:   host pointer, read during the call only; the device pointers it holds are borrowed
+ *           until the enqueued kernel completes.
+ *   stream: a hipStream_t (NULL = the null stream).
+ * Enqueues ONE kernel launch and returns without waiting.  With AMAX in the chain, *amax is
+ * overwritten with max|y| when the kernel completes (the last workgroup to finish reduces the
+ * per-workgroup maxima and publishes it).  Returns GE_ERR_INVALID_ARG for a NULL handle or
+ * args, for a pointer an op needs that is NULL or misaligned, or for a workspace smaller than
+ * gemm_epilogue_workspace_size (nothing is enqueued then), GE_ERR_HIP if the launch fails.  An
+ * empty problem (batch, M or N zero) launches only a one-thread kernel that writes *amax = 0
+ * (and, with COL_SUM, a kernel that zeroes col_sum). */
 ge_status_t gemm_epilogue_run(ge_handle_t handle, const ge_args_t* args, void* stream);
 
-/* Frees the plan.  NULL is a no-op. */
+/* Frees the plan's host memory (the end of a plan's life in the cuDNN tutorial's plan-reuse
+ * model, closing paragraphs: a plan is built once and executed many times).  NULL is a no-op.  Work
+ * already enqueued with the handle is unaffected: run() copies what the kernel needs. */
 void gemm_epilogue_destroy(ge_handle_t handle);
 
-/* Static description of a status code. */
+/* Static, NUL-terminated description of a status code (never NULL; "unknown status" for a
+ * value outside ge_status_t). */
 const char* gemm_epilogue_status_string(ge_status_t status);
 
 /* Fills *info for instance `tile` (a ge_tile_t).  GE_ERR_INVALID_ARG for an unknown tile or a

@@ -77,6 +77,40 @@ def compare(w, inp, prob, what, rows=None):
 RAGGED = dict(batch=2, M=300, N=264, K=200)
 
 
+def plan_tile(prob):
+    """(rows, columns) of the kernel instance the plan chose, from its description."""
+    bm, bn = prob.plan.describe().split("tile=")[1].split("x")[:2]
+    return int(bm), int(bn)
+
+
+def workspace_words(w, prob):
+    """Word offsets of the plan's workspace, from the tile the plan actually chose: AMAX --
+    nine ticket counters in words [0, 1024) and one slot per workgroup from word 1024; COL_SUM
+    -- one ticket counter per column tile (16 words apart) from `cs_ctr`, then the partials."""
+    bm, bn = plan_tile(prob)
+    tiles_m, tiles_n = -(-w.M // bm), -(-w.N // bn)
+    wgs = tiles_m * tiles_n * w.batch
+    round64 = lambda x: (x + 63) // 64 * 64
+    cs_ctr = round64(1024 + wgs) if w.has("amax") else 0
+    return {"wgs": wgs, "tiles_m": tiles_m, "tiles_n": tiles_n, "cs_ctr": cs_ctr,
+            "cs_part": round64(cs_ctr + tiles_n * 16)}
+
+
+def assert_counters_zero(w, prob, what=""):
+    """Every ticket counter the plan uses is back at zero (partials and slots may stay)."""
+    if not (w.has("amax") or w.has("col_sum")):
+        assert prob.plan.workspace is None, f"{what}: a workspace without AMAX or COL_SUM"
+        return
+    ws = prob.plan.workspace.view(torch.int32)
+    lay = workspace_words(w, prob)
+    if w.has("amax"):
+        assert int(ws[:1024].count_nonzero()) == 0, f"{what}: AMAX counters"
+    if w.has("col_sum"):
+        ctr = ws[lay["cs_ctr"]: lay["cs_ctr"] + lay["tiles_n"] * 16]
+        assert ctr.numel() == lay["tiles_n"] * 16
+        assert int(ctr.count_nonzero()) == 0, f"{what}: column-tile counters"
+
+
 @pytest.mark.parametrize("tile", SINGLE_TILES, ids=[TILE_NAMES[t] for t in SINGLE_TILES])
 @pytest.mark.parametrize("name", ["c1", "c2", "c4", "c5"])
 def test_ragged_nk_every_tile(name, tile):
@@ -297,14 +331,49 @@ def test_full_workload_sensitive(name):
     compare(w, inp, gpu_run(w, inp), f"{name} full sensitive")
 
 
+def test_nan_bias_gives_the_fp8_nan_code_and_a_nan_amax():
+    """A NaN in the epilogue's input reaches the output as the OCP e4m3 NaN code 0x7F (the
+    oracle's encoder) rather than a saturated +-448, and makes AMAX a NaN."""
+    w = workloads.WORKLOADS["c5"].with_shape(M=300, N=264, K=256)
+    inp = workloads.generate(w)
+    bias = inp["bias"].copy()
+    bias[7] = 0x7FC0                        # quiet NaN
+    bias[200] = 0xFFC0                      # NaN with the sign bit set
+    inp = {**inp, "bias": bias}
+    prob = gpu_run(w, inp)
+    ref = oracle.run_workload(w, inp)
+    codes = prob.y_host_bits()
+    nan = np.isnan(ref.y)
+    assert nan[..., 7].all() and nan[..., 200].all() and int(nan.sum()) == 2 * w.M
+    assert (ref.codes[nan] == 0x7F).all()
+    assert (codes[nan] == 0x7F).all(), np.unique(codes[nan])
+    check_fp8(codes[~nan], ref.codes[~nan], "finite outputs beside the NaN columns")
+    assert np.isnan(ref.amax) and np.isnan(prob.amax_host())
+
+
+def test_nan_residual_stays_nan_in_bf16():
+    """A NaN residual element gives a NaN output element (bf16) and nothing else changes."""
+    w = workloads.WORKLOADS["c4"].with_shape(M=300, N=264, K=256)
+    inp = workloads.generate(w)
+    r = inp["R"].copy()
+    r[0, 17, 33] = 0x7FC0
+    inp = {**inp, "R": r}
+    prob = gpu_run(w, inp)
+    ref = oracle.run_workload(w, inp)
+    y = prob.y_host_bits()
+    nan = np.isnan(ref.y)
+    assert int(nan.sum()) == 1 and nan[0, 17, 33]
+    assert np.isnan(oracle.decode_bf16(y[nan])).all()
+    check_bf16(y[~nan], ref.y[~nan], "finite outputs beside the NaN")
+
+
 def test_amax_workspace_is_left_zeroed_and_checked():
     w = workloads.WORKLOADS["c2"].with_shape(batch=2, M=512, N=512, K=256)
     inp = workloads.generate(w)
     prob = gpu_run(w, inp)
     assert prob.plan.workspace is not None
-    tiles = ((512 + 255) // 256) ** 2 * 2 if "256x256" in prob.plan.describe() else None
-    if tiles is not None:
-        assert prob.plan.workspace.numel() == 4 * (1024 + tiles)
+    # nine counters (1024 words) plus one slot per workgroup of the tile the plan chose
+    assert prob.plan.workspace.numel() == 4 * (1024 + workspace_words(w, prob)["wgs"])
     # the ticket counters (first 4 KiB) are zero again after the run; slots hold partial maxima
     assert int(prob.plan.workspace[:4096].count_nonzero()) == 0
     ref = oracle.run_workload(w, inp)
@@ -358,14 +427,9 @@ def test_graph_replays_match_eager_runs(name):
         torch.cuda.synchronize()
         assert torch.equal(prob.Y, y_eager), f"replay {rep}"
         assert prob.amax_host() == a_eager, f"replay {rep}"
-        ws = prob.plan.workspace.view(torch.int32)
-        if cs_eager is None:
-            assert int(ws[:1024].count_nonzero()) == 0, f"replay {rep}"      # AMAX counters
-        else:
+        if cs_eager is not None:
             assert torch.equal(prob.col_sum, cs_eager), f"replay {rep}"      # bit-identical
-            bn = int(prob.plan.describe().split("tile=")[1].split("x")[1])   # the plan's tile width
-            tiles_n = (w.N + bn - 1) // bn
-            assert int(ws[: tiles_n * 16].count_nonzero()) == 0, f"replay {rep}"  # column-tile counters
+        assert_counters_zero(w, prob, f"replay {rep}")
         prob.run()                                  # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(prob.Y, y_eager)
@@ -403,23 +467,24 @@ def test_col_sum_of_the_pairwise_product(tile):
     compare(w, inp, gpu_run(w, inp, tile), f"pairwise col_sum tile {TILE_NAMES[tile]}")
 
 
-def test_col_sum_is_deterministic_and_leaves_the_workspace_zeroed():
-    w = dataclasses.replace(workloads.WORKLOADS["f2"]).with_shape(batch=2, M=1000, N=1032, K=512)
+@pytest.mark.parametrize("with_amax", [False, True], ids=["col_sum", "col_sum+amax"])
+def test_col_sum_is_deterministic_and_leaves_the_workspace_zeroed(with_amax):
+    w = workloads.WORKLOADS["f2"]
+    if with_amax:
+        w = dataclasses.replace(w, chain=w.chain + (("amax",),))
+    w = w.with_shape(batch=2, M=1000, N=1032, K=512)
     inp = workloads.generate(w)
     prob = gpu_run(w, inp)
     first = prob.col_sum.clone()
-    compare(w, inp, prob, "f2 batch 2")
+    amax_first = prob.amax_host()
+    compare(w, inp, prob, f"f2 batch 2{' + amax' if with_amax else ''}")
+    assert_counters_zero(w, prob, "first run")
     for _ in range(3):
         prob.run()
     torch.cuda.synchronize()
     assert torch.equal(prob.col_sum, first)          # fixed summation order: bit-identical
-    ws = prob.plan.workspace
-    assert int(ws.view(torch.int32)[:1024].count_nonzero()) == 0 or not w.has("amax")
-    # every column-tile counter is back at zero (the partial sums may stay)
-    tiles_n = (w.N + 255) // 256 if "256x256" in prob.plan.describe() else None
-    if tiles_n is not None:
-        ctr = ws.view(torch.int32)[: tiles_n * 16]
-        assert int(ctr.count_nonzero()) == 0
+    assert prob.amax_host() == amax_first
+    assert_counters_zero(w, prob, "after repeats")
 
 
 def test_col_sum_of_an_empty_problem_is_zero():
