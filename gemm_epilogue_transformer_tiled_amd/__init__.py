@@ -16,7 +16,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgemm_epilogue.so")
 
 # ---- enums (mirror include/gemm_epilogue.h) ----
-GE_OK, GE_ERR_INVALID_ARG, GE_ERR_UNSUPPORTED, GE_ERR_DEVICE, GE_ERR_HIP = range(5)
+GE_OK, GE_ERR_INVALID_ARG, GE_ERR_UNSUPPORTED, GE_ERR_DEVICE, GE_ERR_HIP, GE_ERR_SCRATCH = range(6)
+GE_NOALLOC_SCRATCH_BYTES = 4 << 20
 GE_DT_BF16, GE_DT_FP8_E4M3, GE_DT_FP32 = range(3)
 GE_ACT_NONE, GE_ACT_RELU, GE_ACT_GELU_TANH, GE_ACT_SILU = range(4)
 GE_LAYOUT_KN, GE_LAYOUT_NK = range(2)
@@ -68,8 +69,8 @@ class ge_args_t(ctypes.Structure):
 ge_handle_t = ctypes.c_void_p
 
 EXPORTED = ("gemm_epilogue_validate", "gemm_epilogue_create", "gemm_epilogue_workspace_size",
-            "gemm_epilogue_run", "gemm_epilogue_destroy", "gemm_epilogue_status_string",
-            "gemm_epilogue_describe", "gemm_epilogue_tile_info")
+            "gemm_epilogue_run", "gemm_epilogue_run_noalloc", "gemm_epilogue_destroy",
+            "gemm_epilogue_status_string", "gemm_epilogue_describe", "gemm_epilogue_tile_info")
 
 
 def _load() -> ctypes.CDLL:
@@ -91,6 +92,8 @@ def _load() -> ctypes.CDLL:
     lib.gemm_epilogue_workspace_size.restype = ctypes.c_int
     lib.gemm_epilogue_run.argtypes = [ge_handle_t, ctypes.POINTER(ge_args_t), ctypes.c_void_p]
     lib.gemm_epilogue_run.restype = ctypes.c_int
+    lib.gemm_epilogue_run_noalloc.argtypes = [ge_handle_t, ctypes.POINTER(ge_args_t), ctypes.c_void_p]
+    lib.gemm_epilogue_run_noalloc.restype = ctypes.c_int
     lib.gemm_epilogue_destroy.argtypes = [ge_handle_t]
     lib.gemm_epilogue_destroy.restype = None
     lib.gemm_epilogue_status_string.argtypes = [ctypes.c_int]
@@ -136,6 +139,11 @@ def gemm_epilogue_workspace_size(handle: int) -> int:
 
 def gemm_epilogue_run(handle: int, args: ge_args_t, stream: int = 0) -> int:
     return lib.gemm_epilogue_run(handle, ctypes.byref(args), stream)
+
+
+def gemm_epilogue_run_noalloc(handle: int, args: ge_args_t, stream: int = 0) -> int:
+    """gemm_epilogue_run with the library's static device scratch instead of args.workspace."""
+    return lib.gemm_epilogue_run_noalloc(handle, ctypes.byref(args), stream)
 
 
 def gemm_epilogue_destroy(handle: Optional[int]) -> None:

@@ -257,11 +257,15 @@ ge_status_t gemm_epilogue_workspace_size(ge_handle_t h, size_t* bytes) {
   return GE_OK;
 }
 
-ge_status_t gemm_epilogue_run(ge_handle_t h, const ge_args_t* a, void* stream) {
-  if (!h || !a) return GE_ERR_INVALID_ARG;
+namespace {
+
+bool empty_problem(const ge_desc_t& d) { return d.batch == 0 || d.M == 0 || d.N == 0; }
+
+// Every pointer the plan's chain needs is present and aligned, and the workspace is large
+// enough; nothing is enqueued before this passes.
+ge_status_t check_args(const ge_plan* h, const ge_args_t* a) {
   const ge_desc_t& d = h->desc;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const bool empty = d.batch == 0 || d.M == 0 || d.N == 0;
+  const bool empty = empty_problem(d);
   const uint32_t f = h->flags;
 
   if (f & ge::F_AMAX) {
@@ -286,6 +290,15 @@ ge_status_t gemm_epilogue_run(ge_handle_t h, const ge_args_t* a, void* stream) {
     if ((f & ge::F_RESIDUAL) && (!a->residual || !aligned(a->residual, 16))) return GE_ERR_INVALID_ARG;
     if ((f & ge::F_ACT_GRAD) && (!a->aux || !aligned(a->aux, 16))) return GE_ERR_INVALID_ARG;
   }
+
+  return GE_OK;
+}
+
+// Enqueues the plan's work (arguments already checked).
+ge_status_t enqueue(const ge_plan* h, const ge_args_t* a, hipStream_t s) {
+  const ge_desc_t& d = h->desc;
+  const bool empty = empty_problem(d);
+  const uint32_t f = h->flags;
 
   if (empty) {
     // nothing to reduce: AMAX of no outputs is 0
@@ -341,6 +354,45 @@ ge_status_t gemm_epilogue_run(ge_handle_t h, const ge_args_t* a, void* stream) {
   return GE_OK;
 }
 
+}  // namespace
+
+ge_status_t gemm_epilogue_run(ge_handle_t h, const ge_args_t* a, void* stream) {
+  if (!h || !a) return GE_ERR_INVALID_ARG;
+  const ge_status_t st = check_args(h, a);
+  if (st != GE_OK) return st;
+  return enqueue(h, a, reinterpret_cast<hipStream_t>(stream));
+}
+
+ge_status_t gemm_epilogue_run_noalloc(ge_handle_t h, const ge_args_t* a, void* stream) {
+  if (!h || !a) return GE_ERR_INVALID_ARG;
+  const ge_desc_t& d = h->desc;
+  const size_t need = workspace_bytes(h);
+  const bool uses_scratch = need > 0 && !empty_problem(d);
+  if (uses_scratch && need > GE_NOALLOC_SCRATCH_BYTES) return GE_ERR_SCRATCH;
+  ge_args_t b = *a;
+  b.workspace = nullptr;
+  b.workspace_bytes = 0;
+  if (uses_scratch) {
+    void* ptr = nullptr;
+    if (ge::noalloc_scratch(&ptr) != hipSuccess || !ptr) return GE_ERR_HIP;
+    b.workspace = ptr;
+    b.workspace_bytes = need;
+  }
+  const ge_status_t st = check_args(h, &b);
+  if (st != GE_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (uses_scratch) {
+    // the array keeps the previous call's contents, possibly another plan's partials where this
+    // plan keeps its counters: zero the counters (a kernel, not a memset node)
+    const int64_t wgs = h->tiles_m * h->tiles_n * d.batch;
+    const size_t words = ge::counter_words((h->flags & ge::F_AMAX) != 0, (h->flags & ge::F_COL_SUM) != 0, wgs,
+                                           h->tiles_n);
+    if (ge::launch_zero_words(static_cast<uint32_t*>(b.workspace), (int64_t)words, s) != hipSuccess)
+      return GE_ERR_HIP;
+  }
+  return enqueue(h, &b, s);
+}
+
 void gemm_epilogue_destroy(ge_handle_t h) { delete h; }
 
 const char* gemm_epilogue_status_string(ge_status_t s) {
@@ -350,6 +402,7 @@ const char* gemm_epilogue_status_string(ge_status_t s) {
     case GE_ERR_UNSUPPORTED: return "GE_ERR_UNSUPPORTED: outside the supported set";
     case GE_ERR_DEVICE: return "GE_ERR_DEVICE: no gfx950 device is current";
     case GE_ERR_HIP: return "GE_ERR_HIP: a HIP call or kernel launch failed";
+    case GE_ERR_SCRATCH: return "GE_ERR_SCRATCH: the plan needs more scratch than GE_NOALLOC_SCRATCH_BYTES";
     default: return "unknown status";
   }
 }

@@ -111,5 +111,15 @@ inline size_t colsum_part_word(bool amax, int64_t workgroups, int64_t tiles_n) {
   return round64(colsum_ctr_word(amax, workgroups) + (size_t)tiles_n * kColSumCtrStride);
 }   // up to this many workgroups take one ticket each on the top counter
 inline size_t amax_workspace_bytes(int64_t workgroups) { return 4 * ((size_t)kAmaxSlot0 + (size_t)workgroups); }
+// Leading words of the workspace that hold ticket counters (everything before the COL_SUM
+// partials, or the AMAX counters alone): what must be zero when a kernel starts.
+inline size_t counter_words(bool amax, bool colsum, int64_t workgroups, int64_t tiles_n) {
+  if (colsum) return colsum_part_word(amax, workgroups, tiles_n);
+  return amax ? (size_t)kAmaxSlot0 : 0;
+}
+
+// Device address of the static scratch array behind gemm_epilogue_run_noalloc on the current
+// device (looked up once per device).
+hipError_t noalloc_scratch(void** out);
 
 }  // namespace ge

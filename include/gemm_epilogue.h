@@ -110,8 +110,13 @@ typedef enum {
   GE_ERR_INVALID_ARG = 1,   /* null pointer, negative size, bad stride, bad op order */
   GE_ERR_UNSUPPORTED = 2,   /* well-formed but outside the supported set */
   GE_ERR_DEVICE = 3,        /* no HIP device, or the current device is not gfx950 */
-  GE_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+  GE_ERR_HIP = 4,           /* a HIP runtime call or kernel launch failed */
+  GE_ERR_SCRATCH = 5        /* gemm_epilogue_run_noalloc: the plan needs more scratch than
+                               GE_NOALLOC_SCRATCH_BYTES */
 } ge_status_t;
+
+/* Size of the static device scratch behind gemm_epilogue_run_noalloc (per GPU). */
+#define GE_NOALLOC_SCRATCH_BYTES (4u << 20)
 
 typedef enum { GE_DT_BF16 = 0, GE_DT_FP8_E4M3 = 1, GE_DT_FP32 = 2 } ge_dtype_t;
 
@@ -257,6 +262,25 @@ ge_status_t gemm_epilogue_workspace_size(ge_handle_t handle, size_t* bytes);
  * empty problem (batch, M or N zero) launches only a one-thread kernel that writes *amax = 0
  * (and, with COL_SUM, a kernel that zeroes col_sum). */
 ge_status_t gemm_epilogue_run(ge_handle_t handle, const ge_args_t* args, void* stream);
+
+/* For callers that cannot allocate device memory -- code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc: gemm_epilogue_run without a caller-given
+ * workspace.  Same plan, same kernels, same results as gemm_epilogue_run; args->workspace and
+ * args->workspace_bytes are ignored.  The AMAX / COL_SUM scratch comes from a static device
+ * array of GE_NOALLOC_SCRATCH_BYTES (4 MiB) that the library's code object holds on every GPU
+ * it runs on until the process ends; its device address is looked up once per device
+ * (hipGetSymbolAddress, on the first call made with that device current).  Each call first
+ * enqueues a small kernel that zeroes the ticket counters the plan uses (the array keeps the
+ * previous call's contents), then the fused kernel: two launches on `stream`, no hipMalloc,
+ * hipFree, memset node or other allocating call.  Chains without AMAX and COL_SUM use no
+ * scratch and enqueue the fused kernel alone.
+ * Returns GE_ERR_SCRATCH, enqueueing nothing, when gemm_epilogue_workspace_size exceeds
+ * GE_NOALLOC_SCRATCH_BYTES (e.g. COL_SUM over more than about a million row-tile x column
+ * partials); otherwise the statuses of gemm_epilogue_run, plus GE_ERR_HIP when the scratch
+ * address cannot be looked up.
+ * RACE: every call on one GPU shares that GPU's array, so calls that overlap in time on one
+ * GPU (two streams, two host threads) corrupt each other's AMAX and COL_SUM; order them. */
+ge_status_t gemm_epilogue_run_noalloc(ge_handle_t handle, const ge_args_t* args, void* stream);
 
 /* Frees the plan's host memory (the end of a plan's life in the cuDNN tutorial's plan-reuse
  * model, closing paragraphs: a plan is built once and executed many times).  NULL is a no-op.  Work

@@ -136,8 +136,9 @@ def test_null_arguments_and_status_strings():
     assert ge.lib.gemm_epilogue_validate(None) == ge.GE_ERR_INVALID_ARG
     assert ge.lib.gemm_epilogue_create(None, None) == ge.GE_ERR_INVALID_ARG
     assert ge.lib.gemm_epilogue_run(None, None, None) == ge.GE_ERR_INVALID_ARG
+    assert ge.lib.gemm_epilogue_run_noalloc(None, None, None) == ge.GE_ERR_INVALID_ARG
     ge.gemm_epilogue_destroy(None)
-    for s in range(5):
+    for s in range(6):
         assert ge.gemm_epilogue_status_string(s).startswith("GE_")
     assert "unknown" in ge.gemm_epilogue_status_string(77)
 
