@@ -65,10 +65,16 @@ const ge_op_t* find_op(const ge_desc_t* d, int kind) {
   return nullptr;
 }
 
-// Bytes from a matrix's base to one past its last element: (rows-1)*ld + cols.
-int64_t extent_elems(int64_t rows, int64_t cols, int64_t ld) {
+// Bytes from a matrix's base to one past its last element: ((rows-1)*ld + cols) * esize,
+// saturating at INT64_MAX (every such extent is then rejected): descriptors come from callers,
+// so leading dimensions may be anything non-negative.
+int64_t extent_bytes(int64_t rows, int64_t cols, int64_t ld, int64_t esize) {
   if (rows <= 0 || cols <= 0) return 0;
-  return (rows - 1) * ld + cols;
+  int64_t e;
+  if (__builtin_mul_overflow(rows - 1, ld, &e) || __builtin_add_overflow(e, cols, &e) ||
+      __builtin_mul_overflow(e, esize, &e))
+    return INT64_MAX;
+  return e;
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -103,6 +109,8 @@ ge_status_t gemm_epilogue_validate(const ge_desc_t* d) {
   if (d->b_layout != GE_LAYOUT_KN && d->b_layout != GE_LAYOUT_NK) return GE_ERR_INVALID_ARG;
   if (d->tile < 0 || d->tile > GE_TILE_COUNT) return GE_ERR_INVALID_ARG;
   const bool bnk = d->b_layout == GE_LAYOUT_NK;
+  // sizes beyond 32 bits are outside the supported set; past this point M + 256 etc. cannot overflow
+  const bool huge = d->M > INT32_MAX || d->N > INT32_MAX || d->K > INT32_MAX || d->batch > INT32_MAX;
 
   // op chain: known kinds, canonical order, each at most once, exclusive pairs
   int last_rank = -1;
@@ -155,7 +163,7 @@ ge_status_t gemm_epilogue_validate(const ge_desc_t* d) {
   if (grad && (d->ldz < 0 || d->stride_z < 0)) return GE_ERR_INVALID_ARG;
   if (grad && d->M > 0 && d->ldz < d->N) return GE_ERR_INVALID_ARG;
   if (grad && (d->ldz % 8 || d->stride_z % 8)) return GE_ERR_UNSUPPORTED;
-  if (grad && extent_elems(d->M + 256, d->N, d->ldz) * 2 > kMaxExtent) return GE_ERR_UNSUPPORTED;
+  if (grad && !huge && extent_bytes(d->M + 256, d->N, d->ldz, 2) > kMaxExtent) return GE_ERR_UNSUPPORTED;
   if (d->M > 0 && d->lda < d->K) return GE_ERR_INVALID_ARG;
   if (!bnk && d->K > 0 && d->ldb < d->N) return GE_ERR_INVALID_ARG;
   if (bnk && d->N > 0 && d->ldb < d->K) return GE_ERR_INVALID_ARG;
@@ -164,13 +172,12 @@ ge_status_t gemm_epilogue_validate(const ge_desc_t* d) {
   if (d->batch > 1 && d->stride_y == 0 && d->M > 0 && d->N > 0) return GE_ERR_INVALID_ARG;  // batches would race
 
   // supported set: 16-byte vector access everywhere (16 fp8 operand values per 16 bytes)
+  if (huge) return GE_ERR_UNSUPPORTED;
   if (d->N % 8 || d->K % 8) return GE_ERR_UNSUPPORTED;
   if (f8in && (d->K % 16 || d->lda % 16 || d->ldb % 16 || d->stride_a % 16 || d->stride_b % 16))
     return GE_ERR_UNSUPPORTED;
   if (d->lda % 8 || d->ldb % 8 || d->ldy % 8 || (res && d->ldr % 8)) return GE_ERR_UNSUPPORTED;
   if (d->stride_a % 8 || d->stride_b % 8 || d->stride_y % 8 || (res && d->stride_r % 8))
-    return GE_ERR_UNSUPPORTED;
-  if (d->M > INT32_MAX || d->N > INT32_MAX || d->K > INT32_MAX || d->batch > INT32_MAX)
     return GE_ERR_UNSUPPORTED;
   const int64_t esize = d->y_type == GE_DT_FP8_E4M3 ? 1 : 2;
   // Kernels address each operand with 32-bit byte offsets from a per-tile base and mark
@@ -178,13 +185,15 @@ ge_status_t gemm_epilogue_validate(const ge_desc_t* d) {
   // K step past the end included) must therefore stay below 2^31.
   // (operand element size ae; one A slot spans slot_k K values)
   const int64_t ae = f8in ? 1 : 2, slot_k = f8in ? 128 : 64;
-  if (extent_elems(d->M + 256, d->K + slot_k, d->lda) * ae > kMaxExtent) return GE_ERR_UNSUPPORTED;
-  if (!bnk && extent_elems(d->K + 128, d->N, d->ldb) * 2 > kMaxExtent) return GE_ERR_UNSUPPORTED;
-  if (bnk && extent_elems(d->N + 256, d->K + slot_k, d->ldb) * ae > kMaxExtent) return GE_ERR_UNSUPPORTED;
-  if (extent_elems(d->M + 256, d->N, d->ldy) * esize > kMaxExtent) return GE_ERR_UNSUPPORTED;
-  if (res && extent_elems(d->M + 256, d->N, d->ldr) * 2 > kMaxExtent) return GE_ERR_UNSUPPORTED;
-  // grid: one workgroup per 64x64 tile at most
-  if (ceil_div(d->M, 64) * ceil_div(d->N, 64) * d->batch > INT32_MAX) return GE_ERR_UNSUPPORTED;
+  if (extent_bytes(d->M + 256, d->K + slot_k, d->lda, ae) > kMaxExtent) return GE_ERR_UNSUPPORTED;
+  if (!bnk && extent_bytes(d->K + 128, d->N, d->ldb, 2) > kMaxExtent) return GE_ERR_UNSUPPORTED;
+  if (bnk && extent_bytes(d->N + 256, d->K + slot_k, d->ldb, ae) > kMaxExtent) return GE_ERR_UNSUPPORTED;
+  if (extent_bytes(d->M + 256, d->N, d->ldy, esize) > kMaxExtent) return GE_ERR_UNSUPPORTED;
+  if (res && extent_bytes(d->M + 256, d->N, d->ldr, 2) > kMaxExtent) return GE_ERR_UNSUPPORTED;
+  // grid: one workgroup per 64x64 tile at most (M, N, batch < 2^31 here: the product of the
+  // first two fits, the third factor is checked by division)
+  const int64_t tiles64 = ceil_div(d->M, 64) * ceil_div(d->N, 64);
+  if (tiles64 > 0 && d->batch > INT32_MAX / tiles64) return GE_ERR_UNSUPPORTED;
   return GE_OK;
 }
 

@@ -66,19 +66,14 @@ TileInfo tile_info(TileKind kind);
 // Per-tile instance sets (ge_tile_*.hip).
 hipError_t launch_tile_256x256_kn(int act, bool fp8_out, const Params& p, hipStream_t stream);
 hipError_t launch_tile_256x256_nk(int act, bool fp8_out, const Params& p, hipStream_t stream);
-TileInfo tile_info_256x256();
 hipError_t launch_tile_256x128_pair_kn(int act, bool fp8_out, const Params& p, hipStream_t stream);
 hipError_t launch_tile_256x128_pair_nk(int act, bool fp8_out, const Params& p, hipStream_t stream);
-TileInfo tile_info_256x128_pair();
 hipError_t launch_tile_128x128_kn(int act, bool fp8_out, const Params& p, hipStream_t stream);
 hipError_t launch_tile_128x128_nk(int act, bool fp8_out, const Params& p, hipStream_t stream);
-TileInfo tile_info_128x128();
 hipError_t launch_tile_64x64_kn(int act, bool fp8_out, const Params& p, hipStream_t stream);
 hipError_t launch_tile_64x64_nk(int act, bool fp8_out, const Params& p, hipStream_t stream);
-TileInfo tile_info_64x64();
 hipError_t launch_tile_128x128_pair_kn(int act, bool fp8_out, const Params& p, hipStream_t stream);
 hipError_t launch_tile_128x128_pair_nk(int act, bool fp8_out, const Params& p, hipStream_t stream);
-TileInfo tile_info_128x128_pair();
 // fp8-e4m3 operands, B laid out [N][K]
 hipError_t launch_tile_256x256_f8(int act, bool fp8_out, const Params& p, hipStream_t stream);
 hipError_t launch_tile_256x128_pair_f8(int act, bool fp8_out, const Params& p, hipStream_t stream);

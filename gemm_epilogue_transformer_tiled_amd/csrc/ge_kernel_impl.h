@@ -39,6 +39,7 @@
 #include <utility>
 
 #include "ge_internal.h"
+#include "ge_tiles.h"
 
 namespace ge {
 namespace {
@@ -66,53 +67,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kGeluC = -2.0f * 1.4426950408889634f * 0.7978845608028654f;
 constexpr float kGeluCubic = 0.044715f;
 
-template <int BM_, int BN_, bool PAIR_, int WPE_>
-struct Tile {
-  static constexpr int BM = BM_, BN = BN_;
-  static constexpr bool PAIR = PAIR_;
-  static constexpr int WPE = WPE_;                   // waves per SIMD the kernel is built for
-  static constexpr int WAVES = 4, NT = 256;          // 2 x 2 waves
-  static constexpr int WM = BM / 2, WN = BN / 2;     // per-wave output tile
-  static constexpr int FM = WM / 32, FN = WN / 32;   // 32x32 MFMA blocks per wave
-  static constexpr int NB = PAIR ? 2 : 1;            // B operands
-  // Pipeline: K steps of BK = 32.  B tiles ([BK][BN] per operand) go through a ring of
-  // NS = 4 LDS stages; A tiles are staged two steps at a time ([BM][64], 128-byte rows, so
-  // every fetched cache line is used whole) in two slots.  The tiles of step k+2 are
-  // fetched while step k computes.
-  static constexpr int BK = 32, NS = 4, PD = 2;
-  static constexpr int GROUPS = BK / 16;             // 16-deep MFMA groups per step
-  static constexpr int A_ROWB = 128;                 // one A row: 64 K values
-  static constexpr int A_CHUNKS = A_ROWB / 16;
-  static constexpr int A_SLOT = BM * A_ROWB;         // two steps of A
-  static constexpr int B_ROWB = BN * 2;              // bytes per staged B row
-  static constexpr int B_CHUNKS = B_ROWB / 16;       // 16-byte chunks per B row
-  static constexpr int B_BYTES = BK * B_ROWB;        // one B operand, one step
-  static constexpr int B_STAGE = NB * B_BYTES;
-  // Epilogue: each wave stages a 32-row block of fp32 rows (WN + 4 floats) in LDS; two
-  // waves share an A slot, which is sized to hold them.
-  static constexpr int EP_LD = WN + 4;
-  static constexpr int EP_WAVE_BYTES = 32 * EP_LD * 4;
-  static constexpr int A_ALLOC = A_SLOT > 2 * EP_WAVE_BYTES ? A_SLOT : 2 * EP_WAVE_BYTES;
-  static constexpr int LDS = 2 * A_ALLOC + NS * B_STAGE;
-  // Direct global->LDS loads: one instruction moves 1 KB (64 lanes x 16 bytes).
-  static constexpr int A_ROWS_PER_LOAD = 1024 / A_ROWB;
-  static constexpr int A_LOADS = A_SLOT / 1024 / WAVES;            // per wave per A slot
-  static constexpr int B_ROWS_PER_LOAD = 1024 / B_ROWB;
-  static constexpr int B_LOADS_PER_OP = BK / B_ROWS_PER_LOAD;     // per operand per step
-  static constexpr int B_LOADS = NB * B_LOADS_PER_OP / WAVES;     // per wave per step
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile must split into 2x2 waves of 32x32 blocks");
-  static_assert(A_LOADS >= 1 && A_SLOT % (1024 * WAVES) == 0, "A loads must divide over the waves");
-  static_assert(B_LOADS >= 1 && (NB * B_LOADS_PER_OP) % WAVES == 0, "B loads must divide over the waves");
-  static_assert(B_LOADS_PER_OP % B_LOADS == 0 || B_LOADS % B_LOADS_PER_OP == 0, "one operand per load");
-  static_assert(A_LOADS + B_LOADS < 64, "vmcnt range");
-  static_assert(LDS + 1024 + 64 <= 160 * 1024, "LDS budget of one workgroup");
-};
-
-using T256 = Tile<256, 256, false, 1>;
-using T256P = Tile<256, 128, true, 1>;
-using T128 = Tile<128, 128, false, 2>;
-using T64 = Tile<64, 64, false, 2>;
-using T128P = Tile<128, 128, true, 1>;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   // raw buffer: stride 0, num_records = extent in bytes (< 2^31, checked on the host)
@@ -1056,10 +1010,6 @@ void fused_gemm_epilogue(Params p) {
   }
 }
 
-template <class T>
-constexpr TileInfo info_of() {
-  return TileInfo{T::BM, T::BN, T::NT, T::WAVES, T::PAIR, T::LDS};
-}
 
 template <class T, int ACT, bool GRAD, bool FP8, bool ROWSTAT, bool BNK>
 void launch_k(const Params& p, hipStream_t s, unsigned grid) {

@@ -18,17 +18,6 @@ __global__ void amax_zero_kernel(uint32_t* amax) {
 
 }  // namespace
 
-TileInfo tile_info(TileKind kind) {
-  switch (kind) {
-    case TILE_256x256: return tile_info_256x256();
-    case TILE_256x128_PAIR: return tile_info_256x128_pair();
-    case TILE_128x128: return tile_info_128x128();
-    case TILE_64x64: return tile_info_64x64();
-    case TILE_128x128_PAIR: return tile_info_128x128_pair();
-    default: return TileInfo{0, 0, 0, 0, false, 0};
-  }
-}
-
 hipError_t launch_fused(TileKind kind, int act, bool fp8_out, const Params& p, hipStream_t stream) {
   if (p.flags & F_IN_FP8) {
     switch (kind) {

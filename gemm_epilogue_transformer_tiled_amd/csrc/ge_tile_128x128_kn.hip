@@ -7,6 +7,4 @@ hipError_t launch_tile_128x128_kn(int act, bool fp8_out, const Params& p, hipStr
   return launch_tile<T128, false>(act, fp8_out, p, stream);
 }
 
-TileInfo tile_info_128x128() { return info_of<T128>(); }
-
 }  // namespace ge

@@ -7,6 +7,4 @@ hipError_t launch_tile_128x128_pair_kn(int act, bool fp8_out, const Params& p, h
   return launch_tile<T128P, false>(act, fp8_out, p, stream);
 }
 
-TileInfo tile_info_128x128_pair() { return info_of<T128P>(); }
-
 }  // namespace ge

@@ -7,6 +7,4 @@ hipError_t launch_tile_256x128_pair_kn(int act, bool fp8_out, const Params& p, h
   return launch_tile<T256P, false>(act, fp8_out, p, stream);
 }
 
-TileInfo tile_info_256x128_pair() { return info_of<T256P>(); }
-
 }  // namespace ge

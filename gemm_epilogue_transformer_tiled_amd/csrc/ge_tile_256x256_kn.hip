@@ -7,6 +7,4 @@ hipError_t launch_tile_256x256_kn(int act, bool fp8_out, const Params& p, hipStr
   return launch_tile<T256, false>(act, fp8_out, p, stream);
 }
 
-TileInfo tile_info_256x256() { return info_of<T256>(); }
-
 }  // namespace ge

@@ -7,6 +7,4 @@ hipError_t launch_tile_64x64_kn(int act, bool fp8_out, const Params& p, hipStrea
   return launch_tile<T64, false>(act, fp8_out, p, stream);
 }
 
-TileInfo tile_info_64x64() { return info_of<T64>(); }
-
 }  // namespace ge
