@@ -12,6 +12,7 @@ import ctypes
 import os
 from typing import Dict, List, Optional, Tuple
 
+import numpy as np
 import torch
 
 from . import GE_DT_BF16, GE_DT_FP8_E4M3, GE_LAYOUT_KN, GE_LAYOUT_NK, Plan, make_args, make_desc, make_ops
@@ -23,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libge_baselines.so")
 EXPORTED = ("ge_unfused_scale", "ge_unfused_bias_col", "ge_unfused_act", "ge_unfused_act_mul",
             "ge_unfused_row_rms", "ge_unfused_row_scale", "ge_unfused_add", "ge_unfused_amax",
             "ge_unfused_quant_fp8", "ge_unfused_act_grad", "ge_unfused_col_sum", "ge_probe_mfma",
-            "ge_probe_copy")
+            "ge_probe_mfma_f8", "ge_probe_copy")
 ACTS = {"none": 0, "relu": 1, "gelu_tanh": 2, "silu": 3}
 
 _p, _i64, _i, _f = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
@@ -40,6 +41,7 @@ _SIGS = {
     "ge_unfused_act_grad": [_p, _p, _p, _i64, _i, _p],
     "ge_unfused_col_sum": [_p, _p, _i64, _i64, _p],
     "ge_probe_mfma": [_p, _i, _i, _p],
+    "ge_probe_mfma_f8": [_p, _p, _p, _p, _i, _p],
     "ge_probe_copy": [_p, _p, _i64, _p],
 }
 
@@ -218,6 +220,22 @@ def probe_mfma(workgroups: int = 1024, iters: int = 4096) -> Dict:
     flops = workgroups * 4 * 16 * iters * 32768.0
     return {"tflops": round(flops / best / 1e9, 1), "ms": round(best, 4),
             "implied_clock_ghz": round(flops / (best * 1e-3) / (256 * 4096) / 1e9, 3)}
+
+
+def mfma_f8(src0: np.ndarray, src1: np.ndarray, c: np.ndarray) -> np.ndarray:
+    """One v_mfma_f32_32x32x64_f8f6f4 per wave: src0, src1 uint8 e4m3 codes [waves, 64, 32]
+    (lane, register byte), c float32 [waves, 64, 16] (lane, accumulator register); returns the
+    float32 result registers [waves, 64, 16]."""
+    waves = src0.shape[0]
+    assert src0.shape == (waves, 64, 32) and src1.shape == (waves, 64, 32) and c.shape == (waves, 64, 16)
+    dev = "cuda"
+    t0 = torch.from_numpy(np.ascontiguousarray(src0, dtype=np.uint8)).to(dev)
+    t1 = torch.from_numpy(np.ascontiguousarray(src1, dtype=np.uint8)).to(dev)
+    tc = torch.from_numpy(np.ascontiguousarray(c, dtype=np.float32)).to(dev)
+    td = torch.empty_like(tc)
+    call("ge_probe_mfma_f8", t0.data_ptr(), t1.data_ptr(), tc.data_ptr(), td.data_ptr(), waves, _stream())
+    torch.cuda.synchronize()
+    return td.cpu().numpy()
 
 
 def probe_copy(mib: int = 1024) -> Dict:

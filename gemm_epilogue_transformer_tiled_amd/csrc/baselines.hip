@@ -264,6 +264,18 @@ __global__ __launch_bounds__(256) void mfma_probe(float* sink, int iters) {
   sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// One fp8 matrix-core instruction per wave on caller-given register contents: lane l of wave w
+// takes 32 bytes of e4m3 codes from src0 and from src1 at byte (64 w + l) * 32 and 16 fp32
+// accumulator values from c at float (64 w + l) * 16, runs v_mfma_f32_32x32x64_f8f6f4 (e4m3 for
+// both sources, no block scales) and writes the 16 result values to d at the same place.  This
+// shows how the instruction sums its 64 products into the accumulator.
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+__global__ __launch_bounds__(64) void mfma_f8_probe(const i32x8_t* __restrict__ s0, const i32x8_t* __restrict__ s1,
+                                                    const f32x16_t* __restrict__ c, f32x16_t* __restrict__ d) {
+  const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  d[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(s0[i], s1[i], c[i], 0, 0, 0, 0, 0, 0);
+}
+
 __global__ __launch_bounds__(kThreads) void copy_kernel(const u32x4_t* __restrict__ src, u32x4_t* __restrict__ dst,
                                                         int64_t nv) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -359,6 +371,15 @@ int ge_unfused_quant_fp8(const uint16_t* x, uint8_t* y, int64_t n, float scale, 
 int ge_probe_mfma(float* sink, int workgroups, int iters, void* stream) {
   if (!sink || workgroups <= 0 || iters < 0) return 1;
   hipLaunchKernelGGL(mfma_probe, dim3((unsigned)workgroups), dim3(256), 0, (hipStream_t)stream, sink, iters);
+  return launched();
+}
+
+int ge_probe_mfma_f8(const uint8_t* src0, const uint8_t* src1, const float* c, float* d, int waves, void* stream) {
+  if (waves < 0 || (waves > 0 && (!src0 || !src1 || !c || !d))) return 1;
+  if ((((uintptr_t)src0) | ((uintptr_t)src1) | ((uintptr_t)c) | ((uintptr_t)d)) & 63u) return 1;
+  if (waves == 0) return 0;
+  hipLaunchKernelGGL(mfma_f8_probe, dim3((unsigned)waves), dim3(64), 0, (hipStream_t)stream, (const i32x8_t*)src0,
+                     (const i32x8_t*)src1, (const f32x16_t*)c, (f32x16_t*)d);
   return launched();
 }
 

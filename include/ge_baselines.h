@@ -78,6 +78,14 @@ int ge_unfused_quant_fp8(const uint16_t* x, uint8_t* y, int64_t n, float scale, 
  * workgroups * 4 * 16 * iters * 32768. */
 int ge_probe_mfma(float* sink, int workgroups, int iters, void* stream);
 
+/* fp8 matrix-core probe: `waves` single-wave workgroups, each running ONE
+ * v_mfma_f32_32x32x64_f8f6f4 with e4m3 codes in both sources and no block scales on its own
+ * register contents.  Lane l of wave w reads 32 bytes of src0 and of src1 at byte offset
+ * (64*w + l)*32 and 16 fp32 accumulator values of c at float offset (64*w + l)*16, and writes its
+ * 16 result values to d at the same offsets.  All pointers 64-byte aligned.  Used to measure
+ * how the instruction sums its 64 products (the accuracy of fp8-operand GEMMs). */
+int ge_probe_mfma_f8(const uint8_t* src0, const uint8_t* src1, const float* c, float* d, int waves, void* stream);
+
 /* Streaming copy of `bytes` (a multiple of 16, 16-byte aligned pointers): reads and writes each
  * byte once. */
 int ge_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);

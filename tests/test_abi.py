@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 def test_baselines_library_exports_every_declared_symbol():
     from gemm_epilogue_transformer_tiled_amd import baselines
     names = _declared_symbols(r"ge_(?:unfused|probe)_\w+")
-    assert len(names) == 13
+    assert len(names) == 14
     lib = ctypes.CDLL(baselines.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n

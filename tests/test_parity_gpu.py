@@ -545,7 +545,7 @@ def test_largest_supported_operand_extent(in_dtype):
     ref = oracle.run_workload(w.with_shape(M=len(rows)), {**small, "A": a_bits[None]})
     y = Y[0, torch.from_numpy(rows).cuda()].cpu().view(torch.int16).numpy().view(np.uint16)
     # fp8 operands: allow the fp8 instruction's accumulation error (ReLU's slope is 1)
-    allow = fp8_acc_bound(a_bits[None], small["B"], w.alpha, K) if fp8 else None
+    allow = fp8_acc_bound(a_bits[None], small["B"], w.alpha) if fp8 else None
     check_bf16(y[None], ref.y, f"largest extent {in_dtype}", allow=allow)
 
 
