@@ -21,7 +21,8 @@ GE_NOALLOC_SCRATCH_BYTES = 4 << 20
 GE_DT_BF16, GE_DT_FP8_E4M3, GE_DT_FP32 = range(3)
 GE_ACT_NONE, GE_ACT_RELU, GE_ACT_GELU_TANH, GE_ACT_SILU = range(4)
 GE_LAYOUT_KN, GE_LAYOUT_NK = range(2)
-GE_TILE_256x256, GE_TILE_256x128_PAIR, GE_TILE_128x128, GE_TILE_64x64, GE_TILE_128x128_PAIR, GE_TILE_COUNT = range(6)
+(GE_TILE_256x256, GE_TILE_256x128_PAIR, GE_TILE_128x128, GE_TILE_64x64, GE_TILE_128x128_PAIR,
+ GE_TILE_256x256_2W, GE_TILE_256x128_PAIR_2W, GE_TILE_COUNT) = range(8)
 (GE_OP_SCALE, GE_OP_ROW_RMS, GE_OP_ROW_SCALE, GE_OP_BIAS_COL, GE_OP_ACT, GE_OP_PAIRWISE_ACT_MUL,
  GE_OP_RESIDUAL, GE_OP_AMAX, GE_OP_QUANT_FP8, GE_OP_ACT_GRAD, GE_OP_COL_SUM) = range(11)
 GE_MAX_OPS = 8

@@ -31,7 +31,8 @@ namespace {
 
 static_assert(GE_TILE_256x256 == ge::TILE_256x256 && GE_TILE_256x128_PAIR == ge::TILE_256x128_PAIR &&
                   GE_TILE_128x128 == ge::TILE_128x128 && GE_TILE_64x64 == ge::TILE_64x64 &&
-                  GE_TILE_128x128_PAIR == ge::TILE_128x128_PAIR && GE_TILE_COUNT == ge::TILE_KIND_COUNT,
+                  GE_TILE_128x128_PAIR == ge::TILE_128x128_PAIR && GE_TILE_256x256_2W == ge::TILE_256x256_2W &&
+                  GE_TILE_256x128_PAIR_2W == ge::TILE_256x128_PAIR_2W && GE_TILE_COUNT == ge::TILE_KIND_COUNT,
               "public tile ids mirror the kernel instances");
 
 constexpr int64_t kMaxExtent = 0x7FFFFFF0;   // buffer extents are 31-bit byte counts
@@ -79,22 +80,39 @@ int64_t extent_bytes(int64_t rows, int64_t cols, int64_t ld, int64_t esize) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// The two-wave instances cover forward epilogues without the row statistic, on bf16 operands
+// with B given [K][N] and K a multiple of 64.
+bool two_wave_ok(const ge_desc_t* d);
+
 ge::TileKind pick_tile(const ge_desc_t* d, bool pair) {
   if (d->tile > 0) return (ge::TileKind)(d->tile - 1);        // validated: matches the chain
   const char* force = std::getenv("GE_FORCE_TILE");
   if (force && *force) {
     const int k = std::atoi(force);
-    if (k >= 0 && k < ge::TILE_KIND_COUNT && ge::tile_info((ge::TileKind)k).pair == pair)
+    if (k >= 0 && k < ge::TILE_KIND_COUNT && ge::tile_info((ge::TileKind)k).pair == pair &&
+        (!ge::two_wave_tile((ge::TileKind)k) || two_wave_ok(d)))
       return (ge::TileKind)k;
   }
   auto tiles = [&](int bm, int bn) { return ceil_div(d->M, bm) * ceil_div(d->N, bn) * d->batch; };
-  if (pair) return tiles(256, 128) >= 256 ? ge::TILE_256x128_PAIR : ge::TILE_128x128_PAIR;
-  if (tiles(256, 256) >= 256) return ge::TILE_256x256;
+  // the largest tile that still gives >= 256 workgroups; at 256 x 256 (256 x 128 pairwise) the
+  // two-wave instance where it applies (its matrix cores are fed by one wave while the other
+  // loads)
+  const bool tw = two_wave_ok(d);
+  if (pair) {
+    if (tiles(256, 128) < 256) return ge::TILE_128x128_PAIR;
+    return tw ? ge::TILE_256x128_PAIR_2W : ge::TILE_256x128_PAIR;
+  }
+  if (tiles(256, 256) >= 256) return tw ? ge::TILE_256x256_2W : ge::TILE_256x256;
   if (tiles(128, 128) >= 128) return ge::TILE_128x128;
   return ge::TILE_64x64;
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool two_wave_ok(const ge_desc_t* d) {
+  return d->b_layout == GE_LAYOUT_KN && d->a_type == GE_DT_BF16 && !has_op(d, GE_OP_ACT_GRAD) &&
+         !has_op(d, GE_OP_ROW_RMS) && d->K % 64 == 0;
+}
 
 }  // namespace
 
@@ -132,6 +150,7 @@ ge_status_t gemm_epilogue_validate(const ge_desc_t* d) {
   if (has_op(d, GE_OP_ROW_RMS) && d->K < 1) return GE_ERR_INVALID_ARG;
   // a requested instance must be a pairwise one exactly when the chain is pairwise
   if (d->tile > 0 && ge::tile_info((ge::TileKind)(d->tile - 1)).pair != pair) return GE_ERR_INVALID_ARG;
+  const bool two_wave_requested = d->tile > 0 && ge::two_wave_tile((ge::TileKind)(d->tile - 1));
 
   // dtypes: bf16 operands, or fp8-e4m3 operands with B given [N][K]
   auto known = [](int32_t t) { return t == GE_DT_BF16 || t == GE_DT_FP8_E4M3 || t == GE_DT_FP32; };
@@ -173,6 +192,7 @@ ge_status_t gemm_epilogue_validate(const ge_desc_t* d) {
 
   // supported set: 16-byte vector access everywhere (16 fp8 operand values per 16 bytes)
   if (huge) return GE_ERR_UNSUPPORTED;
+  if (two_wave_requested && !two_wave_ok(d)) return GE_ERR_UNSUPPORTED;
   if (d->N % 8 || d->K % 8) return GE_ERR_UNSUPPORTED;
   if (f8in && (d->K % 16 || d->lda % 16 || d->ldb % 16 || d->stride_a % 16 || d->stride_b % 16))
     return GE_ERR_UNSUPPORTED;
@@ -290,7 +310,7 @@ ge_status_t check_args(const ge_plan* h, const ge_args_t* a) {
     if (!a->Y || !aligned(a->Y, 16)) return GE_ERR_INVALID_ARG;
     if (d.K > 0) {
       if (!a->A || !a->B || !aligned(a->A, 16) || !aligned(a->B, 16)) return GE_ERR_INVALID_ARG;
-      if (h->tile == ge::TILE_256x128_PAIR || h->tile == ge::TILE_128x128_PAIR) {
+      if (ge::tile_info(h->tile).pair) {
         if (!a->B2 || !aligned(a->B2, 16)) return GE_ERR_INVALID_ARG;
       }
     }

@@ -22,15 +22,21 @@ enum : uint32_t {
 
 enum Act : int { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_TANH = 2, ACT_SILU = 3 };
 
-// Kernel instances (tile shapes).  Each is MI355X-specific: 4 waves of 64 lanes.
+// Kernel instances (tile shapes).  Each is MI355X-specific: 4 or 8 waves of 64 lanes.
 enum TileKind : int {
   TILE_256x256 = 0,      // 2x2 waves, 128x128 per wave
   TILE_256x128_PAIR = 1, // pairwise: two B operands, 2x2 waves, 128x64 x2 accumulators per wave
   TILE_128x128 = 2,      // 2x2 waves, 64x64 per wave
   TILE_64x64 = 3,        // 2x2 waves, 32x32 per wave
   TILE_128x128_PAIR = 4, // pairwise, 2x2 waves, 64x64 x2 per wave
-  TILE_KIND_COUNT = 5
+  TILE_256x256_2W = 5,   // two waves per SIMD: 2x4 waves, 128x64 per wave
+  TILE_256x128_PAIR_2W = 6, // two waves per SIMD, pairwise: 2x4 waves, 128x32 x2 per wave
+  TILE_KIND_COUNT = 7
 };
+
+// The two-wave instances exist for forward epilogues on bf16 operands with B given [K][N] and
+// K a multiple of 64.
+inline bool two_wave_tile(TileKind k) { return k == TILE_256x256_2W || k == TILE_256x128_PAIR_2W; }
 
 struct Params {
   const uint16_t* A;       // bf16 elements, or fp8 codes (bytes) with F_IN_FP8
@@ -74,6 +80,8 @@ hipError_t launch_tile_64x64_kn(int act, bool fp8_out, const Params& p, hipStrea
 hipError_t launch_tile_64x64_nk(int act, bool fp8_out, const Params& p, hipStream_t stream);
 hipError_t launch_tile_128x128_pair_kn(int act, bool fp8_out, const Params& p, hipStream_t stream);
 hipError_t launch_tile_128x128_pair_nk(int act, bool fp8_out, const Params& p, hipStream_t stream);
+hipError_t launch_tile_256x256w8_kn(int act, bool fp8_out, const Params& p, hipStream_t stream);
+hipError_t launch_tile_256x128w8_pair_kn(int act, bool fp8_out, const Params& p, hipStream_t stream);
 // fp8-e4m3 operands, B laid out [N][K]
 hipError_t launch_tile_256x256_f8(int act, bool fp8_out, const Params& p, hipStream_t stream);
 hipError_t launch_tile_256x128_pair_f8(int act, bool fp8_out, const Params& p, hipStream_t stream);

@@ -203,8 +203,11 @@ __device__ __forceinline__ void sched_group8() {
 // dequantisation factors of delayed scaling (1 / (scale_A * scale_B)) are the epilogue's
 // alpha; everything after the accumulator is shared with the bf16 path.
 template <class T, int ACT, bool GRAD, bool FP8, bool ROWSTAT, bool KMASK, bool BNK, bool F8IN = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(T::WPE, T::WPE)))
+__global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(T::WPE, T::WPE)))
 void fused_gemm_epilogue(Params p) {
+  constexpr bool PP = T::WAVES == 8;              // two waves per SIMD, alternating phases
+  static_assert(!PP || (!BNK && !F8IN && !GRAD && !KMASK && !ROWSTAT),
+                "the two-wave instances: B [K][N], bf16, K % 64 == 0, no row statistic");
   constexpr int ES = F8IN ? 1 : 2;                // bytes per operand element
   constexpr int BKE = F8IN ? 64 : T::BK;          // K values per step (64 bytes of a row)
   constexpr uint32_t EPC = 16 / ES;               // K values per 16-byte chunk
@@ -670,35 +673,96 @@ void fused_gemm_epilogue(Params p) {
       if constexpr (T::PAIR) b2rs = GE_B_RS(b2_base, BNK ? (ka) : (kb));       \
     }                                                                          \
   } while (0)
-  GE_SET_RS(kt * BKE, kt * BKE);
-  issue_a(kt * BKE, aslot(S0{}));
-  issue_b(bstage(S0{}), kt * BKE);
-  if constexpr (!BNK) {
+  if constexpr (PP) {
+    // ---- two waves per SIMD: a memory phase and a matrix phase per step ----
+    // Both groups run this sequence with one barrier between phases; group 1 starts one phase
+    // behind group 0, so in every phase one wave of each SIMD issues MFMAs while the other
+    // issues loads and fragment reads.  Group 0 reads step j in phase 2j, group 1 in 2j+1.
+    //   memory phase of step j: start the direct loads of B step j+3 (its stage held step j-1,
+    //     read by both groups before the previous barrier) and, for even j, of the A slot of
+    //     steps j+2 and j+3 (it held steps j-2 and j-1); read every fragment of step j; wait
+    //     for them and for this wave's loads of step j+1 (group 0 reads that step two phases
+    //     later, and every wave passes the barrier in between).
+    //   matrix phase of step j: the step's MFMAs only, at raised wave priority, so the
+    //     partner wave's memory work fills the issue slots the MFMAs leave.
+    const int grp = wave >> 2;
+    Frags fr0, fr1;
+    GE_SET_RS(kt * BKE, kt * BKE);
+    issue_a(kt * BKE, aslot(S0{}));
+    issue_b(bstage(S0{}), kt * BKE);
     GE_SET_RS(kt * BKE, (kt + 1) * BKE);
     issue_b(bstage(S1{}), (kt + 1) * BKE);
-  }
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(BNK ? 0 : T::B_LOADS));
-  __builtin_amdgcn_s_barrier();
-  if constexpr (F8IN) {
-    read_a8(aslot(S0{}), 0, fa8[0]);
-    read_b8(bstage(S0{}), 0, Q0c{}, QHc{});
+    GE_SET_RS(kt * BKE, (kt + 2) * BKE);
+    issue_b(bstage(S2{}), (kt + 2) * BKE);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * T::B_LOADS));   // A slot and B of step kt landed
+    __builtin_amdgcn_s_barrier();
+    if (grp == 1) __builtin_amdgcn_s_barrier();               // one phase behind group 0
+    auto mem_phase = [&](auto s_c, int j) {
+      constexpr int S = decltype(s_c)::value;
+      constexpr bool EVEN = S % 2 == 0;
+      using Cur = std::integral_constant<int, S>;
+      using FillA = std::integral_constant<int, S + 2>;
+      using FillB = std::integral_constant<int, S + 3>;
+      GE_SET_RS((j + 2) * BKE, (j + 3) * BKE);
+      issue_b(bstage(FillB{}), (j + 3) * BKE);
+      if constexpr (EVEN) issue_a((j + 2) * BKE, aslot(FillA{}));
+      read_frags(aslot(Cur{}), bstage(Cur{}), S % 2, 0, fr0);
+      read_frags(aslot(Cur{}), bstage(Cur{}), S % 2, 1, fr1);
+      // loads younger than those of step j+1: even j -- B of steps j+2, j+3 and the A slot
+      // of j+2, j+3; odd j -- B of step j+3 (the A slot of j+1 came with B of step j+2)
+      constexpr int YOUNGER = EVEN ? 2 * T::B_LOADS + T::A_LOADS : T::B_LOADS;
+      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(YOUNGER));
+      __builtin_amdgcn_s_barrier();
+    };
+    auto mat_phase = [&]() {
+      __builtin_amdgcn_s_setprio(1);
+      mfmas(fr0);
+      mfmas(fr1);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_s_barrier();
+    };
+    for (; kt < nk; kt += T::NS) {
+      mem_phase(S0{}, kt);
+      mat_phase();
+      mem_phase(S1{}, kt + 1);
+      mat_phase();
+      mem_phase(S2{}, kt + 2);
+      mat_phase();
+      mem_phase(S3{}, kt + 3);
+      mat_phase();
+    }
+    if (grp == 0) __builtin_amdgcn_s_barrier();               // matches group 1's last phase
   } else {
-    read_frags(aslot(S0{}), bstage(S0{}), 0, 0, f0);
-  }
-  auto step = [&](auto s_c, int k) {
-    if constexpr (F8IN) k_step8(s_c, k);
-    else k_step(s_c, k);
-  };
-  for (; kt < nk; kt += T::NS) {
-    // each step fills the stages of step + 2 (A: on even steps, the slot of steps + 2, + 3)
-    GE_SET_RS((kt + 2) * BKE, (kt + 2) * BKE);
-    step(S0{}, kt);
-    GE_SET_RS((kt + 2) * BKE, (kt + 3) * BKE);
-    step(S1{}, kt + 1);
-    GE_SET_RS((kt + 4) * BKE, (kt + 4) * BKE);
-    step(S2{}, kt + 2);
-    GE_SET_RS((kt + 4) * BKE, (kt + 5) * BKE);
-    step(S3{}, kt + 3);
+    GE_SET_RS(kt * BKE, kt * BKE);
+    issue_a(kt * BKE, aslot(S0{}));
+    issue_b(bstage(S0{}), kt * BKE);
+    if constexpr (!BNK) {
+      GE_SET_RS(kt * BKE, (kt + 1) * BKE);
+      issue_b(bstage(S1{}), (kt + 1) * BKE);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(BNK ? 0 : T::B_LOADS));
+    __builtin_amdgcn_s_barrier();
+    if constexpr (F8IN) {
+      read_a8(aslot(S0{}), 0, fa8[0]);
+      read_b8(bstage(S0{}), 0, Q0c{}, QHc{});
+    } else {
+      read_frags(aslot(S0{}), bstage(S0{}), 0, 0, f0);
+    }
+    auto step = [&](auto s_c, int k) {
+      if constexpr (F8IN) k_step8(s_c, k);
+      else k_step(s_c, k);
+    };
+    for (; kt < nk; kt += T::NS) {
+      // each step fills the stages of step + 2 (A: on even steps, the slot of steps + 2, + 3)
+      GE_SET_RS((kt + 2) * BKE, (kt + 2) * BKE);
+      step(S0{}, kt);
+      GE_SET_RS((kt + 2) * BKE, (kt + 3) * BKE);
+      step(S1{}, kt + 1);
+      GE_SET_RS((kt + 4) * BKE, (kt + 4) * BKE);
+      step(S2{}, kt + 2);
+      GE_SET_RS((kt + 4) * BKE, (kt + 5) * BKE);
+      step(S3{}, kt + 3);
+    }
   }
 #undef GE_SET_RS
 #undef GE_B_RS
@@ -740,7 +804,7 @@ void fused_gemm_epilogue(Params p) {
   constexpr int RPP = 64 / LPR;                         // rows per phase-2 pass
   constexpr int PASSES = 32 / RPP;
   __syncthreads();                                      // every wave is done with the stages
-  float* ep = (float*)((wave < 2 ? aslot0 : aslot1) + (wave & 1) * T::EP_WAVE_BYTES);
+  float* ep = (float*)((wave < T::EP_PER_SLOT ? aslot0 : aslot1) + (wave % T::EP_PER_SLOT) * T::EP_WAVE_BYTES);
 
   const int p2_row = lane / LPR, p2_col = 4 * (lane % LPR);
   const int gcol = n0 + wn0 + p2_col;
@@ -891,6 +955,20 @@ void fused_gemm_epilogue(Params p) {
       phase2(j, std::integral_constant<bool, false>{}, rvb[0]);
   }
 
+  // ---- cross-workgroup reductions: memory ordering ----
+  // COL_SUM and AMAX hand values between workgroups through workspace slots and ticket
+  // counters, all of them agent-scope atomics with relaxed order.  The order they need comes
+  // from how this GPU performs them: an agent-scope atomic store writes through the XCD's L2
+  // to the memory side, an agent-scope atomic load or read-modify-write is performed there, and
+  // s_waitcnt vmcnt(0) returns once this wave's stores are acknowledged at that level.  Each
+  // workgroup waits so between its slot stores and its ticket; the tickets of one counter are
+  // performed in one order at the memory side; the workgroup that draws a counter's last
+  // ticket issues its slot loads only after that read-modify-write has returned, so it reads
+  // every slot stored before any ticket of that counter (and, through a group's last
+  // workgroup, of its whole group).  Release/acquire tickets would state the same order in the
+  // language's model, but the release writes back every dirty line of the XCD's L2 (the
+  // output tiles too, which no reader of the workspace needs) at each workgroup's ticket and
+  // costs 1-7% of the kernel's time; the slots need none of it.
   // ---- COL_SUM ----
   // Lanes holding the same four columns (equal lane % LPR) add up their rows; the two waves of
   // a column half (wave_m = 0, 1) meet in LDS; the workgroup stores its partial column sums
@@ -1063,6 +1141,33 @@ hipError_t launch_tile_f8(int act, bool fp8, const Params& p, hipStream_t s) {
     case ACT_GELU_TANH:
       return fp8 ? launch_t8<T, ACT_GELU_TANH, true>(p, s) : launch_t8<T, ACT_GELU_TANH, false>(p, s);
     case ACT_SILU: return fp8 ? launch_t8<T, ACT_SILU, true>(p, s) : launch_t8<T, ACT_SILU, false>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Two-wave instances (two waves per SIMD): forward epilogues without the row statistic, on
+// bf16 operands with B given [K][N] and K a multiple of 64 (checked on the host; anything else
+// is refused here too).  The row statistic's sums would need registers these instances do not
+// have: they spill, and the one-wave-per-SIMD instances are then the faster ones.
+template <class T, int ACT, bool FP8>
+hipError_t launch_pp(const Params& p, hipStream_t s) {
+  static_assert(T::WAVES == 8, "two-wave tile");
+  const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * p.batch;
+  if (grid <= 0) return hipSuccess;
+  if ((p.flags & (F_ACT_GRAD | F_B_NK | F_IN_FP8 | F_ROW_RMS)) || p.K % 64 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, false, FP8, false, false, false>), dim3((unsigned)grid),
+                     dim3(T::NT), 0, s, p);
+  return hipGetLastError();
+}
+
+template <class T>
+hipError_t launch_tile_pp(int act, bool fp8, const Params& p, hipStream_t s) {
+  switch (act) {
+    case ACT_NONE: return fp8 ? launch_pp<T, ACT_NONE, true>(p, s) : launch_pp<T, ACT_NONE, false>(p, s);
+    case ACT_RELU: return fp8 ? launch_pp<T, ACT_RELU, true>(p, s) : launch_pp<T, ACT_RELU, false>(p, s);
+    case ACT_GELU_TANH:
+      return fp8 ? launch_pp<T, ACT_GELU_TANH, true>(p, s) : launch_pp<T, ACT_GELU_TANH, false>(p, s);
+    case ACT_SILU: return fp8 ? launch_pp<T, ACT_SILU, true>(p, s) : launch_pp<T, ACT_SILU, false>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -26,8 +26,13 @@ hipError_t launch_fused(TileKind kind, int act, bool fp8_out, const Params& p, h
       case TILE_128x128: return launch_tile_128x128_f8(act, fp8_out, p, stream);
       case TILE_64x64: return launch_tile_64x64_f8(act, fp8_out, p, stream);
       case TILE_128x128_PAIR: return launch_tile_128x128_pair_f8(act, fp8_out, p, stream);
-      default: return hipErrorInvalidValue;
+      default: return hipErrorInvalidValue;   // (no fp8-operand two-wave instances)
     }
+  }
+  if (two_wave_tile(kind)) {
+    if (p.flags & F_B_NK) return hipErrorInvalidValue;
+    return kind == TILE_256x256_2W ? launch_tile_256x256w8_kn(act, fp8_out, p, stream)
+                                   : launch_tile_256x128w8_pair_kn(act, fp8_out, p, stream);
   }
   switch (kind) {
     case TILE_256x256: return (p.flags & F_B_NK) ? launch_tile_256x256_nk(act, fp8_out, p, stream)

@@ -63,6 +63,14 @@ class DeviceProblem:
         return dataclasses.replace(self, plan=Plan(desc), args=args)
 
 
+def descriptor(w) -> ge_desc_t:
+    """The descriptor of workload `w` (dense operands and output, no tile requested)."""
+    in_t = GE_DT_FP8_E4M3 if getattr(w, "in_dtype", "bf16") == "fp8_e4m3" else GE_DT_BF16
+    return make_desc(w.batch, w.M, w.N, w.K, make_ops(w.chain),
+                     y_type=GE_DT_FP8_E4M3 if w.out == "fp8_e4m3" else GE_DT_BF16, a_type=in_t, b_type=in_t,
+                     b_layout=GE_LAYOUT_NK if getattr(w, "b_layout", "kn") == "nk" else GE_LAYOUT_KN)
+
+
 def prepare(w, inputs: Dict[str, np.ndarray], device="cuda", y_fill: Optional[int] = None,
             tile: Optional[int] = None, cache: Optional[tuning.TileCache] = None) -> DeviceProblem:
     """Uploads inputs, allocates Y (and AMAX), creates the plan for workload ``w``.  The kernel
@@ -82,10 +90,7 @@ def prepare(w, inputs: Dict[str, np.ndarray], device="cuda", y_fill: Optional[in
         Y.view(torch.uint8).fill_(y_fill)
     amax = torch.full((1,), -1.0, dtype=torch.float32, device=device) if w.has("amax") else None
     col = torch.full((w.N,), float("nan"), dtype=torch.float32, device=device) if w.has("col_sum") else None
-    in_t = GE_DT_FP8_E4M3 if getattr(w, "in_dtype", "bf16") == "fp8_e4m3" else GE_DT_BF16
-    desc = make_desc(w.batch, w.M, w.N, w.K, make_ops(w.chain),
-                     y_type=GE_DT_FP8_E4M3 if fp8 else GE_DT_BF16, a_type=in_t, b_type=in_t,
-                     b_layout=GE_LAYOUT_NK if getattr(w, "b_layout", "kn") == "nk" else GE_LAYOUT_KN)
+    desc = descriptor(w)
     if tile is None and cache is not None:
         tile = cache.lookup(desc)
     if tile is not None:

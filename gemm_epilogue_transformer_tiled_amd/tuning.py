@@ -25,19 +25,24 @@ import json
 import os
 from typing import Callable, Dict, List, Optional
 
-from . import GE_OP_PAIRWISE_ACT_MUL, GE_TILE_COUNT, ge_desc_t, gemm_epilogue_tile_info
+from . import GE_OK, GE_OP_PAIRWISE_ACT_MUL, GE_TILE_COUNT, ge_desc_t, gemm_epilogue_tile_info, gemm_epilogue_validate
 
 LDS_PER_CU = 160 * 1024          # MI355X (gfx950): LDS bytes per compute unit
 
 
 def admissible_tiles(desc: ge_desc_t, lds_budget: int = LDS_PER_CU) -> List[int]:
-    """Instances whose pairwise-ness matches the descriptor's chain and whose workgroup LDS
-    fits the budget, in id order."""
+    """Instances whose pairwise-ness matches the descriptor's chain, that the library accepts
+    for it (the two-wave instances cover forward chains on bf16 operands, B [K][N], K a
+    multiple of 64) and whose workgroup LDS fits the budget, in id order."""
     pair = any(desc.ops[i].kind == GE_OP_PAIRWISE_ACT_MUL for i in range(desc.n_ops))
     out = []
     for t in range(GE_TILE_COUNT):
         info = gemm_epilogue_tile_info(t)
-        if bool(info.pairwise) == pair and info.lds_bytes <= lds_budget:
+        if bool(info.pairwise) != pair or info.lds_bytes > lds_budget:
+            continue
+        d = ge_desc_t.from_buffer_copy(desc)
+        d.tile = t + 1
+        if gemm_epilogue_validate(d) == GE_OK:
             out.append(t)
     return out
 

@@ -124,15 +124,22 @@ typedef enum { GE_ACT_NONE = 0, GE_ACT_RELU = 1, GE_ACT_GELU_TANH = 2, GE_ACT_SI
 
 typedef enum { GE_LAYOUT_KN = 0, GE_LAYOUT_NK = 1 } ge_layout_t;
 
-/* Kernel instances (output tile shapes).  Every instance runs 4 waves of 64 lanes (2 x 2 over
- * the tile); the pairwise ones hold two accumulators (gate and up). */
+/* Kernel instances (output tile shapes).  The first five run 4 waves of 64 lanes (2 x 2 over the
+ * tile, one wave per SIMD); the _2W ones run 8 waves (2 x 4, two waves per SIMD that alternate
+ * between memory work and matrix-core work) and exist for forward epilogues without ROW_RMS on
+ * bf16 operands with B given [K][N] and K a multiple of 64 (other descriptors that request them
+ * get GE_ERR_UNSUPPORTED).  The pairwise instances hold two accumulators (gate and up).  With
+ * tile = 0 the library takes a _2W instance where it applies and the grid has >= 256
+ * workgroups of its shape. */
 typedef enum {
   GE_TILE_256x256 = 0,
   GE_TILE_256x128_PAIR = 1,
   GE_TILE_128x128 = 2,
   GE_TILE_64x64 = 3,
   GE_TILE_128x128_PAIR = 4,
-  GE_TILE_COUNT = 5
+  GE_TILE_256x256_2W = 5,
+  GE_TILE_256x128_PAIR_2W = 6,
+  GE_TILE_COUNT = 7
 } ge_tile_t;
 
 /* Static facts of one instance: tile rows and columns, whether it is a pairwise instance,

@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 ge = pytest.importorskip("gemm_epilogue_transformer_tiled_amd")
 from gemm_epilogue_transformer_tiled_amd import runner  # noqa: E402
 
-TILE_NAMES = {0: "256x256", 1: "256x128p", 2: "128x128", 3: "64x64", 4: "128x128p"}
+TILE_NAMES = {0: "256x256", 1: "256x128p", 2: "128x128", 3: "64x64", 4: "128x128p", 5: "256x256", 6: "256x128p"}
 SINGLE_TILES = [0, 2, 3]
 PAIR_TILES = [1, 4]
 
@@ -588,3 +588,102 @@ def test_run_rejects_bad_arguments_without_launching():
     rms = workloads.WORKLOADS["c4"].with_shape(M=128, N=128, K=128)
     pr = runner.prepare(rms, workloads.generate(rms))
     expect_invalid(pr, residual=None)
+
+
+# ---------------------------------------------------------------------------------------------
+# Two-wave instances (two waves per SIMD alternating memory and matrix phases): forward chains
+# on bf16 operands with B given [K][N] and K a multiple of 64.  Ragged M and N, K = 192 (the
+# loop's leading all-zero steps included), batch 2; every chain of the workloads; full sizes.
+# ---------------------------------------------------------------------------------------------
+
+TWO_WAVE = {"single": 5, "pair": 6}
+TWO_WAVE_SHAPE = dict(batch=2, M=300, N=264, K=192)
+
+
+def run_two_wave(w, inp):
+    prob = gpu_run(w, inp, TWO_WAVE["pair" if w.pairwise else "single"])
+    assert "threads=512" in prob.plan.describe(), prob.plan.describe()
+    return prob
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c5"])
+def test_two_wave_ragged(name):
+    w = workloads.WORKLOADS[name].with_shape(**TWO_WAVE_SHAPE)
+    inp = workloads.generate(w)
+    compare(w, inp, run_two_wave(w, inp), f"{name} two-wave ragged")
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c5"])
+def test_two_wave_sensitive(name):
+    w = workloads.WORKLOADS[name].with_shape(**TWO_WAVE_SHAPE)
+    inp = workloads.generate(w, sensitive=True)
+    compare(w, inp, run_two_wave(w, inp), f"{name} two-wave sensitive")
+
+
+@pytest.mark.parametrize("chain", [(("scale",), ("row_scale",), ("bias",), ("act", "silu"), ("residual",), ("col_sum",),
+                                    ("amax",)),
+                                   (("bias",), ("act", "relu"), ("amax",)),
+                                   (("scale",), ("pairwise", "gelu_tanh"), ("residual",), ("col_sum",)),
+                                   (("row_scale",), ("pairwise", "silu"), ("amax",))],
+                         ids=["rowscale-bias-silu-res-colsum-amax", "bias-relu-amax", "pair-gelu-res-colsum",
+                              "rowscale-pair-silu-amax"])
+def test_two_wave_chains(chain):
+    base = workloads.WORKLOADS["c3" if any(op[0] == "pairwise" for op in chain) else "c2"]
+    w = dataclasses.replace(base, chain=chain).with_shape(**TWO_WAVE_SHAPE)
+    inp = workloads.generate(w)
+    if w.has("row_scale"):
+        inp = {**inp, "row_scale": np.random.default_rng(5).uniform(0.5, 1.5, (w.batch, w.M)).astype(np.float32)}
+    compare(w, inp, run_two_wave(w, inp), f"two-wave {chain}")
+
+
+@pytest.mark.parametrize("K", [0, 64, 128, 256, 320])
+def test_two_wave_k_steps(K):
+    """K of 0, 1, 2, 4 and 5 steps of 64: whole and partial rings of the four-step loop."""
+    w = workloads.WORKLOADS["c2"].with_shape(batch=1, M=256, N=512, K=K)
+    inp = workloads.generate(w)
+    compare(w, inp, run_two_wave(w, inp), f"two-wave K={K}")
+
+
+def test_two_wave_is_refused_where_it_does_not_apply():
+    """A requested two-wave instance with B given [N][K], fp8 operands, an activation gradient,
+    the row statistic or K not a multiple of 64 is GE_ERR_UNSUPPORTED at validation."""
+    ops = ge.make_ops((("scale",), ("act", "relu")))
+    assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 192, ops, tile=5)) == ge.GE_OK
+    assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 200, ops, tile=5)) == ge.GE_ERR_UNSUPPORTED
+    assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 192, ops, tile=5,
+                                                  b_layout=ge.GE_LAYOUT_NK)) == ge.GE_ERR_UNSUPPORTED
+    rms = ge.make_ops((("row_rms", 1e-6), ("act", "relu")))
+    assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 192, rms, tile=5)) == ge.GE_ERR_UNSUPPORTED
+    rms_pair = ge.make_ops((("row_rms", 1e-6), ("pairwise", "silu")))
+    assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 192, rms_pair, tile=6)) == ge.GE_ERR_UNSUPPORTED
+    grad = ge.make_ops((("act_grad", "gelu_tanh"),))
+    assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 192, grad, tile=5)) == ge.GE_ERR_UNSUPPORTED
+    f8 = ge.make_desc(1, 256, 256, 192, ops, tile=5, a_type=ge.GE_DT_FP8_E4M3, b_type=ge.GE_DT_FP8_E4M3,
+                      b_layout=ge.GE_LAYOUT_NK)
+    assert ge.gemm_epilogue_validate(f8) == ge.GE_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name,threads", [("c1", 256), ("c2", 512), ("c3", 512), ("c4", 256), ("c5", 512),
+                                          ("f1", 256), ("f2", 256), ("f3", 256)])
+def test_default_instance(name, threads):
+    """With no tile requested the library takes the two-wave instances for the chains they cover
+    at >= 256 workgroups (c2, c3, c5) and the one-wave-per-SIMD instances elsewhere (the row
+    statistic, the backward step, fp8 operands, small grids)."""
+    assert not os.environ.get("GE_FORCE_TILE")
+    h = ge.gemm_epilogue_create(runner.descriptor(workloads.WORKLOADS[name]))
+    try:
+        assert f"threads={threads}" in ge.gemm_epilogue_describe(h), ge.gemm_epilogue_describe(h)
+    finally:
+        ge.gemm_epilogue_destroy(h)
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c5"])
+def test_two_wave_full_workload(name):
+    """The workloads at full size on the two-wave instances (sampled rows for the largest)."""
+    w = workloads.WORKLOADS[name]
+    inp = workloads.generate(w)
+    prob = run_two_wave(w, inp)
+    rows = None if name == "c2" else np.r_[0:40, 1000:1040, w.M - 300:w.M]
+    compare(w, inp, prob, f"{name} two-wave full", rows=rows)
+    if rows is not None and w.has("amax"):
+        check_amax(prob.amax_host(), oracle.run_workload(w, inp).amax, f"{name} two-wave full amax")

@@ -7,15 +7,17 @@ import pytest
 import gemm_epilogue_transformer_tiled_amd as ge
 from gemm_epilogue_transformer_tiled_amd import tuning
 
-SHAPES = {ge.GE_TILE_256x256: (256, 256, 0), ge.GE_TILE_256x128_PAIR: (256, 128, 1),
-          ge.GE_TILE_128x128: (128, 128, 0), ge.GE_TILE_64x64: (64, 64, 0),
-          ge.GE_TILE_128x128_PAIR: (128, 128, 1)}
+SHAPES = {ge.GE_TILE_256x256: (256, 256, 0, 256), ge.GE_TILE_256x128_PAIR: (256, 128, 1, 256),
+          ge.GE_TILE_128x128: (128, 128, 0, 256), ge.GE_TILE_64x64: (64, 64, 0, 256),
+          ge.GE_TILE_128x128_PAIR: (128, 128, 1, 256), ge.GE_TILE_256x256_2W: (256, 256, 0, 512),
+          ge.GE_TILE_256x128_PAIR_2W: (256, 128, 1, 512)}
 
 
 def test_tile_info_of_every_instance():
-    for t, (bm, bn, pair) in SHAPES.items():
+    assert len(SHAPES) == ge.GE_TILE_COUNT
+    for t, (bm, bn, pair, threads) in SHAPES.items():
         i = ge.gemm_epilogue_tile_info(t)
-        assert (i.bm, i.bn, i.pairwise, i.threads) == (bm, bn, pair, 256)
+        assert (i.bm, i.bn, i.pairwise, i.threads) == (bm, bn, pair, threads)
         assert 0 < i.lds_bytes <= tuning.LDS_PER_CU
     for bad in (-1, ge.GE_TILE_COUNT):
         with pytest.raises(ge.GemmEpilogueError):
@@ -29,8 +31,14 @@ def _desc(chain, **kw):
 def test_admissible_tiles_match_the_chain_and_the_lds_budget():
     single = _desc([("scale",), ("bias",), ("act", "relu")])
     pair = _desc([("pairwise", "silu")])
-    assert tuning.admissible_tiles(single) == [0, 2, 3]
-    assert tuning.admissible_tiles(pair) == [1, 4]
+    assert tuning.admissible_tiles(single) == [0, 2, 3, 5]
+    assert tuning.admissible_tiles(pair) == [1, 4, 6]
+    # the two-wave instances only where they apply: not for K % 64 != 0 or B given [N][K] ...
+    assert tuning.admissible_tiles(ge.make_desc(1, 512, 512, 520, ge.make_ops([("scale",)]))) == [0, 2, 3]
+    assert tuning.admissible_tiles(_desc([("scale",)], b_layout=ge.GE_LAYOUT_NK)) == [0, 2, 3]
+    # ... nor with the row statistic
+    assert tuning.admissible_tiles(_desc([("row_rms", 1e-6), ("act", "relu")])) == [0, 2, 3]
+    assert tuning.admissible_tiles(_desc([("row_rms", 1e-6), ("pairwise", "silu")])) == [1, 4]
     # a tighter budget removes the instances that allocate more LDS
     lds = {t: ge.gemm_epilogue_tile_info(t).lds_bytes for t in SHAPES}
     budget = lds[ge.GE_TILE_64x64]
