@@ -206,8 +206,7 @@ template <class T, int ACT, bool GRAD, bool FP8, bool ROWSTAT, bool KMASK, bool 
 __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(T::WPE, T::WPE)))
 void fused_gemm_epilogue(Params p) {
   constexpr bool PP = T::WAVES == 8;              // two waves per SIMD, alternating phases
-  static_assert(!PP || (!BNK && !F8IN && !GRAD && !KMASK && !ROWSTAT),
-                "the two-wave instances: B [K][N], bf16, K % 64 == 0, no row statistic");
+  static_assert(!PP || (!BNK && !F8IN && !GRAD && !KMASK), "the two-wave instances: B [K][N], bf16, K % 64 == 0");
   constexpr int ES = F8IN ? 1 : 2;                // bytes per operand element
   constexpr int BKE = F8IN ? 64 : T::BK;          // K values per step (64 bytes of a row)
   constexpr uint32_t EPC = 16 / ES;               // K values per 16-byte chunk
@@ -227,7 +226,7 @@ void fused_gemm_epilogue(Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char bstage1[B_BUF];
   __shared__ __attribute__((aligned(1024))) unsigned char bstage2[B_BUF23];
   __shared__ __attribute__((aligned(1024))) unsigned char bstage3[B_BUF23];
-  __shared__ float row_ss[ROWSTAT ? T::BM : 1];
+  __shared__ float row_ss[ROWSTAT ? (PP ? 2 : 1) * T::BM : 1];   // two-wave: one half per wave group
   __shared__ uint32_t wave_amax[T::WAVES];
   __shared__ __attribute__((aligned(256))) unsigned char pf_sink[T::WAVES * 256];   // L2 prefetch target
   static_assert(T::NS == 4, "four B stage arrays");
@@ -465,8 +464,9 @@ void fused_gemm_epilogue(Params p) {
       acc[i][j] = f32x16_t{};
       if constexpr (T::PAIR) acc2[i][j] = f32x16_t{};
     }
-  // RMS statistic from the A fragments: waves with wave_n == 0 own the first half of the
-  // wave's 32-row blocks, wave_n == 1 the second half (all of them when FM == 1 and wave_n == 0).
+  // RMS statistic from the A fragments (one-wave instances): waves with wave_n == 0 own the
+  // first half of the wave's 32-row blocks, wave_n == 1 the second half (all of them when
+  // FM == 1 and wave_n == 0).  The two-wave instances take it from the A slots instead.
   constexpr int SS_J = T::FM > 1 ? T::FM / 2 : 1;
   float ss[SS_J];
 #pragma unroll
@@ -511,7 +511,7 @@ void fused_gemm_epilogue(Params p) {
         if constexpr (T::PAIR)
           acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[T::NB - 1][i], f.a[j], acc2[i][j], 0, 0, 0);
       }
-    if constexpr (ROWSTAT) {
+    if constexpr (ROWSTAT && !PP) {
       if (ss_owner) {
 #pragma unroll
         for (int j = 0; j < SS_J; ++j) {
@@ -687,6 +687,18 @@ void fused_gemm_epilogue(Params p) {
     //     partner wave's memory work fills the issue slots the MFMAs leave.
     const int grp = wave >> 2;
     Frags fr0, fr1;
+    // Row statistic: in the memory phase of each odd step j every lane squares half of one
+    // row of the A slot of steps j-1 and j (its last use): slot row (wave % 4) * 64 + lane,
+    // physical chunks sq_c ^ i (i < 4), where sq_c's bit 2 is the wave group, so the two
+    // groups cover the row's eight chunks between them (the sum does not depend on which
+    // K a chunk holds).  sq_c = (l + l / 8) % 8, l = lane % 16, gives the 8 (16) lanes one
+    // LDS pass serves 8 (16) distinct chunk columns: no bank conflicts.  The loads and
+    // v_dot2 run while the other group's MFMAs use the matrix core; the fragments stay as
+    // they are.
+    static_assert(!ROWSTAT || T::BM == 4 * 64, "one slot row per lane of a wave group");
+    float ss1 = 0.0f;
+    const uint32_t sq_row = (uint32_t)((wave & 3) * 64 + lane) * T::A_ROWB;
+    const uint32_t sq_c = ((uint32_t)((lane & 15) + ((lane & 15) >> 3)) & 7u) ^ (uint32_t)(4 * grp);
     GE_SET_RS(kt * BKE, kt * BKE);
     issue_a(kt * BKE, aslot(S0{}));
     issue_b(bstage(S0{}), kt * BKE);
@@ -708,10 +720,28 @@ void fused_gemm_epilogue(Params p) {
       if constexpr (EVEN) issue_a((j + 2) * BKE, aslot(FillA{}));
       read_frags(aslot(Cur{}), bstage(Cur{}), S % 2, 0, fr0);
       read_frags(aslot(Cur{}), bstage(Cur{}), S % 2, 1, fr1);
+      bf16x8_t sq[4];
+      if constexpr (ROWSTAT && !EVEN) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sq[i] = *(const bf16x8_t*)(aslot(Cur{}) + sq_row + ((sq_c ^ (uint32_t)i) << 4));
+      }
       // loads younger than those of step j+1: even j -- B of steps j+2, j+3 and the A slot
       // of j+2, j+3; odd j -- B of step j+3 (the A slot of j+1 came with B of step j+2)
       constexpr int YOUNGER = EVEN ? 2 * T::B_LOADS + T::A_LOADS : T::B_LOADS;
       __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(YOUNGER));
+      if constexpr (ROWSTAT && !EVEN) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x8_t v = sq[i];
+          const bf16x2_t p0 = __builtin_shufflevector(v, v, 0, 1), p1 = __builtin_shufflevector(v, v, 2, 3);
+          const bf16x2_t p2 = __builtin_shufflevector(v, v, 4, 5), p3 = __builtin_shufflevector(v, v, 6, 7);
+          ss1 = __builtin_amdgcn_fdot2_f32_bf16(p0, p0, ss1, false);
+          ss1 = __builtin_amdgcn_fdot2_f32_bf16(p1, p1, ss1, false);
+          ss1 = __builtin_amdgcn_fdot2_f32_bf16(p2, p2, ss1, false);
+          ss1 = __builtin_amdgcn_fdot2_f32_bf16(p3, p3, ss1, false);
+        }
+        asm volatile("" : "+v"(ss1));      // keep the squares in this phase
+      }
       __builtin_amdgcn_s_barrier();
     };
     auto mat_phase = [&]() {
@@ -732,6 +762,7 @@ void fused_gemm_epilogue(Params p) {
       mat_phase();
     }
     if (grp == 0) __builtin_amdgcn_s_barrier();               // matches group 1's last phase
+    if constexpr (ROWSTAT) row_ss[grp * T::BM + (wave & 3) * 64 + lane] = ss1;
   } else {
     GE_SET_RS(kt * BKE, kt * BKE);
     issue_a(kt * BKE, aslot(S0{}));
@@ -773,10 +804,12 @@ void fused_gemm_epilogue(Params p) {
 
   // ---- RMS row statistic: the two lane halves hold different K of the same rows ----
   if constexpr (ROWSTAT) {
+    if constexpr (!PP) {
 #pragma unroll
-    for (int j = 0; j < SS_J; ++j) {
-      const float s = ss[j] + __shfl_xor(ss[j], 32);
-      if (ss_owner && lhalf == 0) row_ss[wm0 + 32 * (ss_j0 + j) + lrow] = s;
+      for (int j = 0; j < SS_J; ++j) {
+        const float s = ss[j] + __shfl_xor(ss[j], 32);
+        if (ss_owner && lhalf == 0) row_ss[wm0 + 32 * (ss_j0 + j) + lrow] = s;
+      }
     }
     __syncthreads();
   }
@@ -929,7 +962,9 @@ void fused_gemm_epilogue(Params p) {
     const int ml = wm0 + 32 * j + lrow;
     float rscale = alpha;
     if constexpr (ROWSTAT) {
-      if (has_rms) rscale *= __builtin_amdgcn_rsqf(row_ss[ml] * inv_k + p.eps);
+      float ssq = row_ss[ml];
+      if constexpr (PP) ssq += row_ss[T::BM + ml];
+      if (has_rms) rscale *= __builtin_amdgcn_rsqf(ssq * inv_k + p.eps);
     }
     if (has_rs) rscale *= (m0 + ml < M) ? p.row_scale[(int64_t)b * M + m0 + ml] : 0.0f;
     // phase 1: lane's row lrow, columns 32i + 8g + 4*lhalf + e of the wave's block
@@ -1145,18 +1180,20 @@ hipError_t launch_tile_f8(int act, bool fp8, const Params& p, hipStream_t s) {
   }
 }
 
-// Two-wave instances (two waves per SIMD): forward epilogues without the row statistic, on
-// bf16 operands with B given [K][N] and K a multiple of 64 (checked on the host; anything else
-// is refused here too).  The row statistic's sums would need registers these instances do not
-// have: they spill, and the one-wave-per-SIMD instances are then the faster ones.
+// Two-wave instances (two waves per SIMD): forward epilogues on bf16 operands with B given
+// [K][N] and K a multiple of 64 (checked on the host; anything else is refused here too).
 template <class T, int ACT, bool FP8>
 hipError_t launch_pp(const Params& p, hipStream_t s) {
   static_assert(T::WAVES == 8, "two-wave tile");
   const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * p.batch;
   if (grid <= 0) return hipSuccess;
-  if ((p.flags & (F_ACT_GRAD | F_B_NK | F_IN_FP8 | F_ROW_RMS)) || p.K % 64 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, false, FP8, false, false, false>), dim3((unsigned)grid),
-                     dim3(T::NT), 0, s, p);
+  if ((p.flags & (F_ACT_GRAD | F_B_NK | F_IN_FP8)) || p.K % 64 != 0) return hipErrorInvalidValue;
+  if (p.flags & F_ROW_RMS)
+    hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, false, FP8, true, false, false>), dim3((unsigned)grid),
+                       dim3(T::NT), 0, s, p);
+  else
+    hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, false, FP8, false, false, false>), dim3((unsigned)grid),
+                       dim3(T::NT), 0, s, p);
   return hipGetLastError();
 }
 

@@ -606,7 +606,7 @@ def run_two_wave(w, inp):
     return prob
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c5"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5", "f1"])
 def test_two_wave_ragged(name):
     w = workloads.WORKLOADS[name].with_shape(**TWO_WAVE_SHAPE)
     inp = workloads.generate(w)
@@ -622,11 +622,12 @@ def test_two_wave_sensitive(name):
 
 @pytest.mark.parametrize("chain", [(("scale",), ("row_scale",), ("bias",), ("act", "silu"), ("residual",), ("col_sum",),
                                     ("amax",)),
-                                   (("bias",), ("act", "relu"), ("amax",)),
+                                   (("row_rms", 1e-6), ("bias",), ("act", "relu"), ("amax",)),
                                    (("scale",), ("pairwise", "gelu_tanh"), ("residual",), ("col_sum",)),
-                                   (("row_scale",), ("pairwise", "silu"), ("amax",))],
-                         ids=["rowscale-bias-silu-res-colsum-amax", "bias-relu-amax", "pair-gelu-res-colsum",
-                              "rowscale-pair-silu-amax"])
+                                   (("row_rms", 1e-6), ("pairwise", "silu"), ("amax",)),
+                                   (("scale",), ("row_rms", 0.5), ("residual",), ("col_sum",))],
+                         ids=["rowscale-bias-silu-res-colsum-amax", "rms-bias-relu-amax", "pair-gelu-res-colsum",
+                              "rms-pair-silu-amax", "scale-rms-eps-res-colsum"])
 def test_two_wave_chains(chain):
     base = workloads.WORKLOADS["c3" if any(op[0] == "pairwise" for op in chain) else "c2"]
     w = dataclasses.replace(base, chain=chain).with_shape(**TWO_WAVE_SHAPE)
@@ -645,17 +646,16 @@ def test_two_wave_k_steps(K):
 
 
 def test_two_wave_is_refused_where_it_does_not_apply():
-    """A requested two-wave instance with B given [N][K], fp8 operands, an activation gradient,
-    the row statistic or K not a multiple of 64 is GE_ERR_UNSUPPORTED at validation."""
+    """A requested two-wave instance with B given [N][K], fp8 operands, an activation gradient or
+    K not a multiple of 64 is GE_ERR_UNSUPPORTED at validation."""
     ops = ge.make_ops((("scale",), ("act", "relu")))
     assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 192, ops, tile=5)) == ge.GE_OK
     assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 200, ops, tile=5)) == ge.GE_ERR_UNSUPPORTED
     assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 192, ops, tile=5,
                                                   b_layout=ge.GE_LAYOUT_NK)) == ge.GE_ERR_UNSUPPORTED
     rms = ge.make_ops((("row_rms", 1e-6), ("act", "relu")))
-    assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 192, rms, tile=5)) == ge.GE_ERR_UNSUPPORTED
-    rms_pair = ge.make_ops((("row_rms", 1e-6), ("pairwise", "silu")))
-    assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 192, rms_pair, tile=6)) == ge.GE_ERR_UNSUPPORTED
+    assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 192, rms, tile=5)) == ge.GE_OK
+    assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 200, rms, tile=5)) == ge.GE_ERR_UNSUPPORTED
     grad = ge.make_ops((("act_grad", "gelu_tanh"),))
     assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 192, grad, tile=5)) == ge.GE_ERR_UNSUPPORTED
     f8 = ge.make_desc(1, 256, 256, 192, ops, tile=5, a_type=ge.GE_DT_FP8_E4M3, b_type=ge.GE_DT_FP8_E4M3,
@@ -663,12 +663,12 @@ def test_two_wave_is_refused_where_it_does_not_apply():
     assert ge.gemm_epilogue_validate(f8) == ge.GE_ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("name,threads", [("c1", 256), ("c2", 512), ("c3", 512), ("c4", 256), ("c5", 512),
-                                          ("f1", 256), ("f2", 256), ("f3", 256)])
+@pytest.mark.parametrize("name,threads", [("c1", 256), ("c2", 512), ("c3", 512), ("c4", 512), ("c5", 512),
+                                          ("f1", 512), ("f2", 256), ("f3", 256)])
 def test_default_instance(name, threads):
     """With no tile requested the library takes the two-wave instances for the chains they cover
-    at >= 256 workgroups (c2, c3, c5) and the one-wave-per-SIMD instances elsewhere (the row
-    statistic, the backward step, fp8 operands, small grids)."""
+    at >= 256 workgroups (c2 .. c5, f1) and the one-wave-per-SIMD instances elsewhere (the
+    backward step with B [N][K], fp8 operands, small grids)."""
     assert not os.environ.get("GE_FORCE_TILE")
     h = ge.gemm_epilogue_create(runner.descriptor(workloads.WORKLOADS[name]))
     try:
@@ -677,7 +677,7 @@ def test_default_instance(name, threads):
         ge.gemm_epilogue_destroy(h)
 
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c5"])
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5", "f1"])
 def test_two_wave_full_workload(name):
     """The workloads at full size on the two-wave instances (sampled rows for the largest)."""
     w = workloads.WORKLOADS[name]
