@@ -50,6 +50,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+GRAPH_PROBE_BELOW_MS = 0.1     # eager steps at least this long are not probed as a graph
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published (the fp8-operand workload)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 METRIC = "fused GEMM-epilogue TFLOP/s (% of MI355X bf16 MFMA peak) per config"
@@ -156,42 +157,51 @@ def time_launches(prob, steps, warmup, launch="auto"):
     """Times `steps` back-to-back launches with inputs resident in HBM.
 
     Two ways to issue the steps: eagerly (one Python call, one hipLaunchKernel per step) or
-    as one replay of a HIP graph holding the `steps` launches.  "auto" picks the faster on
-    an untimed probe of 10 steps each (graphs remove the host launch cost that bounds small
-    kernels; eager launches avoid the graph's inter-node overhead on long ones), then times
-    the `steps` steps in that mode.  Returns (ms per step, mode, probe {mode: ms per step}).
+    as one replay of a HIP graph holding the `steps` launches.  "auto" times 10 eager steps
+    and, only when a step is short enough for the host's launch cost to matter (under
+    GRAPH_PROBE_BELOW_MS), 10 graph steps, and takes the faster.  Longer kernels stay eager
+    without a graph probe: on this GPU a graph replay leaves the eager launches after it
+    slower for tens of milliseconds (a 256x256-tile kernel of ~220 us measured 6-20 % slower
+    for the next 70 launches), which would be timed as the kernel's own cost.  The timed
+    steps follow a fresh warm-up of at least 0.25 s in the chosen mode.  Returns (ms per
+    step, mode, probe {mode: ms per step}).
     """
     import torch
 
     stream = torch.cuda.current_stream()
-    # warm-up: `warmup` steps, continued until 0.25 s have passed when warmup > 0 (the clocks
-    # take that long to settle under load)
-    t0 = time.perf_counter()
-    done = 0
-    while done < warmup or (warmup > 0 and time.perf_counter() - t0 < 0.25):
-        prob.run()
-        done += 1
-        if done % 16 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
 
     def eager(n):
         for _ in range(n):
             prob.run(stream.cuda_stream)
 
+    def warm(fn, per_call):
+        # `warmup` steps, continued until 0.25 s have passed when warmup > 0 (the clocks take
+        # that long to settle under load)
+        t0 = time.perf_counter()
+        done = 0
+        while done < warmup or (warmup > 0 and time.perf_counter() - t0 < 0.25):
+            fn()
+            done += per_call
+            torch.cuda.synchronize()
+
+    warm(lambda: eager(8), 8)
     probe = {}
     if launch == "auto":
         n = min(steps, 10)
         probe["eager"] = _region_ms(lambda: eager(n), stream) / n
-        g = _graph_of(prob, n)
-        probe["graph"] = _region_ms(g.replay, stream) / n
-        del g
-        launch = min(probe, key=probe.get)
+        launch = "eager"
+        if probe["eager"] < GRAPH_PROBE_BELOW_MS:
+            g = _graph_of(prob, n)
+            probe["graph"] = _region_ms(g.replay, stream) / n
+            del g
+            launch = min(probe, key=probe.get)
     if launch == "graph":
         g = _graph_of(prob, steps)
+        warm(g.replay, steps)
         ms = _region_ms(g.replay, stream) / steps
         del g
     else:
+        warm(lambda: eager(8), 8)
         ms = _region_ms(lambda: eager(steps), stream) / steps
     return ms, launch, {k: round(v, 6) for k, v in probe.items()}
 
