@@ -18,8 +18,9 @@ BUILD_DIR = os.path.join(HERE, "_build")
 TARGETS = {
     os.path.join(HERE, "libgemm_epilogue.so"): [
         f"ge_tile_{t}_{lay}.hip" for t in ("256x256", "256x128_pair", "128x128", "64x64", "128x128_pair")
-        for lay in ("kn", "nk", "f8")] + ["ge_tile_256x256w8_kn.hip", "ge_tile_256x128w8_pair_kn.hip",
-                                          "ge_kernels.hip", "noalloc.hip", "tiles.cpp", "api.cpp"],
+        for lay in ("kn", "nk", "f8")] + [f"ge_tile_{t}_{lay}.hip" for t in ("256x256w8", "256x128w8_pair")
+                                          for lay in ("kn", "nk")] + [
+        "ge_kernels.hip", "noalloc.hip", "tiles.cpp", "api.cpp"],
     os.path.join(HERE, "libge_baselines.so"): ["baselines.hip"],
 }
 LIB = os.path.join(HERE, "libgemm_epilogue.so")

@@ -206,7 +206,7 @@ template <class T, int ACT, bool GRAD, bool FP8, bool ROWSTAT, bool KMASK, bool 
 __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(T::WPE, T::WPE)))
 void fused_gemm_epilogue(Params p) {
   constexpr bool PP = T::WAVES == 8;              // two waves per SIMD, alternating phases
-  static_assert(!PP || (!BNK && !F8IN && !GRAD && !KMASK), "the two-wave instances: B [K][N], bf16, K % 64 == 0");
+  static_assert(!PP || (!F8IN && !KMASK), "the two-wave instances: bf16 operands, K % 64 == 0");
   constexpr int ES = F8IN ? 1 : 2;                // bytes per operand element
   constexpr int BKE = F8IN ? 64 : T::BK;          // K values per step (64 bytes of a row)
   constexpr uint32_t EPC = 16 / ES;               // K values per 16-byte chunk
@@ -680,8 +680,9 @@ void fused_gemm_epilogue(Params p) {
     // issues loads and fragment reads.  Group 0 reads step j in phase 2j, group 1 in 2j+1.
     //   memory phase of step j: start the direct loads of B step j+3 (its stage held step j-1,
     //     read by both groups before the previous barrier) and, for even j, of the A slot of
-    //     steps j+2 and j+3 (it held steps j-2 and j-1); read every fragment of step j; wait
-    //     for them and for this wave's loads of step j+1 (group 0 reads that step two phases
+    //     steps j+2 and j+3 (it held steps j-2 and j-1) -- with B given [N][K], B is staged in
+    //     two-step slots like A and loaded with it; read every fragment of step j; wait for
+    //     them and for this wave's loads of step j+1 (group 0 reads that step two phases
     //     later, and every wave passes the barrier in between).
     //   matrix phase of step j: the step's MFMAs only, at raised wave priority, so the
     //     partner wave's memory work fills the issue slots the MFMAs leave.
@@ -702,11 +703,13 @@ void fused_gemm_epilogue(Params p) {
     GE_SET_RS(kt * BKE, kt * BKE);
     issue_a(kt * BKE, aslot(S0{}));
     issue_b(bstage(S0{}), kt * BKE);
-    GE_SET_RS(kt * BKE, (kt + 1) * BKE);
-    issue_b(bstage(S1{}), (kt + 1) * BKE);
-    GE_SET_RS(kt * BKE, (kt + 2) * BKE);
-    issue_b(bstage(S2{}), (kt + 2) * BKE);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * T::B_LOADS));   // A slot and B of step kt landed
+    if constexpr (!BNK) {
+      GE_SET_RS(kt * BKE, (kt + 1) * BKE);
+      issue_b(bstage(S1{}), (kt + 1) * BKE);
+      GE_SET_RS(kt * BKE, (kt + 2) * BKE);
+      issue_b(bstage(S2{}), (kt + 2) * BKE);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(BNK ? 0 : 2 * T::B_LOADS));   // A slot and B of step kt landed
     __builtin_amdgcn_s_barrier();
     if (grp == 1) __builtin_amdgcn_s_barrier();               // one phase behind group 0
     auto mem_phase = [&](auto s_c, int j) {
@@ -716,8 +719,15 @@ void fused_gemm_epilogue(Params p) {
       using FillA = std::integral_constant<int, S + 2>;
       using FillB = std::integral_constant<int, S + 3>;
       GE_SET_RS((j + 2) * BKE, (j + 3) * BKE);
-      issue_b(bstage(FillB{}), (j + 3) * BKE);
-      if constexpr (EVEN) issue_a((j + 2) * BKE, aslot(FillA{}));
+      if constexpr (BNK) {
+        if constexpr (EVEN) {
+          issue_a((j + 2) * BKE, aslot(FillA{}));
+          issue_b(bstage(FillA{}), (j + 2) * BKE);
+        }
+      } else {
+        issue_b(bstage(FillB{}), (j + 3) * BKE);
+        if constexpr (EVEN) issue_a((j + 2) * BKE, aslot(FillA{}));
+      }
       read_frags(aslot(Cur{}), bstage(Cur{}), S % 2, 0, fr0);
       read_frags(aslot(Cur{}), bstage(Cur{}), S % 2, 1, fr1);
       bf16x8_t sq[4];
@@ -726,8 +736,10 @@ void fused_gemm_epilogue(Params p) {
         for (int i = 0; i < 4; ++i) sq[i] = *(const bf16x8_t*)(aslot(Cur{}) + sq_row + ((sq_c ^ (uint32_t)i) << 4));
       }
       // loads younger than those of step j+1: even j -- B of steps j+2, j+3 and the A slot
-      // of j+2, j+3; odd j -- B of step j+3 (the A slot of j+1 came with B of step j+2)
-      constexpr int YOUNGER = EVEN ? 2 * T::B_LOADS + T::A_LOADS : T::B_LOADS;
+      // of j+2, j+3; odd j -- B of step j+3 (the A slot of j+1 came with B of step j+2).
+      // [N][K]: even j -- the A and B slots of j+2, j+3; odd j -- none.
+      constexpr int YOUNGER = BNK ? (EVEN ? T::A_LOADS + BL : 0)
+                                  : (EVEN ? 2 * T::B_LOADS + T::A_LOADS : T::B_LOADS);
       __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(YOUNGER));
       if constexpr (ROWSTAT && !EVEN) {
 #pragma unroll
@@ -1180,31 +1192,41 @@ hipError_t launch_tile_f8(int act, bool fp8, const Params& p, hipStream_t s) {
   }
 }
 
-// Two-wave instances (two waves per SIMD): forward epilogues on bf16 operands with B given
-// [K][N] and K a multiple of 64 (checked on the host; anything else is refused here too).
-template <class T, int ACT, bool FP8>
+// Two-wave instances (two waves per SIMD) of one B layout: bf16 operands and K a multiple of
+// 64 (checked on the host; anything else is refused here too).
+template <class T, int ACT, bool FP8, bool BNK>
 hipError_t launch_pp(const Params& p, hipStream_t s) {
   static_assert(T::WAVES == 8, "two-wave tile");
   const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * p.batch;
   if (grid <= 0) return hipSuccess;
-  if ((p.flags & (F_ACT_GRAD | F_B_NK | F_IN_FP8)) || p.K % 64 != 0) return hipErrorInvalidValue;
-  if (p.flags & F_ROW_RMS)
-    hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, false, FP8, true, false, false>), dim3((unsigned)grid),
+  if ((p.flags & F_IN_FP8) || ((p.flags & F_B_NK) != 0) != BNK || p.K % 64 != 0) return hipErrorInvalidValue;
+  if (p.flags & F_ACT_GRAD) {
+    // backward epilogue instances: bf16 output, no in-kernel row statistic (checked on the host)
+    if constexpr (!T::PAIR && !FP8) {
+      if (p.flags & F_ROW_RMS) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, true, false, false, false, BNK>), dim3((unsigned)grid),
+                         dim3(T::NT), 0, s, p);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else if (p.flags & F_ROW_RMS) {
+    hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, false, FP8, true, false, BNK>), dim3((unsigned)grid),
                        dim3(T::NT), 0, s, p);
-  else
-    hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, false, FP8, false, false, false>), dim3((unsigned)grid),
+  } else {
+    hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, false, FP8, false, false, BNK>), dim3((unsigned)grid),
                        dim3(T::NT), 0, s, p);
+  }
   return hipGetLastError();
 }
 
-template <class T>
+template <class T, bool BNK>
 hipError_t launch_tile_pp(int act, bool fp8, const Params& p, hipStream_t s) {
   switch (act) {
-    case ACT_NONE: return fp8 ? launch_pp<T, ACT_NONE, true>(p, s) : launch_pp<T, ACT_NONE, false>(p, s);
-    case ACT_RELU: return fp8 ? launch_pp<T, ACT_RELU, true>(p, s) : launch_pp<T, ACT_RELU, false>(p, s);
+    case ACT_NONE: return fp8 ? launch_pp<T, ACT_NONE, true, BNK>(p, s) : launch_pp<T, ACT_NONE, false, BNK>(p, s);
+    case ACT_RELU: return fp8 ? launch_pp<T, ACT_RELU, true, BNK>(p, s) : launch_pp<T, ACT_RELU, false, BNK>(p, s);
     case ACT_GELU_TANH:
-      return fp8 ? launch_pp<T, ACT_GELU_TANH, true>(p, s) : launch_pp<T, ACT_GELU_TANH, false>(p, s);
-    case ACT_SILU: return fp8 ? launch_pp<T, ACT_SILU, true>(p, s) : launch_pp<T, ACT_SILU, false>(p, s);
+      return fp8 ? launch_pp<T, ACT_GELU_TANH, true, BNK>(p, s) : launch_pp<T, ACT_GELU_TANH, false, BNK>(p, s);
+    case ACT_SILU: return fp8 ? launch_pp<T, ACT_SILU, true, BNK>(p, s) : launch_pp<T, ACT_SILU, false, BNK>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

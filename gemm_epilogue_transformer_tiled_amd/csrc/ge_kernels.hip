@@ -30,7 +30,9 @@ hipError_t launch_fused(TileKind kind, int act, bool fp8_out, const Params& p, h
     }
   }
   if (two_wave_tile(kind)) {
-    if (p.flags & F_B_NK) return hipErrorInvalidValue;
+    if (p.flags & F_B_NK)
+      return kind == TILE_256x256_2W ? launch_tile_256x256w8_nk(act, fp8_out, p, stream)
+                                     : launch_tile_256x128w8_pair_nk(act, fp8_out, p, stream);
     return kind == TILE_256x256_2W ? launch_tile_256x256w8_kn(act, fp8_out, p, stream)
                                    : launch_tile_256x128w8_pair_kn(act, fp8_out, p, stream);
   }

@@ -637,38 +637,57 @@ def test_two_wave_chains(chain):
     compare(w, inp, run_two_wave(w, inp), f"two-wave {chain}")
 
 
+@pytest.mark.parametrize("layout", ["kn", "nk"])
 @pytest.mark.parametrize("K", [0, 64, 128, 256, 320])
-def test_two_wave_k_steps(K):
+def test_two_wave_k_steps(K, layout):
     """K of 0, 1, 2, 4 and 5 steps of 64: whole and partial rings of the four-step loop."""
-    w = workloads.WORKLOADS["c2"].with_shape(batch=1, M=256, N=512, K=K)
+    w = dataclasses.replace(workloads.WORKLOADS["c2"], b_layout=layout).with_shape(batch=1, M=256, N=512, K=K)
     inp = workloads.generate(w)
-    compare(w, inp, run_two_wave(w, inp), f"two-wave K={K}")
+    compare(w, inp, run_two_wave(w, inp), f"two-wave K={K} {layout}")
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5", "f1"])
+def test_two_wave_ragged_b_nk(name):
+    """B given [N][K]: staged in two-step slots like A on the two-wave instances."""
+    w = dataclasses.replace(workloads.WORKLOADS[name], b_layout="nk").with_shape(**TWO_WAVE_SHAPE)
+    inp = workloads.generate(w)
+    compare(w, inp, run_two_wave(w, inp), f"{name} two-wave ragged B [N][K]")
+
+
+@pytest.mark.parametrize("layout", ["nk", "kn"])
+@pytest.mark.parametrize("chain", BACKWARD_CHAINS, ids=lambda c: "-".join(op[0] + (op[1] if len(op) > 1 and isinstance(op[1], str) else "") for op in c))
+def test_two_wave_backward_chains(chain, layout):
+    w = dataclasses.replace(workloads.WORKLOADS["f2"], chain=chain, b_layout=layout, alpha=0.75,
+                            bias_var=0.3).with_shape(**TWO_WAVE_SHAPE)
+    inp = workloads.generate(w)
+    compare(w, inp, run_two_wave(w, inp), f"two-wave backward {chain} {layout}")
 
 
 def test_two_wave_is_refused_where_it_does_not_apply():
-    """A requested two-wave instance with B given [N][K], fp8 operands, an activation gradient or
-    K not a multiple of 64 is GE_ERR_UNSUPPORTED at validation."""
+    """A requested two-wave instance with fp8 operands or K not a multiple of 64 is
+    GE_ERR_UNSUPPORTED at validation."""
     ops = ge.make_ops((("scale",), ("act", "relu")))
     assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 192, ops, tile=5)) == ge.GE_OK
     assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 200, ops, tile=5)) == ge.GE_ERR_UNSUPPORTED
     assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 192, ops, tile=5,
-                                                  b_layout=ge.GE_LAYOUT_NK)) == ge.GE_ERR_UNSUPPORTED
+                                                  b_layout=ge.GE_LAYOUT_NK)) == ge.GE_OK
     rms = ge.make_ops((("row_rms", 1e-6), ("act", "relu")))
     assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 192, rms, tile=5)) == ge.GE_OK
     assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 200, rms, tile=5)) == ge.GE_ERR_UNSUPPORTED
     grad = ge.make_ops((("act_grad", "gelu_tanh"),))
-    assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 192, grad, tile=5)) == ge.GE_ERR_UNSUPPORTED
+    assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 192, grad, tile=5)) == ge.GE_OK
+    assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 200, grad, tile=5)) == ge.GE_ERR_UNSUPPORTED
     f8 = ge.make_desc(1, 256, 256, 192, ops, tile=5, a_type=ge.GE_DT_FP8_E4M3, b_type=ge.GE_DT_FP8_E4M3,
                       b_layout=ge.GE_LAYOUT_NK)
     assert ge.gemm_epilogue_validate(f8) == ge.GE_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("name,threads", [("c1", 256), ("c2", 512), ("c3", 512), ("c4", 512), ("c5", 512),
-                                          ("f1", 512), ("f2", 256), ("f3", 256)])
+                                          ("f1", 512), ("f2", 512), ("f3", 256)])
 def test_default_instance(name, threads):
     """With no tile requested the library takes the two-wave instances for the chains they cover
-    at >= 256 workgroups (c2 .. c5, f1) and the one-wave-per-SIMD instances elsewhere (the
-    backward step with B [N][K], fp8 operands, small grids)."""
+    at >= 256 workgroups (c2 .. c5, f1, f2) and the one-wave-per-SIMD instances elsewhere (fp8
+    operands, small grids)."""
     assert not os.environ.get("GE_FORCE_TILE")
     h = ge.gemm_epilogue_create(runner.descriptor(workloads.WORKLOADS[name]))
     try:
@@ -677,7 +696,7 @@ def test_default_instance(name, threads):
         ge.gemm_epilogue_destroy(h)
 
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5", "f1"])
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5", "f1", "f2"])
 def test_two_wave_full_workload(name):
     """The workloads at full size on the two-wave instances (sampled rows for the largest)."""
     w = workloads.WORKLOADS[name]
