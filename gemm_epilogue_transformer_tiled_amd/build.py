@@ -19,7 +19,7 @@ TARGETS = {
     os.path.join(HERE, "libgemm_epilogue.so"): [
         f"ge_tile_{t}_{lay}.hip" for t in ("256x256", "256x128_pair", "128x128", "64x64", "128x128_pair")
         for lay in ("kn", "nk", "f8")] + [f"ge_tile_{t}_{lay}.hip" for t in ("256x256w8", "256x128w8_pair")
-                                          for lay in ("kn", "nk")] + [
+                                          for lay in ("kn", "nk", "f8")] + [
         "ge_kernels.hip", "noalloc.hip", "tiles.cpp", "api.cpp"],
     os.path.join(HERE, "libge_baselines.so"): ["baselines.hip"],
 }

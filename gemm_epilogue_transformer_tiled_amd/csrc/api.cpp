@@ -80,7 +80,7 @@ int64_t extent_bytes(int64_t rows, int64_t cols, int64_t ld, int64_t esize) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// The two-wave instances cover bf16 operands with K a multiple of 64.
+// The two-wave instances need K to be a multiple of two steps: 64 (bf16) or 128 (fp8) values.
 bool two_wave_ok(const ge_desc_t* d);
 
 ge::TileKind pick_tile(const ge_desc_t* d, bool pair) {
@@ -109,7 +109,7 @@ ge::TileKind pick_tile(const ge_desc_t* d, bool pair) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 bool two_wave_ok(const ge_desc_t* d) {
-  return d->a_type == GE_DT_BF16 && d->K % 64 == 0;
+  return d->K % (d->a_type == GE_DT_FP8_E4M3 ? 128 : 64) == 0;
 }
 
 }  // namespace

@@ -84,6 +84,8 @@ hipError_t launch_tile_256x256w8_kn(int act, bool fp8_out, const Params& p, hipS
 hipError_t launch_tile_256x128w8_pair_kn(int act, bool fp8_out, const Params& p, hipStream_t stream);
 hipError_t launch_tile_256x256w8_nk(int act, bool fp8_out, const Params& p, hipStream_t stream);
 hipError_t launch_tile_256x128w8_pair_nk(int act, bool fp8_out, const Params& p, hipStream_t stream);
+hipError_t launch_tile_256x256w8_f8(int act, bool fp8_out, const Params& p, hipStream_t stream);
+hipError_t launch_tile_256x128w8_pair_f8(int act, bool fp8_out, const Params& p, hipStream_t stream);
 // fp8-e4m3 operands, B laid out [N][K]
 hipError_t launch_tile_256x256_f8(int act, bool fp8_out, const Params& p, hipStream_t stream);
 hipError_t launch_tile_256x128_pair_f8(int act, bool fp8_out, const Params& p, hipStream_t stream);

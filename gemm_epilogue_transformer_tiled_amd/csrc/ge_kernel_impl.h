@@ -206,7 +206,7 @@ template <class T, int ACT, bool GRAD, bool FP8, bool ROWSTAT, bool KMASK, bool 
 __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(T::WPE, T::WPE)))
 void fused_gemm_epilogue(Params p) {
   constexpr bool PP = T::WAVES == 8;              // two waves per SIMD, alternating phases
-  static_assert(!PP || (!F8IN && !KMASK), "the two-wave instances: bf16 operands, K % 64 == 0");
+  static_assert(!PP || !KMASK, "the two-wave instances: K a multiple of two steps");
   constexpr int ES = F8IN ? 1 : 2;                // bytes per operand element
   constexpr int BKE = F8IN ? 64 : T::BK;          // K values per step (64 bytes of a row)
   constexpr uint32_t EPC = 16 / ES;               // K values per 16-byte chunk
@@ -728,8 +728,14 @@ void fused_gemm_epilogue(Params p) {
         issue_b(bstage(FillB{}), (j + 3) * BKE);
         if constexpr (EVEN) issue_a((j + 2) * BKE, aslot(FillA{}));
       }
-      read_frags(aslot(Cur{}), bstage(Cur{}), S % 2, 0, fr0);
-      read_frags(aslot(Cur{}), bstage(Cur{}), S % 2, 1, fr1);
+      if constexpr (F8IN) {
+        // fp8 operands: one 64-deep step, one register set (the matrix phase uses it whole)
+        read_a8(aslot(Cur{}), S % 2, fa8[0]);
+        read_b8(bstage(Cur{}), S % 2, Q0c{}, QNc{});
+      } else {
+        read_frags(aslot(Cur{}), bstage(Cur{}), S % 2, 0, fr0);
+        read_frags(aslot(Cur{}), bstage(Cur{}), S % 2, 1, fr1);
+      }
       bf16x8_t sq[4];
       if constexpr (ROWSTAT && !EVEN) {
 #pragma unroll
@@ -758,8 +764,12 @@ void fused_gemm_epilogue(Params p) {
     };
     auto mat_phase = [&]() {
       __builtin_amdgcn_s_setprio(1);
-      mfmas(fr0);
-      mfmas(fr1);
+      if constexpr (F8IN) {
+        mfma8(fa8[0], Q0c{}, QNc{});
+      } else {
+        mfmas(fr0);
+        mfmas(fr1);
+      }
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_s_barrier();
     };
@@ -1217,6 +1227,32 @@ hipError_t launch_pp(const Params& p, hipStream_t s) {
                        dim3(T::NT), 0, s, p);
   }
   return hipGetLastError();
+}
+
+// Two-wave instances with fp8 operands (B given [N][K]): forward epilogues, no row statistic
+// (checked on the host), K a multiple of 128 (one slot: two 64-deep steps).
+template <class T, int ACT, bool FP8>
+hipError_t launch_pp8(const Params& p, hipStream_t s) {
+  static_assert(T::WAVES == 8, "two-wave tile");
+  const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * p.batch;
+  if (grid <= 0) return hipSuccess;
+  if ((p.flags & (F_ACT_GRAD | F_ROW_RMS)) || !(p.flags & F_IN_FP8) || !(p.flags & F_B_NK) || p.K % 128 != 0)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL((fused_gemm_epilogue<T, ACT, false, FP8, false, false, true, true>), dim3((unsigned)grid),
+                     dim3(T::NT), 0, s, p);
+  return hipGetLastError();
+}
+
+template <class T>
+hipError_t launch_tile_pp8(int act, bool fp8, const Params& p, hipStream_t s) {
+  switch (act) {
+    case ACT_NONE: return fp8 ? launch_pp8<T, ACT_NONE, true>(p, s) : launch_pp8<T, ACT_NONE, false>(p, s);
+    case ACT_RELU: return fp8 ? launch_pp8<T, ACT_RELU, true>(p, s) : launch_pp8<T, ACT_RELU, false>(p, s);
+    case ACT_GELU_TANH:
+      return fp8 ? launch_pp8<T, ACT_GELU_TANH, true>(p, s) : launch_pp8<T, ACT_GELU_TANH, false>(p, s);
+    case ACT_SILU: return fp8 ? launch_pp8<T, ACT_SILU, true>(p, s) : launch_pp8<T, ACT_SILU, false>(p, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <class T, bool BNK>

@@ -19,6 +19,16 @@ __global__ void amax_zero_kernel(uint32_t* amax) {
 }  // namespace
 
 hipError_t launch_fused(TileKind kind, int act, bool fp8_out, const Params& p, hipStream_t stream) {
+  if (two_wave_tile(kind)) {
+    if (p.flags & F_IN_FP8)
+      return kind == TILE_256x256_2W ? launch_tile_256x256w8_f8(act, fp8_out, p, stream)
+                                     : launch_tile_256x128w8_pair_f8(act, fp8_out, p, stream);
+    if (p.flags & F_B_NK)
+      return kind == TILE_256x256_2W ? launch_tile_256x256w8_nk(act, fp8_out, p, stream)
+                                     : launch_tile_256x128w8_pair_nk(act, fp8_out, p, stream);
+    return kind == TILE_256x256_2W ? launch_tile_256x256w8_kn(act, fp8_out, p, stream)
+                                   : launch_tile_256x128w8_pair_kn(act, fp8_out, p, stream);
+  }
   if (p.flags & F_IN_FP8) {
     switch (kind) {
       case TILE_256x256: return launch_tile_256x256_f8(act, fp8_out, p, stream);
@@ -26,15 +36,8 @@ hipError_t launch_fused(TileKind kind, int act, bool fp8_out, const Params& p, h
       case TILE_128x128: return launch_tile_128x128_f8(act, fp8_out, p, stream);
       case TILE_64x64: return launch_tile_64x64_f8(act, fp8_out, p, stream);
       case TILE_128x128_PAIR: return launch_tile_128x128_pair_f8(act, fp8_out, p, stream);
-      default: return hipErrorInvalidValue;   // (no fp8-operand two-wave instances)
+      default: return hipErrorInvalidValue;
     }
-  }
-  if (two_wave_tile(kind)) {
-    if (p.flags & F_B_NK)
-      return kind == TILE_256x256_2W ? launch_tile_256x256w8_nk(act, fp8_out, p, stream)
-                                     : launch_tile_256x128w8_pair_nk(act, fp8_out, p, stream);
-    return kind == TILE_256x256_2W ? launch_tile_256x256w8_kn(act, fp8_out, p, stream)
-                                   : launch_tile_256x128w8_pair_kn(act, fp8_out, p, stream);
   }
   switch (kind) {
     case TILE_256x256: return (p.flags & F_B_NK) ? launch_tile_256x256_nk(act, fp8_out, p, stream)

@@ -126,8 +126,8 @@ typedef enum { GE_LAYOUT_KN = 0, GE_LAYOUT_NK = 1 } ge_layout_t;
 
 /* Kernel instances (output tile shapes).  The first five run 4 waves of 64 lanes (2 x 2 over the
  * tile, one wave per SIMD); the _2W ones run 8 waves (2 x 4, two waves per SIMD that alternate
- * between memory work and matrix-core work) and exist for bf16 operands with K a multiple of 64
- * (other descriptors that request them get GE_ERR_UNSUPPORTED).  The pairwise instances hold two accumulators (gate and up).  With
+ * between memory work and matrix-core work) and need K to be a multiple of 64 (bf16 operands) or
+ * 128 (fp8 operands); other descriptors that request them get GE_ERR_UNSUPPORTED.  The pairwise instances hold two accumulators (gate and up).  With
  * tile = 0 the library takes a _2W instance where it applies and the grid has >= 256
  * workgroups of its shape. */
 typedef enum {

@@ -270,3 +270,56 @@ def test_fp8_output_feeds_the_next_layer():
     assert in2["A"].shape == (1, l2.M, l2.K) and in2["A"].dtype == np.uint8
     p2 = gpu_run(l2, in2)
     compare(l2, in2, p2, "layer 2 on layer-1 codes")
+
+
+# ---------------------------------------------------------------------------------------------
+# Two-wave instances (8 waves, two per SIMD) with fp8 operands: K a multiple of 128 (one slot
+# holds two 64-deep steps); K of 0, 1, 2, 3 and 5 slots covers whole and partial rings.
+# ---------------------------------------------------------------------------------------------
+
+TWO_WAVE8 = dict(batch=2, M=300, N=264, K=256)
+
+
+def run_two_wave8(w, inp):
+    prob = gpu_run(w, inp, 6 if w.pairwise else 5)
+    assert "threads=512" in prob.plan.describe() and "in=fp8" in prob.plan.describe(), prob.plan.describe()
+    return prob
+
+
+@pytest.mark.parametrize("w0", [F3, F3_BF16], ids=["fp8out", "bf16out"])
+def test_two_wave_ragged(w0):
+    w = w0.with_shape(**TWO_WAVE8)
+    inp = workloads.generate(w)
+    compare(w, inp, run_two_wave8(w, inp), f"fp8 operands {w.out} two-wave")
+
+
+@pytest.mark.parametrize("K", [0, 128, 256, 384, 640])
+def test_two_wave_k_steps(K):
+    w = F3_BF16.with_shape(batch=1, M=136, N=264, K=K)
+    inp = workloads.generate(w)
+    compare(w, inp, run_two_wave8(w, inp), f"fp8 operands two-wave K={K}")
+
+
+def test_two_wave_pairwise_and_residual():
+    w = dataclasses.replace(F3, out="bf16", chain=(("scale",), ("pairwise", "silu"))).with_shape(**TWO_WAVE8)
+    inp = workloads.generate(w)
+    compare(w, inp, run_two_wave8(w, inp), "fp8 operands pairwise two-wave")
+    w = dataclasses.replace(F3, out="bf16",
+                            chain=(("scale",), ("act", "relu"), ("residual",), ("amax",))).with_shape(**TWO_WAVE8)
+    inp = workloads.generate(w)
+    compare(w, inp, run_two_wave8(w, inp), "fp8 operands relu + residual two-wave")
+
+
+def test_two_wave_refuses_k_not_a_multiple_of_128():
+    ops = ge.make_ops((("scale",), ("act", "relu")))
+    kw = dict(a_type=ge.GE_DT_FP8_E4M3, b_type=ge.GE_DT_FP8_E4M3, b_layout=ge.GE_LAYOUT_NK, tile=5)
+    assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 256, ops, **kw)) == ge.GE_OK
+    assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 192, ops, **kw)) == ge.GE_ERR_UNSUPPORTED
+
+
+def test_two_wave_full_workload():
+    w = F3
+    inp = workloads.generate(w)
+    prob = run_two_wave8(w, inp)
+    compare(w, inp, prob, "f3 full two-wave, sampled rows", rows=FULL_ROWS)
+    check_amax(prob.amax_host(), oracle.run_workload(w, inp).amax, "f3 full two-wave")

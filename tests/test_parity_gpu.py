@@ -664,8 +664,8 @@ def test_two_wave_backward_chains(chain, layout):
 
 
 def test_two_wave_is_refused_where_it_does_not_apply():
-    """A requested two-wave instance with fp8 operands or K not a multiple of 64 is
-    GE_ERR_UNSUPPORTED at validation."""
+    """A requested two-wave instance with K not a multiple of two steps (64 bf16 or 128 fp8
+    values) is GE_ERR_UNSUPPORTED at validation."""
     ops = ge.make_ops((("scale",), ("act", "relu")))
     assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 192, ops, tile=5)) == ge.GE_OK
     assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 200, ops, tile=5)) == ge.GE_ERR_UNSUPPORTED
@@ -679,15 +679,15 @@ def test_two_wave_is_refused_where_it_does_not_apply():
     assert ge.gemm_epilogue_validate(ge.make_desc(1, 256, 256, 200, grad, tile=5)) == ge.GE_ERR_UNSUPPORTED
     f8 = ge.make_desc(1, 256, 256, 192, ops, tile=5, a_type=ge.GE_DT_FP8_E4M3, b_type=ge.GE_DT_FP8_E4M3,
                       b_layout=ge.GE_LAYOUT_NK)
-    assert ge.gemm_epilogue_validate(f8) == ge.GE_ERR_UNSUPPORTED
+    assert ge.gemm_epilogue_validate(f8) == ge.GE_ERR_UNSUPPORTED          # fp8: K % 128
 
 
 @pytest.mark.parametrize("name,threads", [("c1", 256), ("c2", 512), ("c3", 512), ("c4", 512), ("c5", 512),
-                                          ("f1", 512), ("f2", 512), ("f3", 256)])
+                                          ("f1", 512), ("f2", 512), ("f3", 512)])
 def test_default_instance(name, threads):
-    """With no tile requested the library takes the two-wave instances for the chains they cover
-    at >= 256 workgroups (c2 .. c5, f1, f2) and the one-wave-per-SIMD instances elsewhere (fp8
-    operands, small grids)."""
+    """With no tile requested the library takes the two-wave instances wherever they apply at
+    >= 256 workgroups (c2 .. c5, f1 .. f3) and the one-wave-per-SIMD instances for small grids
+    (c1)."""
     assert not os.environ.get("GE_FORCE_TILE")
     h = ge.gemm_epilogue_create(runner.descriptor(workloads.WORKLOADS[name]))
     try:

@@ -33,11 +33,12 @@ def test_admissible_tiles_match_the_chain_and_the_lds_budget():
     pair = _desc([("pairwise", "silu")])
     assert tuning.admissible_tiles(single) == [0, 2, 3, 5]
     assert tuning.admissible_tiles(pair) == [1, 4, 6]
-    # the two-wave instances only where they apply: not for K % 64 != 0 or fp8 operands
+    # the two-wave instances only where they apply: K a multiple of two steps (64 bf16, 128 fp8)
     assert tuning.admissible_tiles(ge.make_desc(1, 512, 512, 520, ge.make_ops([("scale",)]))) == [0, 2, 3]
     assert tuning.admissible_tiles(_desc([("scale",)], b_layout=ge.GE_LAYOUT_NK)) == [0, 2, 3, 5]
-    f8 = _desc([("scale",)], b_layout=ge.GE_LAYOUT_NK, a_type=ge.GE_DT_FP8_E4M3, b_type=ge.GE_DT_FP8_E4M3)
-    assert tuning.admissible_tiles(f8) == [0, 2, 3]
+    f8 = dict(b_layout=ge.GE_LAYOUT_NK, a_type=ge.GE_DT_FP8_E4M3, b_type=ge.GE_DT_FP8_E4M3)
+    assert tuning.admissible_tiles(_desc([("scale",)], **f8)) == [0, 2, 3, 5]
+    assert tuning.admissible_tiles(ge.make_desc(1, 512, 512, 576, ge.make_ops([("scale",)]), **f8)) == [0, 2, 3]
     # a tighter budget removes the instances that allocate more LDS
     lds = {t: ge.gemm_epilogue_tile_info(t).lds_bytes for t in SHAPES}
     budget = lds[ge.GE_TILE_64x64]
