@@ -106,6 +106,8 @@ def parse():
                          "the fastest")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bare", action="store_true", help="skip the bare-GEMM comparison")
+    ap.add_argument("--breakdown", action="store_true",
+                    help="also time the chain with each epilogue op left out, in turn (per-op cost)")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache single-launch timing")
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused-sequence comparison")
     ap.add_argument("--no-probes", action="store_true", help="skip the MFMA / copy calibration probes")
@@ -225,6 +227,30 @@ def cold_launches(prob, n, flops):
 
 def bare_chain(w):
     return (("pairwise", "none"),) if w.pairwise else ()
+
+
+# ops that define the kind of output rather than a step of the epilogue; never left out
+STRUCTURAL_OPS = ("pairwise", "quant_fp8")
+
+
+def chain_breakdown(w, inputs, prob, args, mode):
+    """ms per step of the full chain, of the bare store, and of the chain with each epilogue op
+    left out in turn (same instance rule, same inputs): full - without_op is that op's cost."""
+    from gemm_epilogue_transformer_tiled_amd import runner
+
+    out = {"full_ms": round(time_launches(prob, args.steps, args.warmup, mode)[0], 6)}
+    variants = [("bare", w.__class__(**{**w.__dict__, "chain": bare_chain(w), "out": "bf16", "name": w.name + "-bare"}))]
+    for op in w.chain:
+        if op[0] in STRUCTURAL_OPS:
+            continue
+        chain = tuple(o for o in w.chain if o is not op)
+        variants.append((f"without_{op[0]}", w.__class__(**{**w.__dict__, "chain": chain, "name": w.name + "-" + op[0]})))
+    for name, wv in variants:
+        pv = runner.prepare(wv, inputs)
+        out[name + "_ms"] = round(time_launches(pv, args.steps, args.warmup, mode)[0], 6)
+        del pv
+    out["full_again_ms"] = round(time_launches(prob, args.steps, 0, mode)[0], 6)
+    return out
 
 
 def cpu_baseline(w, inputs, seconds):
@@ -378,6 +404,8 @@ def run_one(args):
         result["bare_gemm_ms"] = round(bare_ms, 6)
         result["epilogue_overhead_pct"] = round(((launch_ms + again_ms) / 2 / bare_ms - 1.0) * 100.0, 2)
         del bare
+    if args.breakdown:
+        result["breakdown"] = chain_breakdown(w, inputs, prob, args, mode)
     if not args.no_cold:
         result["cold"] = cold_launches(prob, min(args.steps, 20), flops)
     if not args.no_unfused:
