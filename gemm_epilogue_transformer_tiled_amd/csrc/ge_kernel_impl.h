@@ -688,6 +688,21 @@ void fused_gemm_epilogue(Params p) {
     //     partner wave's memory work fills the issue slots the MFMAs leave.
     const int grp = wave >> 2;
     Frags fr0, fr1;
+    // Step resources: K is a multiple of two steps here, so a step is wholly inside or outside
+    // [0, K), and an outside step needs only an empty extent (its base is never used): one
+    // unsigned compare instead of the clamps of the general case.
+    const uint32_t a_ext32 = (uint32_t)a_ext, b_ext32 = (uint32_t)b_ext;
+    auto rs_pp = [&](const unsigned char* base, uint32_t ext, int k0, uint32_t bytes_per_k) {
+      const uint32_t off = (uint32_t)k0 * bytes_per_k;
+      return make_rsrc(base + off, (uint32_t)k0 < (uint32_t)K ? (int64_t)(ext - off) : 0);
+    };
+    auto set_rs_pp = [&](int ka, int kb) {
+      ars = rs_pp(a_base, a_ext32, ka, ES);
+      const int kbb = BNK ? ka : kb;
+      const uint32_t bpk = BNK ? (uint32_t)ES : ldb2;
+      brs = rs_pp(b_base, b_ext32, kbb, bpk);
+      if constexpr (T::PAIR) b2rs = rs_pp(b2_base, b_ext32, kbb, bpk);
+    };
     // Row statistic: in the memory phase of each odd step j every lane squares half of one
     // row of the A slot of steps j-1 and j (its last use): slot row (wave % 4) * 64 + lane,
     // physical chunks sq_c ^ i (i < 4), where sq_c's bit 2 is the wave group, so the two
@@ -700,13 +715,13 @@ void fused_gemm_epilogue(Params p) {
     float ss1 = 0.0f;
     const uint32_t sq_row = (uint32_t)((wave & 3) * 64 + lane) * T::A_ROWB;
     const uint32_t sq_c = ((uint32_t)((lane & 15) + ((lane & 15) >> 3)) & 7u) ^ (uint32_t)(4 * grp);
-    GE_SET_RS(kt * BKE, kt * BKE);
+    set_rs_pp(kt * BKE, kt * BKE);
     issue_a(kt * BKE, aslot(S0{}));
     issue_b(bstage(S0{}), kt * BKE);
     if constexpr (!BNK) {
-      GE_SET_RS(kt * BKE, (kt + 1) * BKE);
+      set_rs_pp(kt * BKE, (kt + 1) * BKE);
       issue_b(bstage(S1{}), (kt + 1) * BKE);
-      GE_SET_RS(kt * BKE, (kt + 2) * BKE);
+      set_rs_pp(kt * BKE, (kt + 2) * BKE);
       issue_b(bstage(S2{}), (kt + 2) * BKE);
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(BNK ? 0 : 2 * T::B_LOADS));   // A slot and B of step kt landed
@@ -718,7 +733,7 @@ void fused_gemm_epilogue(Params p) {
       using Cur = std::integral_constant<int, S>;
       using FillA = std::integral_constant<int, S + 2>;
       using FillB = std::integral_constant<int, S + 3>;
-      GE_SET_RS((j + 2) * BKE, (j + 3) * BKE);
+      set_rs_pp((j + 2) * BKE, (j + 3) * BKE);
       if constexpr (BNK) {
         if constexpr (EVEN) {
           issue_a((j + 2) * BKE, aslot(FillA{}));
