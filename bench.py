@@ -108,6 +108,8 @@ def parse():
     ap.add_argument("--no-bare", action="store_true", help="skip the bare-GEMM comparison")
     ap.add_argument("--breakdown", action="store_true",
                     help="also time the chain with each epilogue op left out, in turn (per-op cost)")
+    ap.add_argument("--vendor", action="store_true",
+                    help="also time the workload's bare GEMM through torch.matmul (hipBLASLt), same layout")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache single-launch timing")
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused-sequence comparison")
     ap.add_argument("--no-probes", action="store_true", help="skip the MFMA / copy calibration probes")
@@ -227,6 +229,44 @@ def cold_launches(prob, n, flops):
 
 def bare_chain(w):
     return (("pairwise", "none"),) if w.pairwise else ()
+
+
+class _VendorGemm:
+    """The workload's product alone through torch.matmul (hipBLASLt on ROCm), bf16 in and out,
+    on the same device tensors ([batch, rows, cols]): B [K][N] as is, B [N][K] (batch 1 only)
+    as a transposed view of a 2-D matrix (the library's K-contiguous kernel), the pairwise
+    product as one GEMM over [B | B2]."""
+
+    def __init__(self, w, prob):
+        import torch
+
+        A, B = prob.tensors["A"], prob.tensors["B"]
+        nk = getattr(w, "b_layout", "kn") == "nk"
+        if w.pairwise:
+            B = torch.cat([B, prob.tensors["B2"]], dim=1 if nk else 2)
+        if nk:
+            # 2-D only: a batched bf16 product with a transposed right operand is avoided
+            assert A.shape[0] == 1 and B.shape[0] == 1
+            A, B = A[0], B[0].t()
+        self.A, self.B = A, B
+        self.Y = torch.empty(*A.shape[:-1], B.shape[-1], dtype=torch.bfloat16, device=A.device)
+
+    def run(self, stream=None):
+        import torch
+
+        torch.matmul(self.A, self.B, out=self.Y)
+
+
+def vendor_bare_gemm(w, prob, args, mode):
+    """ms per step and TFLOP/s of the vendor library's bare GEMM on the workload (bf16 operands
+    only; None for fp8 operands)."""
+    if getattr(w, "in_dtype", "bf16") != "bf16" or (getattr(w, "b_layout", "kn") == "nk" and w.batch != 1):
+        return None
+    v = _VendorGemm(w, prob)
+    ms, vmode, _ = time_launches(v, args.steps, args.warmup, mode)
+    del v
+    return {"library": "torch.matmul (hipBLASLt)", "ms_per_step": round(ms, 6),
+            "tflops": round(w.flops() / (ms * 1e-3) / 1e12, 3), "launch_mode": vmode}
 
 
 # ops that define the kind of output rather than a step of the epilogue; never left out
@@ -406,6 +446,8 @@ def run_one(args):
         del bare
     if args.breakdown:
         result["breakdown"] = chain_breakdown(w, inputs, prob, args, mode)
+    if args.vendor:
+        result["vendor_bare_gemm"] = vendor_bare_gemm(w, prob, args, mode)
     if not args.no_cold:
         result["cold"] = cold_launches(prob, min(args.steps, 20), flops)
     if not args.no_unfused:
