@@ -63,9 +63,9 @@ ABNORMAL_RC = {-6, -9, -11, -15, 124, 134, 137, 139}
 # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE (x2.0) + WRITE_SIZE (x1.0) of the fused
 # kernel at each workload; the factors scale the counters to the bytes of a plain 1 GiB device
 # copy.  Valid only for the kernel source they were taken on (sha256 prefix below).
-MEASURED_TRAFFIC_SOURCE = "204cbce0bc73625a"
-MEASURED_TRAFFIC = {"c1": 1066177, "c2": 101045783, "c3": 2384938526, "c4": 537304736, "c5": 1694951166,
-                    "f1": 2389946665, "f2": 1829360954, "f3": 877692112}
+MEASURED_TRAFFIC_SOURCE = "c8b052bce7104966"
+MEASURED_TRAFFIC = {"c1": 1066178, "c2": 101030452, "c3": 2381450395, "c4": 537329825, "c5": 1685808689,
+                    "f1": 2387676023, "f2": 1809803177, "f3": 877331184}
 
 
 def kernel_source_hash():
