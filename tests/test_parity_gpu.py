@@ -706,3 +706,35 @@ def test_two_wave_full_workload(name):
     compare(w, inp, prob, f"{name} two-wave full", rows=rows)
     if rows is not None and w.has("amax"):
         check_amax(prob.amax_host(), oracle.run_workload(w, inp).amax, f"{name} two-wave full amax")
+
+
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+def test_two_wave_strided_operands_and_broadcast_b(layout):
+    """Two-wave instance: lda > K, a padded ldb and a batch stride of 0 on B (one weight shared
+    by every batch), ragged M and N, in both B layouts."""
+    batch, M, N, K = 3, 300, 264, 192
+    nk = layout == "nk"
+    lda, ldb = K + 40, (K + 24 if nk else N + 24)
+    w = dataclasses.replace(workloads.WORKLOADS["c2"], b_layout=layout).with_shape(batch=batch, M=M, N=N, K=K)
+    inp = workloads.generate(w, sensitive=True)
+    A_pad = np.zeros((batch, M, lda), dtype=np.uint16)
+    A_pad[:, :, :K] = inp["A"]
+    rows, cols = (N, K) if nk else (K, N)
+    B_pad = np.zeros((1, rows, ldb), dtype=np.uint16)
+    B_pad[0, :, :cols] = inp["B"][0]
+    dev = "cuda"
+    A = runner.to_device_bf16(A_pad, dev)
+    B = runner.to_device_bf16(B_pad, dev)
+    bias = runner.to_device_bf16(inp["bias"], dev)
+    Y = torch.empty((batch, M, N), dtype=torch.bfloat16, device=dev)
+    amax = torch.zeros(1, dtype=torch.float32, device=dev)
+    desc = ge.make_desc(batch, M, N, K, ge.make_ops(w.chain), lda=lda, ldb=ldb, stride_b=0, tile=TWO_WAVE["single"],
+                        b_layout=ge.GE_LAYOUT_NK if nk else ge.GE_LAYOUT_KN)
+    plan = ge.Plan(desc)
+    assert "threads=512" in plan.describe(), plan.describe()
+    plan.run(ge.make_args(A=A, B=B, bias=bias, Y=Y, amax=amax, alpha=w.alpha))
+    torch.cuda.synchronize()
+    B_bcast = np.repeat(inp["B"][:1], batch, axis=0)
+    ref = oracle.run_chain(w.chain, inp["A"], B_bcast, bias=inp["bias"], alpha=w.alpha, b_layout=layout)
+    check_bf16(Y.cpu().view(torch.int16).numpy().view(np.uint16), ref.y, f"two-wave strided {layout}")
+    check_amax(float(amax.item()), ref.amax, f"two-wave strided {layout}")
