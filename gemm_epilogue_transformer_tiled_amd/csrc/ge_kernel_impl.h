@@ -738,7 +738,7 @@ void fused_gemm_epilogue(Params p) {
       // their LDS latency) measured +1 to +4.5 % on B [K][N] and fp8 operands, -1 % on bf16
       // B [N][K] (whose even steps carry all eight loads): loads first there.
       auto issue_loads = [&]() {
-        // resources: set by the previous matrix phase (or the prologue) for this step
+        set_rs_pp((j + 2) * BKE, (j + 3) * BKE);
         if constexpr (BNK) {
           if constexpr (EVEN) {
             issue_a((j + 2) * BKE, aslot(FillA{}));
@@ -789,9 +789,7 @@ void fused_gemm_epilogue(Params p) {
       }
       __builtin_amdgcn_s_barrier();
     };
-    // matrix phase of step j; it also sets the resources of the loads of the next memory
-    // phase (step j+1: A slot at j+3, B at j+4) -- scalar work its wave has issue slots for
-    auto mat_phase = [&](int j) {
+    auto mat_phase = [&]() {
       __builtin_amdgcn_s_setprio(1);
       if constexpr (F8IN) {
         mfma8(fa8[0], Q0c{}, QNc{});
@@ -799,20 +797,18 @@ void fused_gemm_epilogue(Params p) {
         mfmas(fr0);
         mfmas(fr1);
       }
-      set_rs_pp((j + 3) * BKE, (j + 4) * BKE);
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_s_barrier();
     };
-    set_rs_pp((kt + 2) * BKE, (kt + 3) * BKE);                // the first memory phase's loads
     for (; kt < nk; kt += T::NS) {
       mem_phase(S0{}, kt);
-      mat_phase(kt);
+      mat_phase();
       mem_phase(S1{}, kt + 1);
-      mat_phase(kt + 1);
+      mat_phase();
       mem_phase(S2{}, kt + 2);
-      mat_phase(kt + 2);
+      mat_phase();
       mem_phase(S3{}, kt + 3);
-      mat_phase(kt + 3);
+      mat_phase();
     }
     if (grp == 0) __builtin_amdgcn_s_barrier();               // matches group 1's last phase
     if constexpr (ROWSTAT) row_ss[grp * T::BM + (wave & 3) * 64 + lane] = ss1;
