@@ -63,9 +63,9 @@ ABNORMAL_RC = {-6, -9, -11, -15, 124, 134, 137, 139}
 # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE (x2.0) + WRITE_SIZE (x1.0) of the fused
 # kernel at each workload; the factors scale the counters to the bytes of a plain 1 GiB device
 # copy.  Valid only for the kernel source they were taken on (sha256 prefix below).
-MEASURED_TRAFFIC_SOURCE = "c8b052bce7104966"
-MEASURED_TRAFFIC = {"c1": 1066178, "c2": 101030452, "c3": 2381450395, "c4": 537329825, "c5": 1685808689,
-                    "f1": 2387676023, "f2": 1809803177, "f3": 877331184}
+MEASURED_TRAFFIC_SOURCE = "5b364dc76a07e471"
+MEASURED_TRAFFIC = {"c1": 1066178, "c2": 101018705, "c3": 2406239665, "c4": 537293905, "c5": 1684358980,
+                    "f1": 2390124653, "f2": 1775022972, "f3": 877306467}
 
 
 def kernel_source_hash():
