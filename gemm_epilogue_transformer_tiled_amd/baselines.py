@@ -204,7 +204,8 @@ class Unfused:
 
 
 def probe_mfma(workgroups: int = 1024, iters: int = 4096) -> Dict:
-    """Sustained matrix-core TFLOP/s (v_mfma_f32_32x32x16_bf16 on register data)."""
+    """Sustained matrix-core TFLOP/s (v_mfma_f32_32x32x16_bf16 on random register operands that
+    change from one instruction to the next)."""
     sink = torch.empty(workgroups * 256, dtype=torch.float32, device="cuda")
     call("ge_probe_mfma", sink.data_ptr(), workgroups, 16, _stream())     # warm
     torch.cuda.synchronize()

@@ -242,19 +242,34 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const uint16_t* __restr
 }
 
 // ---- probes ----
+// Operand values for the matrix-core probe: random bf16 in [-2, 2) from a hash of (thread, set,
+// element), so that, as in a GEMM's inner loop, consecutive instructions see unrelated bits.
+__device__ __forceinline__ uint32_t probe_hash(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352dU;
+  x ^= x >> 15;
+  x *= 0x846ca68bU;
+  x ^= x >> 16;
+  return x;
+}
+
 __global__ __launch_bounds__(256) void mfma_probe(float* sink, int iters) {
-  bf16x8_t a, b;
+  const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+  bf16x8_t a[4], b[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    a[i] = (__bf16)(1e-3f * (float)(threadIdx.x + i));
-    b[i] = (__bf16)(1e-3f * (float)(i - (int)threadIdx.x));
-  }
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a[s][i] = (__bf16)(((float)(probe_hash(t * 64 + s * 8 + i) & 0xFFFF) - 32768.0f) / 16384.0f);
+      b[s][i] = (__bf16)(((float)(probe_hash(t * 64 + 32 + s * 8 + i) & 0xFFFF) - 32768.0f) / 16384.0f);
+    }
   f32x16_t acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = f32x16_t{};
   for (int it = 0; it < iters; ++it) {
+    // chain i takes operand sets (i % 4, i / 4): every instruction's operands differ from the last
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
+    for (int i = 0; i < 16; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % 4], b[i / 4], acc[i], 0, 0, 0);
   }
   float s = 0.0f;
 #pragma unroll

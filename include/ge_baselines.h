@@ -73,8 +73,10 @@ int ge_unfused_amax(const uint16_t* x, int64_t n, float* amax, void* stream);
 int ge_unfused_quant_fp8(const uint16_t* x, uint8_t* y, int64_t n, float scale, void* stream);
 
 /* Matrix-core probe: `workgroups` workgroups of 4 waves, each wave running 16 independent
- * chains of `iters` v_mfma_f32_32x32x16_bf16 on register data; `sink` receives
- * workgroups * 256 floats (keeps the work live).  Floating-point work per launch:
+ * chains of `iters` v_mfma_f32_32x32x16_bf16 on random register operands (four sets per
+ * source, so consecutive instructions see different bits, as in a GEMM -- the matrix core's
+ * power, and so its sustained rate, depends on the data); `sink` receives workgroups * 256
+ * floats (keeps the work live).  Floating-point work per launch:
  * workgroups * 4 * 16 * iters * 32768. */
 int ge_probe_mfma(float* sink, int workgroups, int iters, void* stream);
 
