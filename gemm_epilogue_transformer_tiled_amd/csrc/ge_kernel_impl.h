@@ -15,7 +15,8 @@
 // superoptimizer write-up's section 9 is gathered from the A operand while it
 // is staged, so no separate scale kernel or round trip of S is needed.
 //
-// Mainloop design (per workgroup of 4 waves, 2 x 2 over the output tile):
+// Mainloop design (one-wave instances: a workgroup of 4 waves, 2 x 2 over the output tile,
+// one wave per SIMD; the two-wave instances below differ in how the waves take turns):
 //   * Operands reach LDS with direct global->LDS buffer loads (16 bytes per lane, 1 KB per
 //     instruction, no register staging).  Out-of-range rows, columns and K chunks are
 //     given an offset past the buffer extent, so the hardware returns zeros -- ragged
@@ -35,6 +36,11 @@
 //     loads and Y stores cover whole rows.
 //   * Workgroup ids are remapped so each XCD (own L2) receives a contiguous run of tiles,
 //     which are then walked in groups of 8 tile-rows for L2 reuse.
+//   * Two-wave instances (8 waves, 2 x 4 over a 256-row tile, two per SIMD): the same LDS
+//     stages and slots, but the waves form two groups of four that alternate a memory phase
+//     (this step's fragment reads, later steps' loads, waits) and a matrix phase (MFMAs only,
+//     at raised priority), one phase apart, so one wave per SIMD keeps the matrix core busy
+//     while the other waits on memory; the row statistic comes from the staged A slots.
 #include <type_traits>
 #include <utility>
 
