@@ -14,6 +14,9 @@ from typing import Iterable, Optional, Sequence, Tuple
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgemm_epilogue.so")
+# The reference build of the same sources: the one-wave instances with a mainloop that
+# overlaps nothing, bit-identical to this library by construction (race tests only).
+SERIAL_LIB_PATH = os.path.join(_HERE, "libgemm_epilogue_serial.so")
 
 # ---- enums (mirror include/gemm_epilogue.h) ----
 GE_OK, GE_ERR_INVALID_ARG, GE_ERR_UNSUPPORTED, GE_ERR_DEVICE, GE_ERR_HIP, GE_ERR_SCRATCH = range(6)
@@ -74,17 +77,17 @@ EXPORTED = ("gemm_epilogue_validate", "gemm_epilogue_create", "gemm_epilogue_wor
             "gemm_epilogue_status_string", "gemm_epilogue_describe", "gemm_epilogue_tile_info")
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python gemm_epilogue_transformer_tiled_amd/build.py` "
+            f"{path} is not built; run `python gemm_epilogue_transformer_tiled_amd/build.py` "
             "(there is no host fallback for this library)")
     # One HIP runtime per process: torch ships its own libamdhip64 (DT_NEEDED
     # "libamdhip64.so", soname "libamdhip64.so.7").  Loading torch first makes this
     # library's "libamdhip64.so.7" dependency resolve to that same loaded runtime;
     # loading this library first would make torch pull in a second runtime.
     import torch  # noqa: F401
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     lib.gemm_epilogue_validate.argtypes = [ctypes.POINTER(ge_desc_t)]
     lib.gemm_epilogue_validate.restype = ctypes.c_int
     lib.gemm_epilogue_create.argtypes = [ctypes.POINTER(ge_desc_t), ctypes.POINTER(ge_handle_t)]
@@ -107,6 +110,15 @@ def _load() -> ctypes.CDLL:
 
 
 lib = _load()
+_serial_lib: Optional[ctypes.CDLL] = None
+
+
+def load_serial_library() -> ctypes.CDLL:
+    """The reference build (``SERIAL_LIB_PATH``), loaded once; pass it to ``Plan(library=...)``."""
+    global _serial_lib
+    if _serial_lib is None:
+        _serial_lib = _load(SERIAL_LIB_PATH)
+    return _serial_lib
 
 
 class GemmEpilogueError(RuntimeError):
@@ -239,19 +251,33 @@ def make_args(A=None, B=None, B2=None, bias=None, row_scale=None, residual=None,
 
 class Plan:
     """Owns one handle (and its zero-filled device workspace, allocated by torch):
-    create once, run many times on torch tensors and the current stream."""
+    create once, run many times on torch tensors and the current stream.  `library`: a
+    library loaded by this module (default: ``lib``; the reference build for race tests)."""
 
-    def __init__(self, desc: ge_desc_t, device="cuda"):
+    def __init__(self, desc: ge_desc_t, device="cuda", library: Optional[ctypes.CDLL] = None):
         self.desc = desc
-        self.handle = gemm_epilogue_create(desc)
+        self.lib = lib if library is None else library
+        h = ge_handle_t()
+        st = self.lib.gemm_epilogue_create(ctypes.byref(desc), ctypes.byref(h))
+        if st != GE_OK:
+            raise GemmEpilogueError(st, "gemm_epilogue_create")
+        self.handle = h.value
         self.workspace = None
-        nbytes = gemm_epilogue_workspace_size(self.handle)
+        n = ctypes.c_size_t()
+        st = self.lib.gemm_epilogue_workspace_size(self.handle, ctypes.byref(n))
+        if st != GE_OK:
+            raise GemmEpilogueError(st, "gemm_epilogue_workspace_size")
+        nbytes = n.value
         if nbytes:
             import torch
             self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
     def describe(self) -> str:
-        return gemm_epilogue_describe(self.handle)
+        buf = ctypes.create_string_buffer(256)
+        st = self.lib.gemm_epilogue_describe(self.handle, buf, len(buf))
+        if st != GE_OK:
+            raise GemmEpilogueError(st, "gemm_epilogue_describe")
+        return buf.value.decode()
 
     def run(self, args: ge_args_t, stream: Optional[int] = None) -> None:
         if stream is None:
@@ -260,13 +286,13 @@ class Plan:
         if self.workspace is not None and not args.workspace:
             args.workspace = self.workspace.data_ptr()
             args.workspace_bytes = self.workspace.numel()
-        st = gemm_epilogue_run(self.handle, args, stream)
+        st = self.lib.gemm_epilogue_run(self.handle, ctypes.byref(args), stream)
         if st != GE_OK:
             raise GemmEpilogueError(st, "gemm_epilogue_run")
 
     def close(self) -> None:
         if self.handle:
-            gemm_epilogue_destroy(self.handle)
+            self.lib.gemm_epilogue_destroy(self.handle)
             self.handle = None
 
     def __del__(self):

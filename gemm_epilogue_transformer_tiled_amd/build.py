@@ -1,5 +1,6 @@
-"""Builds libgemm_epilogue.so (the fused path) and libge_baselines.so (unfused comparators and
-calibration probes) in-tree with hipcc for gfx950.
+"""Builds libgemm_epilogue.so (the fused path), libgemm_epilogue_serial.so (its reference build:
+the one-wave instances with a mainloop that overlaps nothing, for bit-for-bit race tests) and
+libge_baselines.so (unfused comparators and calibration probes) in-tree with hipcc for gfx950.
 
 Usage: python gemm_epilogue_transformer_tiled_amd/build.py  (runs by path: importing the
 package itself needs the library this script builds)
@@ -14,14 +15,15 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
-# library -> its sources
+ONE_WAVE = [f"ge_tile_{t}_{lay}.hip" for t in ("256x256", "256x128_pair", "128x128", "64x64", "128x128_pair")
+            for lay in ("kn", "nk", "f8")]
+TWO_WAVE = [f"ge_tile_{t}_{lay}.hip" for t in ("256x256w8", "256x128w8_pair") for lay in ("kn", "nk", "f8")]
+COMMON = ["ge_kernels.hip", "noalloc.hip", "tiles.cpp", "api.cpp"]
+# library -> (its sources, extra compiler flags)
 TARGETS = {
-    os.path.join(HERE, "libgemm_epilogue.so"): [
-        f"ge_tile_{t}_{lay}.hip" for t in ("256x256", "256x128_pair", "128x128", "64x64", "128x128_pair")
-        for lay in ("kn", "nk", "f8")] + [f"ge_tile_{t}_{lay}.hip" for t in ("256x256w8", "256x128w8_pair")
-                                          for lay in ("kn", "nk", "f8")] + [
-        "ge_kernels.hip", "noalloc.hip", "tiles.cpp", "api.cpp"],
-    os.path.join(HERE, "libge_baselines.so"): ["baselines.hip"],
+    os.path.join(HERE, "libgemm_epilogue.so"): (ONE_WAVE + TWO_WAVE + COMMON, ()),
+    os.path.join(HERE, "libgemm_epilogue_serial.so"): (ONE_WAVE + COMMON, ("-DGE_SERIAL_PIPELINE=1",)),
+    os.path.join(HERE, "libge_baselines.so"): (["baselines.hip"], ()),
 }
 LIB = os.path.join(HERE, "libgemm_epilogue.so")
 
@@ -34,23 +36,25 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, extra = job
+    out_dir = os.path.join(BUILD_DIR, "serial") if extra else BUILD_DIR
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-6000:]}")
+        raise RuntimeError(f"hipcc failed for {src} {' '.join(extra)}:\n{r.stderr[-6000:]}")
     return obj
 
 
 def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    sources = [src for srcs in TARGETS.values() for src in srcs]
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(sources), os.cpu_count() or 4)) as ex:
-        objs = dict(zip(sources, ex.map(_compile, sources)))
-    for lib, srcs in TARGETS.items():
+    os.makedirs(os.path.join(BUILD_DIR, "serial"), exist_ok=True)
+    jobs = sorted({(src, extra) for srcs, extra in TARGETS.values() for src in srcs})
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 4)) as ex:
+        objs = dict(zip(jobs, ex.map(_compile, jobs)))
+    for lib, (srcs, extra) in TARGETS.items():
         tmp = lib + ".tmp"
-        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *[objs[s] for s in srcs]]
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *[objs[(s, extra)] for s in srcs]]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"link failed for {lib}:\n{r.stderr[-6000:]}")

@@ -109,6 +109,7 @@ ge::TileKind pick_tile(const ge_desc_t* d, bool pair) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 bool two_wave_ok(const ge_desc_t* d) {
+  if (GE_SERIAL_PIPELINE) return false;                     // the reference build has none
   return d->K % (d->a_type == GE_DT_FP8_E4M3 ? 128 : 64) == 0;
 }
 
@@ -448,11 +449,11 @@ ge_status_t gemm_epilogue_tile_info(int32_t tile, ge_tile_info_t* info) {
 ge_status_t gemm_epilogue_describe(ge_handle_t h, char* buf, size_t len) {
   if (!h || !buf || len == 0) return GE_ERR_INVALID_ARG;
   const ge::TileInfo ti = ge::tile_info(h->tile);
-  std::snprintf(buf, len, "tile=%dx%dx64 pair=%d in=%s b=%s threads=%d lds=%d grid=%lld act=%d fp8=%d flags=0x%x",
+  std::snprintf(buf, len, "tile=%dx%dx64 pair=%d in=%s b=%s threads=%d lds=%d grid=%lld act=%d fp8=%d flags=0x%x%s",
                 ti.bm, ti.bn, ti.pair ? 1 : 0, (h->flags & ge::F_IN_FP8) ? "fp8" : "bf16",
                 (h->flags & ge::F_B_NK) ? "NK" : "KN", ti.threads, ti.lds_bytes,
                 (long long)(h->tiles_m * h->tiles_n * h->desc.batch), h->act, h->fp8_out ? 1 : 0,
-                (unsigned)h->flags);
+                (unsigned)h->flags, GE_SERIAL_PIPELINE ? " pipeline=serial" : "");
   return GE_OK;
 }
 

@@ -4,6 +4,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Reference build: GE_SERIAL_PIPELINE=1 compiles the one-wave instances with a mainloop that
+// overlaps nothing (each two-step slot is loaded, waited for and read between two full
+// barriers) and leaves the two-wave instances out.  The MFMAs, their operands and their order
+// are those of the pipelined build, so its results are bit-identical to it; a difference
+// means a synchronisation mistake in the pipelined mainloop.
+#ifndef GE_SERIAL_PIPELINE
+#define GE_SERIAL_PIPELINE 0
+#endif
+
 namespace ge {
 
 // Epilogue flags decided at run time (uniform per launch).
@@ -34,8 +43,7 @@ enum TileKind : int {
   TILE_KIND_COUNT = 7
 };
 
-// The two-wave instances exist for forward epilogues on bf16 operands with B given [K][N] and
-// K a multiple of 64.
+// The two-wave instances need K to be a multiple of two steps (64 bf16 or 128 fp8 values).
 inline bool two_wave_tile(TileKind k) { return k == TILE_256x256_2W || k == TILE_256x128_PAIR_2W; }
 
 struct Params {

@@ -818,6 +818,41 @@ void fused_gemm_epilogue(Params p) {
     }
     if (grp == 0) __builtin_amdgcn_s_barrier();               // matches group 1's last phase
     if constexpr (ROWSTAT) row_ss[grp * T::BM + (wave & 3) * 64 + lane] = ss1;
+  } else if constexpr (GE_SERIAL_PIPELINE) {
+    // ---- reference build: one two-step slot at a time, nothing overlapped ----
+    // Load the slot's A and B (B [K][N]: both steps' stages), wait for every load, barrier;
+    // read and multiply steps k and k+1 with the pipelined build's fragments, MFMAs and order;
+    // wait for the reads, barrier, so no stage is refilled while a wave still reads it.
+    for (int k = kt; k < nk; k += 2) {
+      GE_SET_RS(k * BKE, k * BKE);
+      issue_a(k * BKE, aslot(S0{}));
+      issue_b(bstage(S0{}), k * BKE);
+      if constexpr (!BNK) {
+        GE_SET_RS(k * BKE, (k + 1) * BKE);
+        issue_b(bstage(S1{}), (k + 1) * BKE);
+      }
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      __builtin_amdgcn_s_barrier();
+      if constexpr (F8IN) {
+        read_a8(aslot(S0{}), 0, fa8[0]);
+        read_b8(bstage(S0{}), 0, Q0c{}, QNc{});
+        mfma8(fa8[0], Q0c{}, QNc{});
+        read_a8(aslot(S0{}), 1, fa8[0]);
+        read_b8(bstage(S0{}), 1, Q0c{}, QNc{});
+        mfma8(fa8[0], Q0c{}, QNc{});
+      } else {
+        read_frags(aslot(S0{}), bstage(S0{}), 0, 0, f0);
+        read_frags(aslot(S0{}), bstage(S0{}), 0, 1, f1);
+        mfmas(f0);
+        mfmas(f1);
+        read_frags(aslot(S1{}), bstage(S1{}), 1, 0, f0);
+        read_frags(aslot(S1{}), bstage(S1{}), 1, 1, f1);
+        mfmas(f0);
+        mfmas(f1);
+      }
+      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
+      __builtin_amdgcn_s_barrier();
+    }
   } else {
     GE_SET_RS(kt * BKE, kt * BKE);
     issue_a(kt * BKE, aslot(S0{}));

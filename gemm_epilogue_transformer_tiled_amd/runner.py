@@ -54,13 +54,14 @@ class DeviceProblem:
     def col_sum_host(self):
         return None if self.col_sum is None else self.col_sum.cpu().numpy().astype(np.float64)
 
-    def with_tile(self, tile: int) -> "DeviceProblem":
-        """The same problem (same device tensors and outputs) planned on kernel instance `tile`."""
+    def with_tile(self, tile: int, library=None) -> "DeviceProblem":
+        """The same problem (same device tensors and outputs) planned on kernel instance `tile`
+        (of `library`, a library loaded by the binding; default: the fused path's)."""
         desc = ge_desc_t.from_buffer_copy(self.plan.desc)
         desc.tile = tile + 1
         args = ge_args_t.from_buffer_copy(self.args)
         args.workspace, args.workspace_bytes = None, 0        # the new plan brings its own
-        return dataclasses.replace(self, plan=Plan(desc), args=args)
+        return dataclasses.replace(self, plan=Plan(desc, library=library), args=args)
 
 
 def descriptor(w) -> ge_desc_t:

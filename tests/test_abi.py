@@ -31,6 +31,24 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(ge.EXPORTED)
 
 
+def test_reference_build_exports_the_same_symbols_and_has_no_two_wave_instances():
+    """The reference build (serial mainloop) loads beside the fused library, exports the same
+    entry points, and refuses the two-wave instances it leaves out."""
+    names = _declared_symbols()
+    ser = ge.load_serial_library()
+    assert ser is not ge.lib
+    for n in names:
+        assert hasattr(ser, n), n
+    for tile in (ge.GE_TILE_256x256_2W, ge.GE_TILE_256x128_PAIR_2W):
+        pair = tile == ge.GE_TILE_256x128_PAIR_2W
+        ops = ge.make_ops([("pairwise", "silu")] if pair else [("scale",), ("amax",)])
+        d = ge.make_desc(1, 512, 512, 256, ops, tile=tile)
+        assert ge.lib.gemm_epilogue_validate(ctypes.byref(d)) == ge.GE_OK
+        assert ser.gemm_epilogue_validate(ctypes.byref(d)) == ge.GE_ERR_UNSUPPORTED
+        d.tile = (ge.GE_TILE_256x128_PAIR if pair else ge.GE_TILE_256x256) + 1
+        assert ser.gemm_epilogue_validate(ctypes.byref(d)) == ge.GE_OK
+
+
 def test_baselines_library_exports_every_declared_symbol():
     from gemm_epilogue_transformer_tiled_amd import baselines
     names = _declared_symbols(r"ge_(?:unfused|probe)_\w+")
