@@ -63,9 +63,9 @@ ABNORMAL_RC = {-6, -9, -11, -15, 124, 134, 137, 139}
 # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE (x2.0) + WRITE_SIZE (x1.0) of the fused
 # kernel at each workload; the factors scale the counters to the bytes of a plain 1 GiB device
 # copy.  Valid only for the kernel source they were taken on (sha256 prefix below).
-MEASURED_TRAFFIC_SOURCE = "dbbf931ca9a0118c"
-MEASURED_TRAFFIC = {"c1": 1066179, "c2": 101017364, "c3": 2406204692, "c4": 537326455, "c5": 1684376578,
-                    "f1": 2390112536, "f2": 1767723826, "f3": 877332093}
+MEASURED_TRAFFIC_SOURCE = "80a746a6253ab499"
+MEASURED_TRAFFIC = {"c1": 1066178, "c2": 101018177, "c3": 2406240255, "c4": 537323117, "c5": 1684367392,
+                    "f1": 2390128484, "f2": 1775190192, "f3": 877296419}
 
 
 def kernel_source_hash():
