@@ -62,21 +62,33 @@ ABNORMAL_RC = {-6, -9, -11, -15, 124, 134, 137, 139}
 
 # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE (x2.0) + WRITE_SIZE (x1.0) of the fused
 # kernel at each workload; the factors scale the counters to the bytes of a plain 1 GiB device
-# copy.  Valid only for the kernel source they were taken on (sha256 prefix below).
-MEASURED_TRAFFIC_SOURCE = "80a746a6253ab499"
+# copy.  Valid only for the device code they were taken on (sha256 prefix of the library's
+# .hip_fatbin section, below): any change to any kernel instance changes it.
+MEASURED_TRAFFIC_CODE = "b0a9ba93d8169d70"
 MEASURED_TRAFFIC = {"c1": 1066178, "c2": 101018177, "c3": 2406240255, "c4": 537323117, "c5": 1684367392,
                     "f1": 2390128484, "f2": 1775190192, "f3": 877296419}
 
 
-def kernel_source_hash():
-    """sha256 prefix over the fused kernel's sources (csrc/ge_*, in name order)."""
-    csrc = os.path.join(ROOT, "gemm_epilogue_transformer_tiled_amd", "csrc")
-    h = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
-        if name.startswith("ge_"):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
-    return h.hexdigest()[:16]
+def kernel_code_hash(lib_path=None):
+    """sha256 prefix of the device code in libgemm_epilogue.so (its .hip_fatbin ELF section)."""
+    import struct
+    path = lib_path or os.path.join(ROOT, "gemm_epilogue_transformer_tiled_amd", "libgemm_epilogue.so")
+    with open(path, "rb") as f:
+        data = f.read()
+    if data[:4] != b"\x7fELF" or data[4] != 2:
+        raise ValueError(f"{path}: not a 64-bit ELF file")
+    e_shoff, = struct.unpack_from("<Q", data, 0x28)
+    e_shentsize, e_shnum, e_shstrndx = struct.unpack_from("<HHH", data, 0x3A)
+    def section(i):
+        name, _type, _flags, _addr, off, size = struct.unpack_from("<IIQQQQ", data, e_shoff + i * e_shentsize)
+        return name, off, size
+    _, str_off, _ = section(e_shstrndx)
+    for i in range(e_shnum):
+        name, off, size = section(i)
+        end = data.index(b"\0", str_off + name)
+        if data[str_off + name:end] == b".hip_fatbin":
+            return hashlib.sha256(data[off:off + size]).hexdigest()[:16]
+    raise ValueError(f"{path}: no .hip_fatbin section")
 
 
 def parse():
@@ -422,7 +434,7 @@ def run_one(args):
             "frac_mfma": round(achieved / peak, 4),
             "ideal_us_at_mfma_peak": round(t_mfma_us, 3),
             "ideal_us_at_hbm_peak": round(t_hbm_us, 3),
-            "traffic": MEASURED_TRAFFIC.get(w.name) if kernel_source_hash() == MEASURED_TRAFFIC_SOURCE else None,
+            "traffic": MEASURED_TRAFFIC.get(w.name) if kernel_code_hash() == MEASURED_TRAFFIC_CODE else None,
             "kernel": "fused_gemm_epilogue",
             "launch_ms_mean": round(launch_ms, 6),
             "algorithmic_flops_per_launch": flops,

@@ -335,8 +335,9 @@ void fused_gemm_epilogue(Params p) {
   // every slice from every tile that uses it cost 1.5-6 %; one prefetcher per slice gains up
   // to 8 %: the operand lines otherwise reach L2 only when the real loads ask for them, a
   // fabric round trip of 1.5-2.5 us under load against two steps of prefetch.)
-  // Only the bf16 [N][K] instances prefetch (measured: it pays there, a loss elsewhere).
-  constexpr bool L2PF = BNK && !F8IN;
+  // Only the one-wave bf16 [N][K] instances prefetch (measured: it pays there, a loss
+  // elsewhere; the two-wave loop hides the loads' latency itself, and a prefetch cost it 6-7 %).
+  constexpr bool L2PF = BNK && !F8IN && !PP;
   constexpr int PF = L2PF ? 2 : 0;                     // prefetch loads per wave per even step
   const uint32_t pf_a_off = ((tn & 3) == 0 && tid < T::BM) ? (uint32_t)tid * lda2 : kOOB;
   constexpr int PF_T = T::NT / T::NB;                  // threads per operand

@@ -49,6 +49,28 @@ def test_reference_build_exports_the_same_symbols_and_has_no_two_wave_instances(
         assert ser.gemm_epilogue_validate(ctypes.byref(d)) == ge.GE_OK
 
 
+def test_device_code_hash_reads_the_fatbin_section():
+    """bench.py keys its measured-traffic table on the device code: the hash covers the
+    library's .hip_fatbin section, which the reference build (other kernels) does not share."""
+    import hashlib
+    import importlib.util
+    import shutil
+    import subprocess
+    spec = importlib.util.spec_from_file_location("bench_for_test", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    h = bench.kernel_code_hash()
+    assert re.fullmatch(r"[0-9a-f]{16}", h)
+    assert bench.kernel_code_hash(ge.SERIAL_LIB_PATH) != h
+    if shutil.which("objcopy"):
+        out = os.path.join(ROOT, "gemm_epilogue_transformer_tiled_amd", "_build", "fatbin_for_test.bin")
+        subprocess.run(["objcopy", "-O", "binary", "--only-section=.hip_fatbin", ge.LIB_PATH, out], check=True)
+        try:
+            assert hashlib.sha256(open(out, "rb").read()).hexdigest()[:16] == h
+        finally:
+            os.remove(out)
+
+
 def test_baselines_library_exports_every_declared_symbol():
     from gemm_epilogue_transformer_tiled_amd import baselines
     names = _declared_symbols(r"ge_(?:unfused|probe)_\w+")
