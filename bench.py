@@ -481,11 +481,15 @@ def run_one(args):
     if not args.no_probes:
         from gemm_epilogue_transformer_tiled_amd import baselines
         mf = baselines.probe_mfma()
+        mf16 = baselines.probe_mfma(form="bf16_16x16x32")
+        mf8 = baselines.probe_mfma(form="fp8_32x32x64")
         cp = baselines.probe_copy()
         result["measured_peaks"] = {"mfma_bf16_tflops": mf["tflops"], "mfma_implied_clock_ghz": mf["implied_clock_ghz"],
+                                    "mfma_bf16_16x16x32_tflops": mf16["tflops"],
+                                    "mfma_fp8_tflops": mf8["tflops"], "mfma_fp8_implied_clock_ghz": mf8["implied_clock_ghz"],
                                     "copy_gbs": cp["gbs"]}
-        if not fp8_in:      # the probe runs the bf16 instruction
-            result["roofline"]["frac_of_measured_mfma_peak"] = round(achieved / mf["tflops"], 4)
+        # against the probe of the instruction the mainloop runs
+        result["roofline"]["frac_of_measured_mfma_peak"] = round(achieved / (mf8 if fp8_in else mf)["tflops"], 4)
         result["roofline"]["frac_of_measured_copy_gbs"] = round(gbs / cp["gbs"], 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_seconds)

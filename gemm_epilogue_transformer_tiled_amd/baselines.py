@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libge_baselines.so")
 EXPORTED = ("ge_unfused_scale", "ge_unfused_bias_col", "ge_unfused_act", "ge_unfused_act_mul",
             "ge_unfused_row_rms", "ge_unfused_row_scale", "ge_unfused_add", "ge_unfused_amax",
             "ge_unfused_quant_fp8", "ge_unfused_act_grad", "ge_unfused_col_sum", "ge_probe_mfma",
-            "ge_probe_mfma_f8", "ge_probe_copy")
+            "ge_probe_mfma_variant", "ge_probe_mfma_f8", "ge_probe_copy")
 ACTS = {"none": 0, "relu": 1, "gelu_tanh": 2, "silu": 3}
 
 _p, _i64, _i, _f = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
@@ -41,6 +41,7 @@ _SIGS = {
     "ge_unfused_act_grad": [_p, _p, _p, _i64, _i, _p],
     "ge_unfused_col_sum": [_p, _p, _i64, _i64, _p],
     "ge_probe_mfma": [_p, _i, _i, _p],
+    "ge_probe_mfma_variant": [_p, _i, _i, _i, _p],
     "ge_probe_mfma_f8": [_p, _p, _p, _p, _i, _p],
     "ge_probe_copy": [_p, _p, _i64, _p],
 }
@@ -203,24 +204,32 @@ class Unfused:
         return y.view(torch.int16).numpy().view(np.uint16)
 
 
-def probe_mfma(workgroups: int = 1024, iters: int = 4096) -> Dict:
-    """Sustained matrix-core TFLOP/s (v_mfma_f32_32x32x16_bf16 on random register operands that
-    change from one instruction to the next)."""
+# matrix-core probe forms: variant -> (chains per wave, flop per instruction)
+PROBE_FORMS = {"bf16_32x32x16": (0, 16, 32768.0), "bf16_16x16x32": (1, 16, 16384.0), "fp8_32x32x64": (2, 8, 131072.0)}
+
+
+def probe_mfma(workgroups: int = 1024, iters: int = 4096, form: str = "bf16_32x32x16") -> Dict:
+    """Sustained matrix-core TFLOP/s of one instruction form (``PROBE_FORMS``; default
+    v_mfma_f32_32x32x16_bf16) on random register operands that change from one instruction to
+    the next."""
+    variant, chains, per_inst = PROBE_FORMS[form]
     sink = torch.empty(workgroups * 256, dtype=torch.float32, device="cuda")
-    call("ge_probe_mfma", sink.data_ptr(), workgroups, 16, _stream())     # warm
+    call("ge_probe_mfma_variant", sink.data_ptr(), workgroups, 16, variant, _stream())     # warm
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     best = None
     for _ in range(3):
         e0.record()
-        call("ge_probe_mfma", sink.data_ptr(), workgroups, iters, _stream())
+        call("ge_probe_mfma_variant", sink.data_ptr(), workgroups, iters, variant, _stream())
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
         best = ms if best is None else min(best, ms)
-    flops = workgroups * 4 * 16 * iters * 32768.0
-    return {"tflops": round(flops / best / 1e9, 1), "ms": round(best, 4),
-            "implied_clock_ghz": round(flops / (best * 1e-3) / (256 * 4096) / 1e9, 3)}
+    flops = workgroups * 4 * chains * iters * per_inst
+    # implied clock: a CU's matrix cores do 4096 bf16 (8192 fp8) flop per cycle, 256 CUs
+    per_cu_cycle = 8192 if form.startswith("fp8") else 4096
+    return {"form": form, "tflops": round(flops / best / 1e9, 1), "ms": round(best, 4),
+            "implied_clock_ghz": round(flops / (best * 1e-3) / (256 * per_cu_cycle) / 1e9, 3)}
 
 
 def mfma_f8(src0: np.ndarray, src1: np.ndarray, c: np.ndarray) -> np.ndarray:

@@ -23,8 +23,10 @@ COMMON = ["ge_kernels.hip", "noalloc.hip", "tiles.cpp", "api.cpp"]
 TARGETS = {
     os.path.join(HERE, "libgemm_epilogue.so"): (ONE_WAVE + TWO_WAVE + COMMON, ()),
     os.path.join(HERE, "libgemm_epilogue_serial.so"): (ONE_WAVE + COMMON, ("-DGE_SERIAL_PIPELINE=1",)),
-    os.path.join(HERE, "libge_baselines.so"): (["baselines.hip"], ()),
+    os.path.join(HERE, "libge_baselines.so"): (["baselines.hip", "probe_mfma16.hip"], ()),
 }
+# per-source compiler flags (the 16x16x32 probe keeps its accumulators in VGPRs: see its header)
+SOURCE_FLAGS = {"probe_mfma16.hip": ("-mllvm", "-amdgpu-mfma-vgpr-form")}
 LIB = os.path.join(HERE, "libgemm_epilogue.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -40,7 +42,7 @@ def _compile(job) -> str:
     src, extra = job
     out_dir = os.path.join(BUILD_DIR, "serial") if extra else BUILD_DIR
     obj = os.path.join(out_dir, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, ()), *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src} {' '.join(extra)}:\n{r.stderr[-6000:]}")

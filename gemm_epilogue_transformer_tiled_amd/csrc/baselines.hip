@@ -279,12 +279,47 @@ __global__ __launch_bounds__(256) void mfma_probe(float* sink, int iters) {
   sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// The fp8 form of the same probe: v_mfma_f32_32x32x64_f8f6f4, the instruction of the
+// fp8-operand mainloop, on random e4m3 codes (no NaN code; four 32-byte sets per source, 8
+// chains: each instruction is 64 cycles, so 8 keep the matrix core fed; operand sets
+// (i % 4, (i / 2) % 4), so consecutive instructions differ in at least one source).  The
+// 16x16x32 bf16 form lives in probe_mfma16.hip, which needs its own compiler flags.
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+__global__ __launch_bounds__(256) void mfma_probe_f8(float* sink, int iters) {
+  const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+  i32x8_t a[4], b[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t wa = probe_hash(t * 64 + k * 8 + i), wb = probe_hash(t * 64 + 32 + k * 8 + i);
+      // e4m3 NaN is S.1111.111: clear the lowest bit of any byte that would be one
+      wa &= ~((((wa & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u) >> 7);
+      wb &= ~((((wb & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u) >> 7);
+      a[k][i] = (int)wa;
+      b[k][i] = (int)wb;
+    }
+  f32x16_t acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = f32x16_t{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i % 4], b[(i / 2) % 4], acc[i], 0, 0, 0, 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += acc[i][j];
+  sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 // One fp8 matrix-core instruction per wave on caller-given register contents: lane l of wave w
 // takes 32 bytes of e4m3 codes from src0 and from src1 at byte (64 w + l) * 32 and 16 fp32
 // accumulator values from c at float (64 w + l) * 16, runs v_mfma_f32_32x32x64_f8f6f4 (e4m3 for
 // both sources, no block scales) and writes the 16 result values to d at the same place.  This
 // shows how the instruction sums its 64 products into the accumulator.
-typedef int i32x8_t __attribute__((ext_vector_type(8)));
 __global__ __launch_bounds__(64) void mfma_f8_probe(const i32x8_t* __restrict__ s0, const i32x8_t* __restrict__ s1,
                                                     const f32x16_t* __restrict__ c, f32x16_t* __restrict__ d) {
   const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
@@ -304,6 +339,9 @@ int launch(K kernel, int64_t blocks, hipStream_t s, Args... args) {
 }
 
 }  // namespace
+
+// probe_mfma16.hip: launches the 16x16x32 bf16 form of the matrix-core probe.
+void ge_launch_probe_mfma16(float* sink, int workgroups, int iters, hipStream_t stream);
 
 extern "C" {
 
@@ -386,6 +424,20 @@ int ge_unfused_quant_fp8(const uint16_t* x, uint8_t* y, int64_t n, float scale, 
 int ge_probe_mfma(float* sink, int workgroups, int iters, void* stream) {
   if (!sink || workgroups <= 0 || iters < 0) return 1;
   hipLaunchKernelGGL(mfma_probe, dim3((unsigned)workgroups), dim3(256), 0, (hipStream_t)stream, sink, iters);
+  return launched();
+}
+
+int ge_probe_mfma_variant(float* sink, int workgroups, int iters, int variant, void* stream) {
+  if (!sink || workgroups <= 0 || iters < 0) return 1;
+  if (variant == 0) {
+    hipLaunchKernelGGL(mfma_probe, dim3((unsigned)workgroups), dim3(256), 0, (hipStream_t)stream, sink, iters);
+  } else if (variant == 1) {
+    ge_launch_probe_mfma16(sink, workgroups, iters, (hipStream_t)stream);
+  } else if (variant == 2) {
+    hipLaunchKernelGGL(mfma_probe_f8, dim3((unsigned)workgroups), dim3(256), 0, (hipStream_t)stream, sink, iters);
+  } else {
+    return 1;
+  }
   return launched();
 }
 

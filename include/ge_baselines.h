@@ -80,6 +80,14 @@ int ge_unfused_quant_fp8(const uint16_t* x, uint8_t* y, int64_t n, float scale, 
  * workgroups * 4 * 16 * iters * 32768. */
 int ge_probe_mfma(float* sink, int workgroups, int iters, void* stream);
 
+/* The same probe on the other matrix-core forms: variant 0 is ge_probe_mfma; variant 1 runs 16
+ * chains of v_mfma_f32_16x16x32_bf16 on the same random bf16 operand sets (work per launch:
+ * workgroups * 4 * 16 * iters * 16384); variant 2 runs 8 chains of v_mfma_f32_32x32x64_f8f6f4
+ * on random e4m3 codes without NaN codes, the fp8-operand mainloop's instruction (work per
+ * launch: workgroups * 4 * 8 * iters * 131072).  Returns 1 for an unknown variant or invalid
+ * arguments. */
+int ge_probe_mfma_variant(float* sink, int workgroups, int iters, int variant, void* stream);
+
 /* fp8 matrix-core probe: `waves` single-wave workgroups, each running ONE
  * v_mfma_f32_32x32x64_f8f6f4 with e4m3 codes in both sources and no block scales on its own
  * register contents.  Lane l of wave w reads 32 bytes of src0 and of src1 at byte offset

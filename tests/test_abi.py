@@ -74,7 +74,7 @@ def test_device_code_hash_reads_the_fatbin_section():
 def test_baselines_library_exports_every_declared_symbol():
     from gemm_epilogue_transformer_tiled_amd import baselines
     names = _declared_symbols(r"ge_(?:unfused|probe)_\w+")
-    assert len(names) == 14
+    assert len(names) == 15
     lib = ctypes.CDLL(baselines.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -91,6 +91,9 @@ def test_baselines_reject_invalid_arguments_without_launching():
     assert lib.ge_unfused_amax(None, 0, None, None) == 1
     assert lib.ge_probe_copy(None, None, 24, None) == 1             # not a multiple of 16
     assert lib.ge_probe_mfma(None, 1, 1, None) == 1
+    assert lib.ge_probe_mfma_variant(None, 1, 1, 0, None) == 1
+    sink = ctypes.c_float()
+    assert lib.ge_probe_mfma_variant(ctypes.byref(sink), 1, 1, 3, None) == 1   # unknown form
     assert lib.ge_unfused_scale(None, None, 0, 1.0, None) == 0      # empty: nothing to do
 
 

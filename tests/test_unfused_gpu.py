@@ -114,5 +114,9 @@ def test_unfused_ops_on_ragged_sizes():
 def test_probes_report_plausible_peaks():
     m = bl.probe_mfma(workgroups=256, iters=256)
     assert 100.0 < m["tflops"] < 2600.0, m
+    m16 = bl.probe_mfma(workgroups=256, iters=256, form="bf16_16x16x32")
+    assert 100.0 < m16["tflops"] < 2600.0, m16
+    m8 = bl.probe_mfma(workgroups=256, iters=256, form="fp8_32x32x64")
+    assert 200.0 < m8["tflops"] < 5200.0, m8
     c = bl.probe_copy(mib=64)
     assert 100.0 < c["gbs"] < 9000.0, c
