@@ -1,5 +1,5 @@
 """Builds libgemm_epilogue.so (the fused path), libgemm_epilogue_serial.so (its reference build:
-the one-wave instances with a mainloop that overlaps nothing, for bit-for-bit race tests) and
+every instance with a mainloop that overlaps nothing, for bit-for-bit race tests) and
 libge_baselines.so (unfused comparators and calibration probes) in-tree with hipcc for gfx950.
 
 Usage: python gemm_epilogue_transformer_tiled_amd/build.py  (runs by path: importing the
@@ -22,7 +22,7 @@ COMMON = ["ge_kernels.hip", "noalloc.hip", "tiles.cpp", "api.cpp"]
 # library -> (its sources, extra compiler flags)
 TARGETS = {
     os.path.join(HERE, "libgemm_epilogue.so"): (ONE_WAVE + TWO_WAVE + COMMON, ()),
-    os.path.join(HERE, "libgemm_epilogue_serial.so"): (ONE_WAVE + COMMON, ("-DGE_SERIAL_PIPELINE=1",)),
+    os.path.join(HERE, "libgemm_epilogue_serial.so"): (ONE_WAVE + TWO_WAVE + COMMON, ("-DGE_SERIAL_PIPELINE=1",)),
     os.path.join(HERE, "libge_baselines.so"): (["baselines.hip", "probe_mfma16.hip"], ()),
 }
 # per-source compiler flags (the 16x16x32 probe keeps its accumulators in VGPRs: see its header)

@@ -109,7 +109,6 @@ ge::TileKind pick_tile(const ge_desc_t* d, bool pair) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 bool two_wave_ok(const ge_desc_t* d) {
-  if (GE_SERIAL_PIPELINE) return false;                     // the reference build has none
   return d->K % (d->a_type == GE_DT_FP8_E4M3 ? 128 : 64) == 0;
 }
 

@@ -4,11 +4,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-// Reference build: GE_SERIAL_PIPELINE=1 compiles the one-wave instances with a mainloop that
-// overlaps nothing (each two-step slot is loaded, waited for and read between two full
-// barriers) and leaves the two-wave instances out.  The MFMAs, their operands and their order
-// are those of the pipelined build, so its results are bit-identical to it; a difference
-// means a synchronisation mistake in the pipelined mainloop.
+// Reference build: GE_SERIAL_PIPELINE=1 compiles every instance with a mainloop that overlaps
+// nothing (each two-step slot is loaded, waited for and read between two full barriers).  The
+// tiles, waves, MFMAs, their operands and their order are those of the pipelined build, so
+// its results are bit-identical to it; a difference means a synchronisation mistake in the
+// pipelined mainloop.
 #ifndef GE_SERIAL_PIPELINE
 #define GE_SERIAL_PIPELINE 0
 #endif

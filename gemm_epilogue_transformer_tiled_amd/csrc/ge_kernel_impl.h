@@ -41,6 +41,8 @@
 //     (this step's fragment reads, later steps' loads, waits) and a matrix phase (MFMAs only,
 //     at raised priority), one phase apart, so one wave per SIMD keeps the matrix core busy
 //     while the other waits on memory; the row statistic comes from the staged A slots.
+//     With bf16 operands they multiply with v_mfma_f32_16x16x32_bf16 (one instruction per
+//     16x16 block and 32-deep step: half the accumulator traffic per flop of 32x32x16).
 #include <type_traits>
 #include <utility>
 
@@ -97,6 +99,14 @@ template <int CHUNKS>
 __device__ __forceinline__ uint32_t swz_b(uint32_t k) {
   const uint32_t q = k & 3u;
   return ((q << 2) | ((q >> 1) << 1)) & (uint32_t)(CHUNKS - 1);
+}
+// The same for the 16x16x32 fragments, whose two 16-lane groups of a half-wave read rows
+// k..k+3 and k+8..k+11 of the same columns: rows with bit 3 set also flip chunk bit 3, which
+// sends the second group's four chunk pairs to the complement of the first group's in every
+// aligned group of sixteen chunks (256 bytes).
+template <int CHUNKS>
+__device__ __forceinline__ uint32_t swz_b16(uint32_t k) {
+  return swz_b<CHUNKS>(k) ^ (k & 8u);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -212,6 +222,10 @@ template <class T, int ACT, bool GRAD, bool FP8, bool ROWSTAT, bool KMASK, bool 
 __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(T::WPE, T::WPE)))
 void fused_gemm_epilogue(Params p) {
   constexpr bool PP = T::WAVES == 8;              // two waves per SIMD, alternating phases
+  // Two-wave bf16 instances multiply with v_mfma_f32_16x16x32_bf16: half the accumulator bytes
+  // per flop of the 32x32x16 form, which under the power limit runs the matrix cores faster
+  // (measured +2.5 to +3.7 % on every bf16 workload against the same loop on 32x32x16).
+  constexpr bool MF16 = PP && !F8IN;
   static_assert(!PP || !KMASK, "the two-wave instances: K a multiple of two steps");
   constexpr int ES = F8IN ? 1 : 2;                // bytes per operand element
   constexpr int BKE = F8IN ? 64 : T::BK;          // K values per step (64 bytes of a row)
@@ -319,7 +333,7 @@ void fused_gemm_epilogue(Params p) {
     } else {
       const int blk = (wave * T::B_LOADS + t) % T::B_LOADS_PER_OP;
       const uint32_t row = (uint32_t)blk * T::B_ROWS_PER_LOAD + (uint32_t)(lane / T::B_CHUNKS);
-      const uint32_t lchunk = (uint32_t)(lane % T::B_CHUNKS) ^ swz_b<T::B_CHUNKS>(row);
+      const uint32_t lchunk = (uint32_t)(lane % T::B_CHUNKS) ^ (MF16 ? swz_b16<T::B_CHUNKS>(row) : swz_b<T::B_CHUNKS>(row));
       b_voff[t] = (n0 + (int)lchunk * 8 < N) ? row * ldb2 + lchunk * 16u : kOOB;
     }
   }
@@ -462,14 +476,54 @@ void fused_gemm_epilogue(Params p) {
   for (int hg = 0; hg < 2 * T::GROUPS; ++hg)
     bnk_frag[hg] = (uint32_t)(wn0 + lrow) * T::A_ROWB + (((uint32_t)(2 * hg + lhalf) ^ swz_a(lrow)) << 4);
 
-  f32x16_t acc[T::FN][T::FM];
-  f32x16_t acc2[T::PAIR ? T::FN : 1][T::PAIR ? T::FM : 1];
+  // 16x16x32 fragments: a lane holds eight consecutive K of one row (A, [N][K] B) or column
+  // ([K][N] B): row/column lane % 16 of the block, K 8 * (lane / 16) .. +7 of the step, i.e.
+  // logical chunk 4h + lane / 16 of a slot row.  swz_a depends on the row mod 32, so 16-row
+  // blocks of even and odd index have a base address each; further 32 rows are immediate
+  // offsets.  [K][N] B: in each 16-lane group q, lane s points at rows 8q + s/4 (and + 4) and
+  // columns nb + 4(s%4) .. +3, and receives column nb + s.
+  constexpr int FN16 = MF16 ? T::WN / 16 : 1, FM16 = MF16 ? T::WM / 16 : 1;
+  const uint32_t l16 = (uint32_t)(lane & 15), q16 = (uint32_t)(lane >> 4);
+  uint32_t a16[2][2], bnk16[2][2];          // [slot half][16-row block parity]
 #pragma unroll
-  for (int i = 0; i < T::FN; ++i)
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int j = 0; j < T::FM; ++j) {
+    for (int par = 0; par < 2; ++par) {
+      const uint32_t r = 16u * (uint32_t)par + l16, c = ((4u * (uint32_t)h + q16) ^ swz_a(r)) << 4;
+      a16[h][par] = ((uint32_t)wm0 + r) * T::A_ROWB + c;
+      bnk16[h][par] = ((uint32_t)wn0 + r) * T::A_ROWB + c;
+    }
+  uint32_t b16[T::NB][FN16];
+#pragma unroll
+  for (int op = 0; op < T::NB; ++op)
+#pragma unroll
+    for (int i = 0; i < FN16; ++i) {
+      const uint32_t k16 = 8u * q16 + (l16 >> 2);
+      const uint32_t ncol = (uint32_t)(wn0 + 16 * i) + 4u * (l16 & 3u);
+      b16[op][i] = (uint32_t)(op * T::B_BYTES) + k16 * T::B_ROWB +
+                   (((ncol >> 3) ^ swz_b16<T::B_CHUNKS>(k16)) << 4) + (ncol & 7u) * 2u;
+    }
+
+  constexpr int AFN = MF16 ? 1 : T::FN, AFM = MF16 ? 1 : T::FM;
+  f32x16_t acc[AFN][AFM];
+  f32x16_t acc2[T::PAIR ? AFN : 1][T::PAIR ? AFM : 1];
+#pragma unroll
+  for (int i = 0; i < AFN; ++i)
+#pragma unroll
+    for (int j = 0; j < AFM; ++j) {
       acc[i][j] = f32x16_t{};
       if constexpr (T::PAIR) acc2[i][j] = f32x16_t{};
+    }
+  // 16x16x32 accumulators: block (i, j) of the wave's tile, lane holds row 16j + lane % 16,
+  // columns 16i + 4 (lane / 16) .. +3
+  f32x4_t c16[FN16][FM16];
+  f32x4_t c16b[T::PAIR ? FN16 : 1][T::PAIR ? FM16 : 1];
+#pragma unroll
+  for (int i = 0; i < FN16; ++i)
+#pragma unroll
+    for (int j = 0; j < FM16; ++j) {
+      c16[i][j] = f32x4_t{};
+      if constexpr (T::PAIR) c16b[i][j] = f32x4_t{};
     }
   // RMS statistic from the A fragments (one-wave instances): waves with wave_n == 0 own the
   // first half of the wave's 32-row blocks, wave_n == 1 the second half (all of them when
@@ -509,7 +563,7 @@ void fused_gemm_epilogue(Params p) {
         f.b[op][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
   };
-  auto mfmas = [&](const Frags& f) {
+  auto mfmas = [&](const auto& f) {
 #pragma unroll
     for (int i = 0; i < T::FN; ++i)
 #pragma unroll
@@ -532,6 +586,43 @@ void fused_gemm_epilogue(Params p) {
         }
       }
     }
+  };
+  struct Frags16 {
+    bf16x8_t a[FM16];
+    bf16x8_t b[T::NB][FN16];
+  };
+  // one 32-deep step (slot half h) of 16x16x32 fragments
+  auto read_frags16 = [&](const unsigned char* as, const unsigned char* bs, int h, Frags16& f) {
+#pragma unroll
+    for (int j = 0; j < FM16; ++j)
+      f.a[j] = *(const bf16x8_t*)(as + a16[h][j & 1] + (j >> 1) * 32 * T::A_ROWB);
+    if constexpr (BNK) {
+#pragma unroll
+      for (int op = 0; op < T::NB; ++op)
+#pragma unroll
+        for (int i = 0; i < FN16; ++i)
+          f.b[op][i] = *(const bf16x8_t*)(bs + bnk16[h][i & 1] + (i >> 1) * 32 * T::A_ROWB + op * T::BN * T::A_ROWB);
+      return;
+    }
+#pragma unroll
+    for (int op = 0; op < T::NB; ++op)
+#pragma unroll
+      for (int i = 0; i < FN16; ++i) {
+        const unsigned char* q = bs + b16[op][i];
+        const v4bf16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf16*)(q));
+        const v4bf16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf16*)(q + 4 * T::B_ROWB));
+        f.b[op][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+  };
+  auto mfmas16 = [&](const auto& f) {
+#pragma unroll
+    for (int i = 0; i < FN16; ++i)
+#pragma unroll
+      for (int j = 0; j < FM16; ++j) {
+        c16[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[0][i], f.a[j], c16[i][j], 0, 0, 0);
+        if constexpr (T::PAIR)
+          c16b[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[T::NB - 1][i], f.a[j], c16b[i][j], 0, 0, 0);
+      }
   };
   constexpr int READS_PER_GROUP = T::FM + 2 * T::NB * T::FN;
   constexpr int MFMAS_PER_GROUP = T::FM * T::FN * T::NB;
@@ -680,7 +771,66 @@ void fused_gemm_epilogue(Params p) {
       if constexpr (T::PAIR) b2rs = GE_B_RS(b2_base, BNK ? (ka) : (kb));       \
     }                                                                          \
   } while (0)
-  if constexpr (PP) {
+  if constexpr (GE_SERIAL_PIPELINE) {
+    // ---- reference build: one two-step slot at a time, nothing overlapped ----
+    // Load the slot's A and B (B [K][N]: both steps' stages), wait for every load, barrier;
+    // read and multiply steps k and k+1 with the pipelined build's fragments, MFMAs and order
+    // (and, on the two-wave tiles, square the slot's rows for the row statistic as their odd
+    // steps do); wait for the reads, barrier, so no stage is refilled while a wave still reads it.
+    [[maybe_unused]] const int grp = wave >> 2;
+    [[maybe_unused]] float ss1 = 0.0f;
+    [[maybe_unused]] const uint32_t sq_row = (uint32_t)((wave & 3) * 64 + lane) * T::A_ROWB;
+    [[maybe_unused]] const uint32_t sq_c = ((uint32_t)((lane & 15) + ((lane & 15) >> 3)) & 7u) ^ (uint32_t)(4 * grp);
+    [[maybe_unused]] Frags16 f16;
+    for (int k = kt; k < nk; k += 2) {
+      GE_SET_RS(k * BKE, k * BKE);
+      issue_a(k * BKE, aslot(S0{}));
+      issue_b(bstage(S0{}), k * BKE);
+      if constexpr (!BNK) {
+        GE_SET_RS(k * BKE, (k + 1) * BKE);
+        issue_b(bstage(S1{}), (k + 1) * BKE);
+      }
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      __builtin_amdgcn_s_barrier();
+      if constexpr (PP && ROWSTAT) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x8_t v = *(const bf16x8_t*)(aslot(S0{}) + sq_row + ((sq_c ^ (uint32_t)i) << 4));
+          const bf16x2_t p0 = __builtin_shufflevector(v, v, 0, 1), p1 = __builtin_shufflevector(v, v, 2, 3);
+          const bf16x2_t p2 = __builtin_shufflevector(v, v, 4, 5), p3 = __builtin_shufflevector(v, v, 6, 7);
+          ss1 = __builtin_amdgcn_fdot2_f32_bf16(p0, p0, ss1, false);
+          ss1 = __builtin_amdgcn_fdot2_f32_bf16(p1, p1, ss1, false);
+          ss1 = __builtin_amdgcn_fdot2_f32_bf16(p2, p2, ss1, false);
+          ss1 = __builtin_amdgcn_fdot2_f32_bf16(p3, p3, ss1, false);
+        }
+      }
+      if constexpr (F8IN) {
+        read_a8(aslot(S0{}), 0, fa8[0]);
+        read_b8(bstage(S0{}), 0, Q0c{}, QNc{});
+        mfma8(fa8[0], Q0c{}, QNc{});
+        read_a8(aslot(S0{}), 1, fa8[0]);
+        read_b8(bstage(S0{}), 1, Q0c{}, QNc{});
+        mfma8(fa8[0], Q0c{}, QNc{});
+      } else if constexpr (MF16) {
+        read_frags16(aslot(S0{}), bstage(S0{}), 0, f16);
+        mfmas16(f16);
+        read_frags16(aslot(S1{}), bstage(S1{}), 1, f16);
+        mfmas16(f16);
+      } else {
+        read_frags(aslot(S0{}), bstage(S0{}), 0, 0, f0);
+        read_frags(aslot(S0{}), bstage(S0{}), 0, 1, f1);
+        mfmas(f0);
+        mfmas(f1);
+        read_frags(aslot(S1{}), bstage(S1{}), 1, 0, f0);
+        read_frags(aslot(S1{}), bstage(S1{}), 1, 1, f1);
+        mfmas(f0);
+        mfmas(f1);
+      }
+      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
+      __builtin_amdgcn_s_barrier();
+    }
+    if constexpr (PP && ROWSTAT) row_ss[grp * T::BM + (wave & 3) * 64 + lane] = ss1;
+  } else if constexpr (PP) {
     // ---- two waves per SIMD: a memory phase and a matrix phase per step ----
     // Both groups run this sequence with one barrier between phases; group 1 starts one phase
     // behind group 0, so in every phase one wave of each SIMD issues MFMAs while the other
@@ -695,6 +845,7 @@ void fused_gemm_epilogue(Params p) {
     //     partner wave's memory work fills the issue slots the MFMAs leave.
     const int grp = wave >> 2;
     Frags fr0, fr1;
+    Frags16 f16;
     // Step resources: K is a multiple of two steps here, so a step is wholly inside or outside
     // [0, K), and an outside step needs only an empty extent (its base is never used): one
     // unsigned compare instead of the clamps of the general case.
@@ -762,6 +913,8 @@ void fused_gemm_epilogue(Params p) {
         // fp8 operands: one 64-deep step, one register set (the matrix phase uses it whole)
         read_a8(aslot(Cur{}), S % 2, fa8[0]);
         read_b8(bstage(Cur{}), S % 2, Q0c{}, QNc{});
+      } else if constexpr (MF16) {
+        read_frags16(aslot(Cur{}), bstage(Cur{}), S % 2, f16);
       } else {
         read_frags(aslot(Cur{}), bstage(Cur{}), S % 2, 0, fr0);
         read_frags(aslot(Cur{}), bstage(Cur{}), S % 2, 1, fr1);
@@ -800,6 +953,8 @@ void fused_gemm_epilogue(Params p) {
       __builtin_amdgcn_s_setprio(1);
       if constexpr (F8IN) {
         mfma8(fa8[0], Q0c{}, QNc{});
+      } else if constexpr (MF16) {
+        mfmas16(f16);
       } else {
         mfmas(fr0);
         mfmas(fr1);
@@ -819,41 +974,6 @@ void fused_gemm_epilogue(Params p) {
     }
     if (grp == 0) __builtin_amdgcn_s_barrier();               // matches group 1's last phase
     if constexpr (ROWSTAT) row_ss[grp * T::BM + (wave & 3) * 64 + lane] = ss1;
-  } else if constexpr (GE_SERIAL_PIPELINE) {
-    // ---- reference build: one two-step slot at a time, nothing overlapped ----
-    // Load the slot's A and B (B [K][N]: both steps' stages), wait for every load, barrier;
-    // read and multiply steps k and k+1 with the pipelined build's fragments, MFMAs and order;
-    // wait for the reads, barrier, so no stage is refilled while a wave still reads it.
-    for (int k = kt; k < nk; k += 2) {
-      GE_SET_RS(k * BKE, k * BKE);
-      issue_a(k * BKE, aslot(S0{}));
-      issue_b(bstage(S0{}), k * BKE);
-      if constexpr (!BNK) {
-        GE_SET_RS(k * BKE, (k + 1) * BKE);
-        issue_b(bstage(S1{}), (k + 1) * BKE);
-      }
-      __builtin_amdgcn_s_waitcnt(kVmcnt0);
-      __builtin_amdgcn_s_barrier();
-      if constexpr (F8IN) {
-        read_a8(aslot(S0{}), 0, fa8[0]);
-        read_b8(bstage(S0{}), 0, Q0c{}, QNc{});
-        mfma8(fa8[0], Q0c{}, QNc{});
-        read_a8(aslot(S0{}), 1, fa8[0]);
-        read_b8(bstage(S0{}), 1, Q0c{}, QNc{});
-        mfma8(fa8[0], Q0c{}, QNc{});
-      } else {
-        read_frags(aslot(S0{}), bstage(S0{}), 0, 0, f0);
-        read_frags(aslot(S0{}), bstage(S0{}), 0, 1, f1);
-        mfmas(f0);
-        mfmas(f1);
-        read_frags(aslot(S1{}), bstage(S1{}), 1, 0, f0);
-        read_frags(aslot(S1{}), bstage(S1{}), 1, 1, f1);
-        mfmas(f0);
-        mfmas(f1);
-      }
-      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
-      __builtin_amdgcn_s_barrier();
-    }
   } else {
     GE_SET_RS(kt * BKE, kt * BKE);
     issue_a(kt * BKE, aslot(S0{}));
@@ -1047,6 +1167,47 @@ void fused_gemm_epilogue(Params p) {
     }
   };
 
+  // per-row scale of slot row ml: alpha, the RMS factor, the caller's row scale
+  auto row_factor = [&](int ml) {
+    float rscale = alpha;
+    if constexpr (ROWSTAT) {
+      float ssq = row_ss[ml];
+      if constexpr (PP) ssq += row_ss[T::BM + ml];
+      if (has_rms) rscale *= __builtin_amdgcn_rsqf(ssq * inv_k + p.eps);
+    }
+    if (has_rs) rscale *= (m0 + ml < M) ? p.row_scale[(int64_t)b * M + m0 + ml] : 0.0f;
+    return rscale;
+  };
+  if constexpr (MF16) {
+#pragma unroll
+    for (int j = 0; j < T::FM; ++j) {
+      prefetch(j);
+      // phase 1: 16x16 blocks 2j, 2j+1 of each column block; lane's rows 16 par + lane % 16,
+      // columns 16i + 4 (lane / 16) + e of the wave's 32-row block
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        const int r = 16 * par + (int)l16;
+        const float rscale = row_factor(wm0 + 32 * j + r);
+#pragma unroll
+        for (int i = 0; i < FN16; ++i) {
+          f32x4_t t;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (T::PAIR) {
+              t[e] = activate<ACT>(c16[i][2 * j + par][e] * rscale) * (c16b[i][2 * j + par][e] * rscale);
+            } else {
+              t[e] = c16[i][2 * j + par][e] * rscale;
+            }
+          }
+          *(f32x4_t*)(ep + r * EP_LD + 16 * i + 4 * (int)q16) = t;
+        }
+      }
+      if (has_res)
+        phase2(j, std::integral_constant<bool, true>{}, rvb[0]);
+      else
+        phase2(j, std::integral_constant<bool, false>{}, rvb[0]);
+    }
+  } else {
 #pragma unroll
   for (int j = 0; j < T::FM; ++j) {
     prefetch(j);
@@ -1079,6 +1240,7 @@ void fused_gemm_epilogue(Params p) {
       phase2(j, std::integral_constant<bool, true>{}, rvb[0]);
     else
       phase2(j, std::integral_constant<bool, false>{}, rvb[0]);
+  }
   }
 
   // ---- cross-workgroup reductions: memory ordering ----

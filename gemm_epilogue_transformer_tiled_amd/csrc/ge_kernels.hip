@@ -19,9 +19,6 @@ __global__ void amax_zero_kernel(uint32_t* amax) {
 }  // namespace
 
 hipError_t launch_fused(TileKind kind, int act, bool fp8_out, const Params& p, hipStream_t stream) {
-#if GE_SERIAL_PIPELINE
-  if (two_wave_tile(kind)) return hipErrorInvalidValue;     // not part of the reference build
-#else
   if (two_wave_tile(kind)) {
     if (p.flags & F_IN_FP8)
       return kind == TILE_256x256_2W ? launch_tile_256x256w8_f8(act, fp8_out, p, stream)
@@ -32,7 +29,6 @@ hipError_t launch_fused(TileKind kind, int act, bool fp8_out, const Params& p, h
     return kind == TILE_256x256_2W ? launch_tile_256x256w8_kn(act, fp8_out, p, stream)
                                    : launch_tile_256x128w8_pair_kn(act, fp8_out, p, stream);
   }
-#endif
   if (p.flags & F_IN_FP8) {
     switch (kind) {
       case TILE_256x256: return launch_tile_256x256_f8(act, fp8_out, p, stream);

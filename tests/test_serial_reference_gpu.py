@@ -3,13 +3,11 @@
 The reference build (``libgemm_epilogue_serial.so``: the same kernel sources compiled with
 ``GE_SERIAL_PIPELINE=1``) loads each two-step operand slot, waits for every load and reads
 the slot between two full barriers, so no LDS stage is read before its loads land or refilled
-while a wave still reads it.  Its MFMAs take the same fragments in the same order as the
-pipelined instances -- one-wave and two-wave alike, every 32x32 output block accumulates K in
-16-deep groups, in increasing order, with the same lane layout -- and the epilogue is the same
-code, so outputs, AMAX and column sums must agree bit for bit; a difference is a
-synchronisation mistake in the pipelined mainloop.  The RMS row statistic and the column sums
-are summed in an order that depends on the instance's wave layout, so those chains are
-compared on the same instance only (the oracle tests cover them on every instance).
+while a wave still reads it.  Every comparison runs the same instance (tile shape, waves,
+matrix-core instruction) in both builds: its MFMAs take the same fragments in the same order,
+the RMS row statistic and the column sums are summed in the same order, and the epilogue is
+the same code, so outputs, AMAX and column sums must agree bit for bit; a difference is a
+synchronisation mistake in the pipelined mainloop.
 
 Every comparison also checks both results against the oracle where the problem is small, so
 the reference build is itself pinned; at full size the comparison covers every output of the
@@ -83,7 +81,7 @@ def _assert_same_bits(a, b, what):
                                 f"bytes, first at byte {diff[:4].tolist()}")
 
 
-def run_both(w, inp, serial_lib, tile=None, ref_tile=None, rows_check=True):
+def run_both(w, inp, serial_lib, tile=None, ref_tile=None):
     """Runs `w` on instance `tile` of the fused library (None: create's choice) and on
     `ref_tile` of the reference build (None: the same instance), compares every output bit
     for bit, and returns the fused library's problem (holding its outputs again)."""
@@ -165,17 +163,21 @@ def test_one_wave_fp8_operands_match_reference(tile, shape, serial_lib):
     run_both(w, inp, serial_lib, tile=tile)
 
 
-# The two-wave instances against the one-wave reference of the same tile shape: the chains
-# without a row statistic or column sums; K a multiple of 64 (128 for fp8 operands).
+# The two-wave instances against their reference-build twins (same tile, waves and MFMA form);
+# K a multiple of 64 (128 for fp8 operands).
 TWO_WAVE_CASES = {
     "c2-kn": (workloads.WORKLOADS["c2"], "kn", dict(batch=2, M=600, N=776, K=576)),
-    "c5-nk": (dataclasses.replace(workloads.WORKLOADS["c5"], b_layout="nk"), "nk", dict(batch=1, M=520, N=1032, K=1088)),
-    "f2-y-nk": (dataclasses.replace(workloads.WORKLOADS["f2"], chain=(("act_grad", "gelu_tanh"), ("amax",))), "nk",
-                dict(batch=1, M=776, N=520, K=640)),
+    "c4-kn": (workloads.WORKLOADS["c4"], "kn", dict(batch=1, M=520, N=1032, K=640)),
+    "c4-nk": (workloads.WORKLOADS["c4"], "nk", dict(batch=2, M=264, N=392, K=1024)),
+    "c5-nk": (workloads.WORKLOADS["c5"], "nk", dict(batch=1, M=520, N=1032, K=1088)),
+    "f2-nk": (workloads.WORKLOADS["f2"], "nk", dict(batch=1, M=776, N=520, K=640)),
+    "f2-kn": (workloads.WORKLOADS["f2"], "kn", dict(batch=2, M=300, N=392, K=512)),
     "relu-res-kn": (dataclasses.replace(workloads.WORKLOADS["c2"], chain=(("scale",), ("act", "relu"), ("residual",))),
                     "kn", dict(batch=1, M=520, N=520, K=1024)),
     "c3-kn": (workloads.WORKLOADS["c3"], "kn", dict(batch=1, M=600, N=520, K=576)),
     "c3-nk": (workloads.WORKLOADS["c3"], "nk", dict(batch=2, M=264, N=392, K=1024)),
+    "f1-kn": (workloads.WORKLOADS["f1"], "kn", dict(batch=1, M=600, N=776, K=512)),
+    "f1-nk": (workloads.WORKLOADS["f1"], "nk", dict(batch=1, M=264, N=520, K=640)),
     "f3": (F3, "nk", dict(batch=1, M=520, N=776, K=1152)),
     "f3-pair": (dataclasses.replace(F3, out="bf16", chain=(("scale",), ("pairwise", "silu"))), "nk",
                 dict(batch=1, M=600, N=392, K=640)),
@@ -183,36 +185,35 @@ TWO_WAVE_CASES = {
 
 
 @pytest.mark.parametrize("case", list(TWO_WAVE_CASES))
-def test_two_wave_matches_one_wave_reference(case, serial_lib):
+def test_two_wave_matches_reference(case, serial_lib):
     w0, layout, shape = TWO_WAVE_CASES[case]
     w = dataclasses.replace(w0, b_layout=layout).with_shape(**shape)
-    assert not (w.has("row_rms") or w.has("col_sum"))
-    pair = w.pairwise
-    tile = ge.GE_TILE_256x128_PAIR_2W if pair else ge.GE_TILE_256x256_2W
-    ref_tile = ge.GE_TILE_256x128_PAIR if pair else ge.GE_TILE_256x256
+    tile = ge.GE_TILE_256x128_PAIR_2W if w.pairwise else ge.GE_TILE_256x256_2W
     inp = workloads.generate(w)
-    prob = run_both(w, inp, serial_lib, tile=tile, ref_tile=ref_tile)
+    prob = run_both(w, inp, serial_lib, tile=tile)
     assert "threads=512" in prob.plan.describe()
     if w.in_dtype == "bf16":
         check_oracle(w, inp, prob, f"two-wave {case}")
 
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c5", "f3"])
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5", "f1", "f2", "f3"])
 def test_full_workload_matches_reference(name, serial_lib):
     """The benchmark's launch (create's choice of instance) on the full workload, every output
-    against the reference build's one-wave instance of the same tile shape."""
+    against the reference build's twin of that instance."""
     w = workloads.WORKLOADS[name]
     inp = workloads.generate(w)
-    pair = w.pairwise
-    prob = run_both(w, inp, serial_lib, tile=None,
-                    ref_tile=ge.GE_TILE_256x128_PAIR if pair else ge.GE_TILE_256x256)
+    prob = runner.prepare(w, inp)
+    tile = {"256x256": ge.GE_TILE_256x256_2W, "256x128": ge.GE_TILE_256x128_PAIR_2W}[
+        "x".join(prob.plan.describe().split("tile=")[1].split("x")[:2])]
+    prob.plan.close()
+    prob = run_both(w, inp, serial_lib, tile=tile)
     assert "threads=512" in prob.plan.describe()
 
 
 @pytest.mark.parametrize("name", ["c4", "f1", "f2"])
 def test_full_workload_one_wave_matches_reference(name, serial_lib):
-    """The chains with a row statistic or column sums at full size, on the one-wave instance of
-    the benchmark's tile shape (the two-wave instance sums them in another order)."""
+    """The chains with a row statistic or column sums at full size on the one-wave instance of
+    the benchmark's tile shape."""
     w = workloads.WORKLOADS[name]
     inp = workloads.generate(w)
     tile = ge.GE_TILE_256x128_PAIR if w.pairwise else ge.GE_TILE_256x256
