@@ -264,18 +264,21 @@ ge_status_t gemm_epilogue_create(const ge_desc_t* desc, ge_handle_t* out) {
   const ge::TileInfo ti = ge::tile_info(p->tile);
   p->tiles_m = ceil_div(desc->M, ti.bm);
   p->tiles_n = ceil_div(desc->N, ti.bn);
+  // two-wave RMS plans with several tile columns: a tile that starts after another tile of its
+  // tile row has published the row statistic reads it instead of recomputing it
+  if ((p->flags & ge::F_ROW_RMS) && ge::two_wave_tile(p->tile) && p->tiles_n > 1) p->flags |= ge::F_RS_SHARE;
   *out = p;
   return GE_OK;
 }
 
 namespace {
-size_t workspace_bytes(const ge_plan* h) {
+ge::WsLayout layout_of(const ge_plan* h) {
   const int64_t wgs = h->tiles_m * h->tiles_n * h->desc.batch;
-  const bool amax = (h->flags & ge::F_AMAX) != 0;
-  if (h->flags & ge::F_COL_SUM)
-    return 4 * (ge::colsum_part_word(amax, wgs, h->tiles_n) + (size_t)(h->desc.batch * h->tiles_m * h->desc.N));
-  return amax ? ge::amax_workspace_bytes(wgs) : 0;
+  return ge::ws_layout((h->flags & ge::F_AMAX) != 0, (h->flags & ge::F_COL_SUM) != 0,
+                       (h->flags & ge::F_RS_SHARE) != 0, wgs, h->tiles_n, h->desc.batch * h->tiles_m, h->desc.N,
+                       ge::tile_info(h->tile).bm);
 }
+size_t workspace_bytes(const ge_plan* h) { return 4 * layout_of(h).total; }
 }  // namespace
 
 ge_status_t gemm_epilogue_workspace_size(ge_handle_t h, size_t* bytes) {
@@ -351,11 +354,11 @@ ge_status_t enqueue(const ge_plan* h, const ge_args_t* a, hipStream_t s) {
   p.Z = static_cast<const uint16_t*>(a->aux);
   p.col_sum = a->col_sum;
   {
-    const int64_t wgs = h->tiles_m * h->tiles_n * d.batch;
-    const bool amax = (f & ge::F_AMAX) != 0;
-    p.cs_ctr = (f & ge::F_COL_SUM) ? p.ws + ge::colsum_ctr_word(amax, wgs) : nullptr;
-    p.cs_part = (f & ge::F_COL_SUM) ? reinterpret_cast<float*>(p.ws + ge::colsum_part_word(amax, wgs, h->tiles_n))
-                                    : nullptr;
+    const ge::WsLayout l = layout_of(h);
+    p.cs_ctr = (f & ge::F_COL_SUM) ? p.ws + l.cs_ctr : nullptr;
+    p.cs_part = (f & ge::F_COL_SUM) ? reinterpret_cast<float*>(p.ws + l.cs_part) : nullptr;
+    p.rs_ctr = (f & ge::F_RS_SHARE) ? p.ws + l.rs_ctr : nullptr;
+    p.rs_val = (f & ge::F_RS_SHARE) ? reinterpret_cast<float*>(p.ws + l.rs_val) : nullptr;
   }
   p.ldz = d.ldz;
   p.sz = d.stride_z;
@@ -411,9 +414,7 @@ ge_status_t gemm_epilogue_run_noalloc(ge_handle_t h, const ge_args_t* a, void* s
   if (uses_scratch) {
     // the array keeps the previous call's contents, possibly another plan's partials where this
     // plan keeps its counters: zero the counters (a kernel, not a memset node)
-    const int64_t wgs = h->tiles_m * h->tiles_n * d.batch;
-    const size_t words = ge::counter_words((h->flags & ge::F_AMAX) != 0, (h->flags & ge::F_COL_SUM) != 0, wgs,
-                                           h->tiles_n);
+    const size_t words = layout_of(h).counters;
     if (ge::launch_zero_words(static_cast<uint32_t*>(b.workspace), (int64_t)words, s) != hipSuccess)
       return GE_ERR_HIP;
   }

@@ -27,6 +27,7 @@ enum : uint32_t {
   F_ACT_GRAD = 1u << 7,  // y = t * act'(Z) instead of act(t)
   F_COL_SUM = 1u << 8,   // column sums of y over rows and batches
   F_IN_FP8 = 1u << 9,    // A and B hold fp8-e4m3 codes (B given [N][K])
+  F_RS_SHARE = 1u << 10, // two-wave F_ROW_RMS: tiles of one tile row share the row statistic
 };
 
 enum Act : int { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_TANH = 2, ACT_SILU = 3 };
@@ -60,6 +61,9 @@ struct Params {
   float* col_sum;          // COL_SUM output [N]
   uint32_t* cs_ctr;        // COL_SUM ticket counters, one per column tile (stride kColSumCtrStride)
   float* cs_part;          // COL_SUM partials [batch * tiles_m][N]
+  uint32_t* rs_ctr;        // F_RS_SHARE: per tile row, a published flag and a ticket counter
+                           // (stride kRowStatCtrStride words)
+  float* rs_val;           // F_RS_SHARE: per tile row, the published sums of squares [BM]
   int64_t ldz, sz;
   int64_t lda, ldb, ldy, ldr;
   int64_t sa, sb, sy, sr;  // batch strides in elements
@@ -117,20 +121,32 @@ constexpr uint32_t kAmaxCounterStride = 64;
 constexpr uint32_t kAmaxSlot0 = 1024;
 constexpr uint32_t kAmaxFlatGrid = 64;
 constexpr uint32_t kColSumCtrStride = 16;   // 64 bytes between column-tile counters
-// Workspace words: [AMAX region][COL_SUM counters][COL_SUM partials], each 256-byte aligned.
+constexpr uint32_t kRowStatCtrStride = 16;  // 64 bytes between tile-row flag/counter pairs
 inline size_t round64(size_t w) { return (w + 63) / 64 * 64; }
-inline size_t colsum_ctr_word(bool amax, int64_t workgroups) {
-  return amax ? round64((size_t)kAmaxSlot0 + (size_t)workgroups) : 0;
-}
-inline size_t colsum_part_word(bool amax, int64_t workgroups, int64_t tiles_n) {
-  return round64(colsum_ctr_word(amax, workgroups) + (size_t)tiles_n * kColSumCtrStride);
-}   // up to this many workgroups take one ticket each on the top counter
-inline size_t amax_workspace_bytes(int64_t workgroups) { return 4 * ((size_t)kAmaxSlot0 + (size_t)workgroups); }
-// Leading words of the workspace that hold ticket counters (everything before the COL_SUM
-// partials, or the AMAX counters alone): what must be zero when a kernel starts.
-inline size_t counter_words(bool amax, bool colsum, int64_t workgroups, int64_t tiles_n) {
-  if (colsum) return colsum_part_word(amax, workgroups, tiles_n);
-  return amax ? (size_t)kAmaxSlot0 : 0;
+// Workspace words: [AMAX region][COL_SUM counters][row-statistic flags and counters]
+// [COL_SUM partials][row-statistic sums], each region 256-byte aligned and present only when
+// the plan uses it.  Everything before the COL_SUM partials is a counter that is zero between
+// runs.
+struct WsLayout {
+  size_t cs_ctr, rs_ctr, cs_part, rs_val;   // word offsets
+  size_t counters;                          // words that hold counters (from word 0)
+  size_t total;                             // words in all
+};
+inline WsLayout ws_layout(bool amax, bool colsum, bool rs_share, int64_t workgroups, int64_t tiles_n,
+                          int64_t rows, int64_t n, int64_t bm) {
+  WsLayout l;
+  l.cs_ctr = amax ? round64((size_t)kAmaxSlot0 + (size_t)workgroups) : 0;
+  l.rs_ctr = colsum ? round64(l.cs_ctr + (size_t)tiles_n * kColSumCtrStride) : l.cs_ctr;
+  l.cs_part = rs_share ? round64(l.rs_ctr + (size_t)rows * kRowStatCtrStride) : l.rs_ctr;
+  l.counters = (colsum || rs_share) ? l.cs_part : (amax ? (size_t)kAmaxSlot0 : 0);
+  l.rs_val = colsum ? round64(l.cs_part + (size_t)rows * (size_t)n) : l.cs_part;
+  if (rs_share)
+    l.total = l.rs_val + (size_t)rows * (size_t)bm;
+  else if (colsum)
+    l.total = l.cs_part + (size_t)rows * (size_t)n;
+  else
+    l.total = amax ? (size_t)kAmaxSlot0 + (size_t)workgroups : 0;
+  return l;
 }
 
 // Device address of the static scratch array behind gemm_epilogue_run_noalloc on the current

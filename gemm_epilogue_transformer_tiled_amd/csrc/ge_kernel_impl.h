@@ -248,6 +248,7 @@ void fused_gemm_epilogue(Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char bstage3[B_BUF23];
   __shared__ float row_ss[ROWSTAT ? (PP ? 2 : 1) * T::BM : 1];   // two-wave: one half per wave group
   __shared__ uint32_t wave_amax[T::WAVES];
+  __shared__ uint32_t rs_have;                    // row statistic already published for this tile row
   __shared__ __attribute__((aligned(256))) unsigned char pf_sink[T::WAVES * 256];   // L2 prefetch target
   static_assert(T::NS == 4, "four B stage arrays");
   // B buffer of step s ([K][N]: its stage; [N][K]: its slot), A slot of step s (two
@@ -771,6 +772,13 @@ void fused_gemm_epilogue(Params p) {
       if constexpr (T::PAIR) b2rs = GE_B_RS(b2_base, BNK ? (ka) : (kb));       \
     }                                                                          \
   } while (0)
+  // Row statistic shared along a tile row (two-wave RMS plans, F_RS_SHARE): a tile that finds
+  // the row's flag set when it starts reads the published sums after its mainloop instead of
+  // squaring its A slots; one that does not computes them (the same values: the same slots in
+  // the same order), publishes them and sets the flag.  No tile waits for another.
+  const bool rs_share = ROWSTAT && PP && !GE_SERIAL_PIPELINE && (p.flags & F_RS_SHARE) != 0;
+  const uint32_t rs_row = (uint32_t)(b * p.tiles_m + tm);
+  bool stat_on = true;
   if constexpr (GE_SERIAL_PIPELINE) {
     // ---- reference build: one two-step slot at a time, nothing overlapped ----
     // Load the slot's A and B (B [K][N]: both steps' stages), wait for every load, barrier;
@@ -873,6 +881,10 @@ void fused_gemm_epilogue(Params p) {
     float ss1 = 0.0f;
     const uint32_t sq_row = (uint32_t)((wave & 3) * 64 + lane) * T::A_ROWB;
     const uint32_t sq_c = ((uint32_t)((lane & 15) + ((lane & 15) >> 3)) & 7u) ^ (uint32_t)(4 * grp);
+    // the tile row's flag: loaded before the prologue's loads, so it lands with them
+    uint32_t have = 0;
+    if (rs_share && tid == 0)
+      have = __hip_atomic_load(p.rs_ctr + rs_row * kRowStatCtrStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     set_rs_pp(kt * BKE, kt * BKE);
     issue_a(kt * BKE, aslot(S0{}));
     issue_b(bstage(S0{}), kt * BKE);
@@ -882,12 +894,18 @@ void fused_gemm_epilogue(Params p) {
       set_rs_pp(kt * BKE, (kt + 2) * BKE);
       issue_b(bstage(S2{}), (kt + 2) * BKE);
     }
+    if (rs_share && tid == 0) {
+      rs_have = have;
+      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(63));       // the LDS store, before the barrier
+    }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(BNK ? 0 : 2 * T::B_LOADS));   // A slot and B of step kt landed
     __builtin_amdgcn_s_barrier();
+    if (rs_share) stat_on = __builtin_amdgcn_readfirstlane(rs_have) == 0u;
     if (grp == 1) __builtin_amdgcn_s_barrier();               // one phase behind group 0
-    auto mem_phase = [&](auto s_c, int j) {
+    auto mem_phase = [&](auto s_c, int j, auto stat_c) {
       constexpr int S = decltype(s_c)::value;
       constexpr bool EVEN = S % 2 == 0;
+      constexpr bool SQ = ROWSTAT && !EVEN && decltype(stat_c)::value;   // this step squares its slot
       using Cur = std::integral_constant<int, S>;
       using FillA = std::integral_constant<int, S + 2>;
       using FillB = std::integral_constant<int, S + 3>;
@@ -920,7 +938,7 @@ void fused_gemm_epilogue(Params p) {
         read_frags(aslot(Cur{}), bstage(Cur{}), S % 2, 1, fr1);
       }
       bf16x8_t sq[4];
-      if constexpr (ROWSTAT && !EVEN) {
+      if constexpr (SQ) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) sq[i] = *(const bf16x8_t*)(aslot(Cur{}) + sq_row + ((sq_c ^ (uint32_t)i) << 4));
       }
@@ -934,7 +952,7 @@ void fused_gemm_epilogue(Params p) {
       constexpr int YOUNGER = BNK ? (EVEN ? T::A_LOADS + BL : 0)
                                   : (EVEN ? 2 * T::B_LOADS + T::A_LOADS : T::B_LOADS);
       __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(YOUNGER));
-      if constexpr (ROWSTAT && !EVEN) {
+      if constexpr (SQ) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const bf16x8_t v = sq[i];
@@ -962,15 +980,26 @@ void fused_gemm_epilogue(Params p) {
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_s_barrier();
     };
-    for (; kt < nk; kt += T::NS) {
-      mem_phase(S0{}, kt);
-      mat_phase();
-      mem_phase(S1{}, kt + 1);
-      mat_phase();
-      mem_phase(S2{}, kt + 2);
-      mat_phase();
-      mem_phase(S3{}, kt + 3);
-      mat_phase();
+    // the loop with and without the row statistic's squares, each with its own registers
+    auto run_loop = [&](auto stat_c) {
+      for (; kt < nk; kt += T::NS) {
+        mem_phase(S0{}, kt, stat_c);
+        mat_phase();
+        mem_phase(S1{}, kt + 1, stat_c);
+        mat_phase();
+        mem_phase(S2{}, kt + 2, stat_c);
+        mat_phase();
+        mem_phase(S3{}, kt + 3, stat_c);
+        mat_phase();
+      }
+    };
+    if constexpr (ROWSTAT) {
+      if (stat_on)
+        run_loop(std::true_type{});
+      else
+        run_loop(std::false_type{});
+    } else {
+      run_loop(std::false_type{});
     }
     if (grp == 0) __builtin_amdgcn_s_barrier();               // matches group 1's last phase
     if constexpr (ROWSTAT) row_ss[grp * T::BM + (wave & 3) * 64 + lane] = ss1;
@@ -1023,6 +1052,38 @@ void fused_gemm_epilogue(Params p) {
       }
     }
     __syncthreads();
+    if (rs_share) {                                      // uniform
+      // publish: every sum performed at device scope before the flag (each thread waits for
+      // its store, then the barrier); read: the flag was seen set when the tile started, so
+      // the sums were performed before it.  The reader keeps the epilogue's sum of the two
+      // halves exact by storing the published sum and a zero.
+      uint32_t* ctr = p.rs_ctr + rs_row * kRowStatCtrStride;
+      uint32_t* val = reinterpret_cast<uint32_t*>(p.rs_val) + rs_row * (uint32_t)T::BM;
+      if (stat_on) {
+        if (tid < T::BM) {
+          const float s = row_ss[tid] + row_ss[T::BM + tid];
+          __hip_atomic_store(val + tid, __float_as_uint(s), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        }
+        __syncthreads();
+        if (tid == 0) {
+          __hip_atomic_store(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __builtin_amdgcn_s_waitcnt(kVmcnt0);           // flag performed before the ticket
+        }
+      } else {
+        if (tid < T::BM) {
+          row_ss[tid] = __uint_as_float(__hip_atomic_load(val + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+          row_ss[T::BM + tid] = 0.0f;
+        }
+        __syncthreads();
+      }
+      // the tile row's ticket: the last of its tiles_n tiles clears the flag and the counter
+      if (tid == 0 &&
+          __hip_atomic_fetch_add(ctr + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)p.tiles_n - 1u) {
+        __hip_atomic_store(ctr + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
 
   // ---- epilogue, two phases per 32-row block of the wave's tile ----

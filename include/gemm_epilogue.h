@@ -197,7 +197,7 @@ typedef struct {
   const void* residual;    /* RESIDUAL */
   void* Y;
   float* amax;             /* AMAX: overwritten with max|y| */
-  void* workspace;         /* AMAX, COL_SUM: device scratch of gemm_epilogue_workspace_size bytes,
+  void* workspace;         /* AMAX, COL_SUM, shared ROW_RMS: device scratch of gemm_epilogue_workspace_size bytes,
                               16-byte aligned, ZERO-FILLED before its first use; each run leaves
                               it zeroed again when it completes.  Runs that share a workspace
                               must not overlap (order them on one stream). */
@@ -235,15 +235,18 @@ ge_status_t gemm_epilogue_create(const ge_desc_t* desc, ge_handle_t* out);
 /* Device scratch the plan needs from the caller, in bytes -- the plan-specific workspace of
  * the cuDNN tutorial (set-up paragraph: a helper allocates the workspace; engine-autotuning
  * paragraph: each candidate plan is built, given a workspace of the size it reports, and
- * timed); 0 without AMAX and COL_SUM.
+ * timed); 0 without AMAX, COL_SUM and a shared row statistic.
  * AMAX: nine ticket counters on their own cache lines plus one partial-maximum slot per
  * workgroup.  COL_SUM: one ticket counter per column tile plus one fp32 partial column sum
- * per row tile, batch and column.
+ * per row tile, batch and column.  ROW_RMS on the two-wave instances with more than one
+ * tile column: per row tile and batch, a published flag and a ticket counter plus the tile's
+ * fp32 sums of squares, so that tiles of a tile row that start after one of them has
+ * published the statistic read it instead of recomputing it (no tile waits for another).
  * The workspace must be zero-filled before its first use, and every run that completes leaves
  * its counters at zero again.  HAZARD: a workspace whose counters are not zero -- never
  * cleared, or shared by two runs that overlap in time (two streams, or a run that did not
- * complete) -- makes AMAX and COL_SUM silently wrong: a counter holding d > 0 elects a "last"
- * workgroup d arrivals early.  Clear it again (e.g. hipMemset) after any such event, and give
+ * complete) -- makes AMAX, COL_SUM and ROW_RMS silently wrong: a counter holding d > 0 elects
+ * a "last" workgroup d arrivals early, and a flag left set makes tiles read stale sums.  Clear it again (e.g. hipMemset) after any such event, and give
  * concurrent runs separate workspaces.  Returns GE_ERR_INVALID_ARG for a NULL handle or bytes. */
 ge_status_t gemm_epilogue_workspace_size(ge_handle_t handle, size_t* bytes);
 
@@ -272,20 +275,20 @@ ge_status_t gemm_epilogue_run(ge_handle_t handle, const ge_args_t* args, void* s
 /* For callers that cannot allocate device memory -- code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc: gemm_epilogue_run without a caller-given
  * workspace.  Same plan, same kernels, same results as gemm_epilogue_run; args->workspace and
- * args->workspace_bytes are ignored.  The AMAX / COL_SUM scratch comes from a static device
+ * args->workspace_bytes are ignored.  The AMAX / COL_SUM / row-statistic scratch comes from a static device
  * array of GE_NOALLOC_SCRATCH_BYTES (4 MiB) that the library's code object holds on every GPU
  * it runs on until the process ends; its device address is looked up once per device
  * (hipGetSymbolAddress, on the first call made with that device current).  Each call first
  * enqueues a small kernel that zeroes the ticket counters the plan uses (the array keeps the
  * previous call's contents), then the fused kernel: two launches on `stream`, no hipMalloc,
- * hipFree, memset node or other allocating call.  Chains without AMAX and COL_SUM use no
- * scratch and enqueue the fused kernel alone.
+ * hipFree, memset node or other allocating call.  Plans without AMAX, COL_SUM and a shared
+ * row statistic use no scratch and enqueue the fused kernel alone.
  * Returns GE_ERR_SCRATCH, enqueueing nothing, when gemm_epilogue_workspace_size exceeds
  * GE_NOALLOC_SCRATCH_BYTES (e.g. COL_SUM over more than about a million row-tile x column
  * partials); otherwise the statuses of gemm_epilogue_run, plus GE_ERR_HIP when the scratch
  * address cannot be looked up.
  * RACE: every call on one GPU shares that GPU's array, so calls that overlap in time on one
- * GPU (two streams, two host threads) corrupt each other's AMAX and COL_SUM; order them. */
+ * GPU (two streams, two host threads) corrupt each other's AMAX, COL_SUM and ROW_RMS; order them. */
 ge_status_t gemm_epilogue_run_noalloc(ge_handle_t handle, const ge_args_t* args, void* stream);
 
 /* Frees the plan's host memory (the end of a plan's life in the cuDNN tutorial's plan-reuse

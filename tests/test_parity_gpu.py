@@ -83,23 +83,34 @@ def plan_tile(prob):
     return int(bm), int(bn)
 
 
+def shares_row_statistic(w, prob):
+    """Two-wave RMS plans with several tile columns share the row statistic along a tile row."""
+    bm, bn = plan_tile(prob)
+    return w.has("row_rms") and "threads=512" in prob.plan.describe() and -(-w.N // bn) > 1
+
+
 def workspace_words(w, prob):
     """Word offsets of the plan's workspace, from the tile the plan actually chose: AMAX --
     nine ticket counters in words [0, 1024) and one slot per workgroup from word 1024; COL_SUM
-    -- one ticket counter per column tile (16 words apart) from `cs_ctr`, then the partials."""
+    -- one ticket counter per column tile (16 words apart) from `cs_ctr`; a shared row
+    statistic -- a flag and a counter per tile row (16 words apart) from `rs_ctr`; then the
+    COL_SUM partials."""
     bm, bn = plan_tile(prob)
     tiles_m, tiles_n = -(-w.M // bm), -(-w.N // bn)
     wgs = tiles_m * tiles_n * w.batch
     round64 = lambda x: (x + 63) // 64 * 64
     cs_ctr = round64(1024 + wgs) if w.has("amax") else 0
-    return {"wgs": wgs, "tiles_m": tiles_m, "tiles_n": tiles_n, "cs_ctr": cs_ctr,
-            "cs_part": round64(cs_ctr + tiles_n * 16)}
+    rs_ctr = round64(cs_ctr + tiles_n * 16) if w.has("col_sum") else cs_ctr
+    rows = w.batch * tiles_m
+    cs_part = round64(rs_ctr + rows * 16) if shares_row_statistic(w, prob) else rs_ctr
+    return {"wgs": wgs, "tiles_m": tiles_m, "tiles_n": tiles_n, "cs_ctr": cs_ctr, "rs_ctr": rs_ctr,
+            "rows": rows, "cs_part": cs_part}
 
 
 def assert_counters_zero(w, prob, what=""):
-    """Every ticket counter the plan uses is back at zero (partials and slots may stay)."""
-    if not (w.has("amax") or w.has("col_sum")):
-        assert prob.plan.workspace is None, f"{what}: a workspace without AMAX or COL_SUM"
+    """Every ticket counter and flag the plan uses is back at zero (partials and slots may stay)."""
+    if not (w.has("amax") or w.has("col_sum") or shares_row_statistic(w, prob)):
+        assert prob.plan.workspace is None, f"{what}: a workspace without AMAX, COL_SUM or a shared statistic"
         return
     ws = prob.plan.workspace.view(torch.int32)
     lay = workspace_words(w, prob)
@@ -109,6 +120,10 @@ def assert_counters_zero(w, prob, what=""):
         ctr = ws[lay["cs_ctr"]: lay["cs_ctr"] + lay["tiles_n"] * 16]
         assert ctr.numel() == lay["tiles_n"] * 16
         assert int(ctr.count_nonzero()) == 0, f"{what}: column-tile counters"
+    if shares_row_statistic(w, prob):
+        ctr = ws[lay["rs_ctr"]: lay["rs_ctr"] + lay["rows"] * 16]
+        assert ctr.numel() == lay["rows"] * 16
+        assert int(ctr.count_nonzero()) == 0, f"{what}: tile-row flags and counters"
 
 
 @pytest.mark.parametrize("tile", SINGLE_TILES, ids=[TILE_NAMES[t] for t in SINGLE_TILES])
@@ -322,6 +337,7 @@ def test_full_workload(name):
     prob = gpu_run(w, inp)
     print(f"\n{name}: {prob.plan.describe()}", flush=True)
     compare(w, inp, prob, f"{name} full")
+    assert_counters_zero(w, prob, f"{name} full")
 
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c5"])
@@ -397,7 +413,7 @@ def test_repeated_runs_are_identical_and_amax_is_overwritten():
     assert prob.amax_host() == a1
 
 
-@pytest.mark.parametrize("name", ["c2", "c5", "f2"])
+@pytest.mark.parametrize("name", ["c2", "c4", "c5", "f2"])
 def test_graph_replays_match_eager_runs(name):
     """The benchmark replays the launches from a HIP graph: every replay, with eager work and
     synchronisation between replays, gives the eager output, AMAX and column sums, and leaves
@@ -634,7 +650,9 @@ def test_two_wave_chains(chain):
     inp = workloads.generate(w)
     if w.has("row_scale"):
         inp = {**inp, "row_scale": np.random.default_rng(5).uniform(0.5, 1.5, (w.batch, w.M)).astype(np.float32)}
-    compare(w, inp, run_two_wave(w, inp), f"two-wave {chain}")
+    prob = run_two_wave(w, inp)
+    compare(w, inp, prob, f"two-wave {chain}")
+    assert_counters_zero(w, prob, f"two-wave {chain}")
 
 
 @pytest.mark.parametrize("layout", ["kn", "nk"])
@@ -704,6 +722,7 @@ def test_two_wave_full_workload(name):
     prob = run_two_wave(w, inp)
     rows = None if name == "c2" else np.r_[0:40, 1000:1040, w.M - 300:w.M]
     compare(w, inp, prob, f"{name} two-wave full", rows=rows)
+    assert_counters_zero(w, prob, f"{name} two-wave full")
     if rows is not None and w.has("amax"):
         check_amax(prob.amax_host(), oracle.run_workload(w, inp).amax, f"{name} two-wave full amax")
 

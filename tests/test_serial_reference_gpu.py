@@ -169,6 +169,10 @@ TWO_WAVE_CASES = {
     "c2-kn": (workloads.WORKLOADS["c2"], "kn", dict(batch=2, M=600, N=776, K=576)),
     "c4-kn": (workloads.WORKLOADS["c4"], "kn", dict(batch=1, M=520, N=1032, K=640)),
     "c4-nk": (workloads.WORKLOADS["c4"], "nk", dict(batch=2, M=264, N=392, K=1024)),
+    # more tiles than the GPU holds at once: later tiles of a tile row read the statistic that
+    # earlier ones published instead of recomputing it
+    "c4-rounds": (workloads.WORKLOADS["c4"], "kn", dict(batch=1, M=8192, N=8192, K=128)),
+    "f1-rounds": (workloads.WORKLOADS["f1"], "nk", dict(batch=2, M=4096, N=11008, K=128)),
     "c5-nk": (workloads.WORKLOADS["c5"], "nk", dict(batch=1, M=520, N=1032, K=1088)),
     "f2-nk": (workloads.WORKLOADS["f2"], "nk", dict(batch=1, M=776, N=520, K=640)),
     "f2-kn": (workloads.WORKLOADS["f2"], "kn", dict(batch=2, M=300, N=392, K=512)),
@@ -192,7 +196,7 @@ def test_two_wave_matches_reference(case, serial_lib):
     inp = workloads.generate(w)
     prob = run_both(w, inp, serial_lib, tile=tile)
     assert "threads=512" in prob.plan.describe()
-    if w.in_dtype == "bf16":
+    if w.in_dtype == "bf16" and w.M * w.N * w.batch <= 2 ** 22:
         check_oracle(w, inp, prob, f"two-wave {case}")
 
 

@@ -99,6 +99,10 @@ CASES = [
      .with_shape(batch=1, M=64, N=72, K=64)),
     ("fp8 out", workloads.WORKLOADS["c5"].with_shape(M=1024, N=2048, K=512),
      workloads.WORKLOADS["c5"].with_shape(M=300, N=264, K=200)),
+    # two-wave RMS plans share the row statistic along a tile row through the scratch array
+    ("rms shared", workloads.WORKLOADS["c4"].with_shape(M=8192, N=2048, K=256),
+     dataclasses.replace(workloads.WORKLOADS["c4"], chain=(("row_rms", 1e-6), ("residual",), ("amax",)))
+     .with_shape(M=4096, N=4096, K=128)),
 ]
 
 
