@@ -64,9 +64,9 @@ ABNORMAL_RC = {-6, -9, -11, -15, 124, 134, 137, 139}
 # kernel at each workload; the factors scale the counters to the bytes of a plain 1 GiB device
 # copy.  Valid only for the device code they were taken on (sha256 prefix of the library's
 # .hip_fatbin section, below): any change to any kernel instance changes it.
-MEASURED_TRAFFIC_CODE = "e9030dfe5724ca4c"
-MEASURED_TRAFFIC = {"c1": 1066177, "c2": 101057324, "c3": 2411624718, "c4": 537324651, "c5": 1714162360,
-                    "f1": 2401342994, "f2": 1713062030, "f3": 877511191}
+MEASURED_TRAFFIC_CODE = "3043a12469fcc574"
+MEASURED_TRAFFIC = {"c1": 1066177, "c2": 101056388, "c3": 2411661605, "c4": 537772793, "c5": 1709636878,
+                    "f1": 2392073093, "f2": 1714601333, "f3": 877333773}
 
 
 def kernel_code_hash(lib_path=None):
