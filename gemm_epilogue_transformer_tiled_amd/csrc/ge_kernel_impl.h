@@ -851,8 +851,8 @@ void fused_gemm_epilogue(Params p) {
     //     later, and every wave passes the barrier in between).
     //   matrix phase of step j: the step's MFMAs only, at raised wave priority, so the
     //     partner wave's memory work fills the issue slots the MFMAs leave.
+    static_assert(MF16 || F8IN, "two-wave instances: 16x16x32 bf16 or fp8 operands");
     const int grp = wave >> 2;
-    Frags fr0, fr1;
     Frags16 f16;
     // Step resources: K is a multiple of two steps here, so a step is wholly inside or outside
     // [0, K), and an outside step needs only an empty extent (its base is never used): one
@@ -931,11 +931,8 @@ void fused_gemm_epilogue(Params p) {
         // fp8 operands: one 64-deep step, one register set (the matrix phase uses it whole)
         read_a8(aslot(Cur{}), S % 2, fa8[0]);
         read_b8(bstage(Cur{}), S % 2, Q0c{}, QNc{});
-      } else if constexpr (MF16) {
-        read_frags16(aslot(Cur{}), bstage(Cur{}), S % 2, f16);
       } else {
-        read_frags(aslot(Cur{}), bstage(Cur{}), S % 2, 0, fr0);
-        read_frags(aslot(Cur{}), bstage(Cur{}), S % 2, 1, fr1);
+        read_frags16(aslot(Cur{}), bstage(Cur{}), S % 2, f16);
       }
       bf16x8_t sq[4];
       if constexpr (SQ) {
@@ -971,11 +968,8 @@ void fused_gemm_epilogue(Params p) {
       __builtin_amdgcn_s_setprio(1);
       if constexpr (F8IN) {
         mfma8(fa8[0], Q0c{}, QNc{});
-      } else if constexpr (MF16) {
-        mfmas16(f16);
       } else {
-        mfmas(fr0);
-        mfmas(fr1);
+        mfmas16(f16);
       }
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_s_barrier();
