@@ -173,6 +173,9 @@ TWO_WAVE_CASES = {
     # earlier ones published instead of recomputing it
     "c4-rounds": (workloads.WORKLOADS["c4"], "kn", dict(batch=1, M=8192, N=8192, K=128)),
     "f1-rounds": (workloads.WORKLOADS["f1"], "nk", dict(batch=2, M=4096, N=11008, K=128)),
+    "rms-chain-rounds": (dataclasses.replace(workloads.WORKLOADS["c4"], chain=(
+        ("scale",), ("row_rms", 1e-6), ("bias",), ("act", "gelu_tanh"), ("residual",), ("col_sum",), ("amax",))),
+        "kn", dict(batch=2, M=4096, N=4104, K=64)),
     "c5-nk": (workloads.WORKLOADS["c5"], "nk", dict(batch=1, M=520, N=1032, K=1088)),
     "f2-nk": (workloads.WORKLOADS["f2"], "nk", dict(batch=1, M=776, N=520, K=640)),
     "f2-kn": (workloads.WORKLOADS["f2"], "kn", dict(batch=2, M=300, N=392, K=512)),
