@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libge_baselines.so")
 EXPORTED = ("ge_unfused_scale", "ge_unfused_bias_col", "ge_unfused_act", "ge_unfused_act_mul",
             "ge_unfused_row_rms", "ge_unfused_row_scale", "ge_unfused_add", "ge_unfused_amax",
             "ge_unfused_quant_fp8", "ge_unfused_act_grad", "ge_unfused_col_sum", "ge_probe_mfma",
-            "ge_probe_mfma_variant", "ge_probe_mfma_f8", "ge_probe_copy")
+            "ge_probe_mfma_variant", "ge_probe_mfma_f8", "ge_probe_lds_load", "ge_probe_copy")
 ACTS = {"none": 0, "relu": 1, "gelu_tanh": 2, "silu": 3}
 
 _p, _i64, _i, _f = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
@@ -43,6 +43,7 @@ _SIGS = {
     "ge_probe_mfma": [_p, _i, _i, _p],
     "ge_probe_mfma_variant": [_p, _i, _i, _i, _p],
     "ge_probe_mfma_f8": [_p, _p, _p, _p, _i, _p],
+    "ge_probe_lds_load": [_p, _i, _p, _i, _i, _p],
     "ge_probe_copy": [_p, _p, _i64, _p],
 }
 
@@ -230,6 +231,26 @@ def probe_mfma(workgroups: int = 1024, iters: int = 4096, form: str = "bf16_32x3
     per_cu_cycle = 8192 if form.startswith("fp8") else 4096
     return {"form": form, "tflops": round(flops / best / 1e9, 1), "ms": round(best, 4),
             "implied_clock_ghz": round(flops / (best * 1e-3) / (256 * per_cu_cycle) / 1e9, 3)}
+
+
+def probe_lds_load(src_kb: int = 2048, workgroups: int = 512, iters: int = 2048) -> Dict:
+    """Sustained rate of direct global->LDS loads from an L2-resident buffer (the fused
+    kernels' operand path with nothing else running), GB/s over all CUs."""
+    src = torch.zeros(src_kb * 1024, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(workgroups * 256, dtype=torch.float32, device="cuda")
+    call("ge_probe_lds_load", src.data_ptr(), src_kb, sink.data_ptr(), workgroups, 16, _stream())   # warm
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for _ in range(3):
+        e0.record()
+        call("ge_probe_lds_load", src.data_ptr(), src_kb, sink.data_ptr(), workgroups, iters, _stream())
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    nbytes = workgroups * iters * 32768.0
+    return {"gbs": round(nbytes / best / 1e6, 1), "ms": round(best, 4), "src_kb": src_kb, "workgroups": workgroups}
 
 
 def mfma_f8(src0: np.ndarray, src1: np.ndarray, c: np.ndarray) -> np.ndarray:

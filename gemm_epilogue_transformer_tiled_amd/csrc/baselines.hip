@@ -326,6 +326,39 @@ __global__ __launch_bounds__(64) void mfma_f8_probe(const i32x8_t* __restrict__ 
   d[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(s0[i], s1[i], c[i], 0, 0, 0, 0, 0, 0);
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations are outstanding (gfx9
+// encoding: vmcnt[3:0] and [15:14]; expcnt and lgkmcnt at their maxima, i.e. not waited for).
+constexpr int probe_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// L2 -> LDS probe: the mainloops' operand path alone.  Each wave of a 256-thread workgroup
+// issues direct global->LDS buffer loads (16 bytes per lane, 1 KB per instruction) from a
+// buffer small enough to stay in L2 into the workgroup's 64 KB of LDS, eight per round with
+// up to sixteen in flight, and nothing else.  Source offsets stay inside the buffer (the
+// resource's extent); LDS destinations stay inside the array.
+__global__ __launch_bounds__(256) void lds_load_probe(const unsigned char* __restrict__ src, int src_kb,
+                                                      float* __restrict__ sink, int iters) {
+  __shared__ __attribute__((aligned(1024))) unsigned char buf[65536];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(src), (short)0, src_kb * 1024, 0x00020000);
+  uint32_t kb = (uint32_t)(blockIdx.x * 37 + wave * 8) % (uint32_t)src_kb;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t off = ((kb + (uint32_t)t) % (uint32_t)src_kb) * 1024u + (uint32_t)lane * 16u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(buf + (wave * 8 + t) * 2048 + (it & 1) * 1024), 16, off, 0,
+          0, 0);
+    }
+    kb = (kb + 32u) % (uint32_t)src_kb;
+    __builtin_amdgcn_s_waitcnt(probe_vmcnt(8));      // the previous round's eight have landed
+  }
+  __builtin_amdgcn_s_waitcnt(probe_vmcnt(0));
+  __syncthreads();
+  sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = (float)buf[threadIdx.x * 4];
+}
+
 __global__ __launch_bounds__(kThreads) void copy_kernel(const u32x4_t* __restrict__ src, u32x4_t* __restrict__ dst,
                                                         int64_t nv) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -447,6 +480,13 @@ int ge_probe_mfma_f8(const uint8_t* src0, const uint8_t* src1, const float* c, f
   if (waves == 0) return 0;
   hipLaunchKernelGGL(mfma_f8_probe, dim3((unsigned)waves), dim3(64), 0, (hipStream_t)stream, (const i32x8_t*)src0,
                      (const i32x8_t*)src1, (const f32x16_t*)c, (f32x16_t*)d);
+  return launched();
+}
+
+int ge_probe_lds_load(const void* src, int src_kb, float* sink, int workgroups, int iters, void* stream) {
+  if (!src || !sink || src_kb < 8 || src_kb > (1 << 20) || workgroups <= 0 || iters < 0) return 1;
+  hipLaunchKernelGGL(lds_load_probe, dim3((unsigned)workgroups), dim3(256), 0, (hipStream_t)stream,
+                     static_cast<const unsigned char*>(src), src_kb, sink, iters);
   return launched();
 }
 

@@ -96,6 +96,13 @@ int ge_probe_mfma_variant(float* sink, int workgroups, int iters, int variant, v
  * how the instruction sums its 64 products (the accuracy of fp8-operand GEMMs). */
 int ge_probe_mfma_f8(const uint8_t* src0, const uint8_t* src1, const float* c, float* d, int waves, void* stream);
 
+/* L2 -> LDS probe, the fused kernels' operand path alone: `workgroups` workgroups of 4 waves,
+ * each wave issuing `iters` rounds of eight direct global->LDS loads (16 bytes per lane, 1 KB
+ * per instruction; up to sixteen in flight) from the first `src_kb` KiB of `src` (8 to 2^20;
+ * small enough to stay in L2 for the rate of L2 hits) into the workgroup's 64 KiB of LDS;
+ * `sink` receives workgroups * 256 floats.  Bytes moved per launch: workgroups * iters * 32768. */
+int ge_probe_lds_load(const void* src, int src_kb, float* sink, int workgroups, int iters, void* stream);
+
 /* Streaming copy of `bytes` (a multiple of 16, 16-byte aligned pointers): reads and writes each
  * byte once. */
 int ge_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);

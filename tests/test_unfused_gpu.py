@@ -118,5 +118,7 @@ def test_probes_report_plausible_peaks():
     assert 100.0 < m16["tflops"] < 2600.0, m16
     m8 = bl.probe_mfma(workgroups=256, iters=256, form="fp8_32x32x64")
     assert 200.0 < m8["tflops"] < 5200.0, m8
+    ll = bl.probe_lds_load(src_kb=1024, workgroups=256, iters=64)
+    assert 500.0 < ll["gbs"] < 200000.0, ll
     c = bl.probe_copy(mib=64)
     assert 100.0 < c["gbs"] < 9000.0, c
