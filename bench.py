@@ -485,10 +485,13 @@ def run_one(args):
         mf8 = baselines.probe_mfma(form="fp8_32x32x64")
         cp = baselines.probe_copy()
         ll = baselines.probe_lds_load()
+        lr = baselines.probe_lds_read()
         result["measured_peaks"] = {"mfma_bf16_tflops": mf["tflops"], "mfma_implied_clock_ghz": mf["implied_clock_ghz"],
                                     "mfma_bf16_16x16x32_tflops": mf16["tflops"],
                                     "mfma_fp8_tflops": mf8["tflops"], "mfma_fp8_implied_clock_ghz": mf8["implied_clock_ghz"],
-                                    "copy_gbs": cp["gbs"], "l2_to_lds_gbs": ll["gbs"]}
+                                    "copy_gbs": cp["gbs"], "l2_to_lds_gbs": ll["gbs"],
+                                    "lds_read_gbs": lr["gbs"], "lds_read_bytes_per_clk_cu": lr["bytes_per_clk_cu"],
+                                    "lds_read_implied_clock_ghz": lr["implied_clock_ghz"]}
         # against the probe of the instruction the mainloop runs
         result["roofline"]["frac_of_measured_mfma_peak"] = round(achieved / (mf8 if fp8_in else mf)["tflops"], 4)
         result["roofline"]["frac_of_measured_copy_gbs"] = round(gbs / cp["gbs"], 4)

@@ -24,7 +24,8 @@ LIB_PATH = os.path.join(_HERE, "libge_baselines.so")
 EXPORTED = ("ge_unfused_scale", "ge_unfused_bias_col", "ge_unfused_act", "ge_unfused_act_mul",
             "ge_unfused_row_rms", "ge_unfused_row_scale", "ge_unfused_add", "ge_unfused_amax",
             "ge_unfused_quant_fp8", "ge_unfused_act_grad", "ge_unfused_col_sum", "ge_probe_mfma",
-            "ge_probe_mfma_variant", "ge_probe_mfma_f8", "ge_probe_lds_load", "ge_probe_copy")
+            "ge_probe_mfma_variant", "ge_probe_mfma_f8", "ge_probe_lds_load", "ge_probe_lds_read",
+            "ge_probe_copy")
 ACTS = {"none": 0, "relu": 1, "gelu_tanh": 2, "silu": 3}
 
 _p, _i64, _i, _f = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
@@ -44,6 +45,7 @@ _SIGS = {
     "ge_probe_mfma_variant": [_p, _i, _i, _i, _p],
     "ge_probe_mfma_f8": [_p, _p, _p, _p, _i, _p],
     "ge_probe_lds_load": [_p, _i, _p, _i, _i, _p],
+    "ge_probe_lds_read": [_p, _p, _i, _i, _p],
     "ge_probe_copy": [_p, _p, _i64, _p],
 }
 
@@ -251,6 +253,36 @@ def probe_lds_load(src_kb: int = 2048, workgroups: int = 512, iters: int = 2048)
         best = ms if best is None else min(best, ms)
     nbytes = workgroups * iters * 32768.0
     return {"gbs": round(nbytes / best / 1e6, 1), "ms": round(best, 4), "src_kb": src_kb, "workgroups": workgroups}
+
+
+def probe_lds_read(workgroups: int = 256, iters: int = 16384) -> Dict:
+    """Sustained LDS read rate (the fused kernels' fragment reads with nothing else running):
+    one 8-wave workgroup per CU reading 16 bytes per lane without bank conflicts.  Returns the
+    aggregate GB/s (host events), the shader clock implied by the workgroups' s_memtime cycles
+    over the kernel's time, and bytes per clock per CU (bytes of one workgroup over its median
+    s_memtime cycles)."""
+    sink = torch.empty(workgroups * 512, dtype=torch.int32, device="cuda")
+    clocks = torch.zeros(2 * workgroups, dtype=torch.int64, device="cuda")
+    call("ge_probe_lds_read", sink.data_ptr(), clocks.data_ptr(), workgroups, 64, _stream())   # warm
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for _ in range(3):
+        e0.record()
+        call("ge_probe_lds_read", sink.data_ptr(), clocks.data_ptr(), workgroups, iters, _stream())
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        if best is None or ms < best[0]:
+            best = (ms, clocks.cpu().numpy().reshape(workgroups, 2).copy())
+    ms, ck = best
+    wg_bytes = iters * 65536.0
+    cycles = float(np.median(ck[:, 0]))
+    ticks = float(np.median(ck[:, 1]))
+    return {"gbs": round(workgroups * wg_bytes / ms / 1e6, 1), "ms": round(ms, 4), "workgroups": workgroups,
+            "bytes_per_clk_cu": round(wg_bytes / cycles, 1) if cycles > 0 else None,
+            "implied_clock_ghz": round(cycles / (ms * 1e6), 3),
+            "memtime_per_realtime_tick": round(cycles / ticks, 2) if ticks > 0 else None}
 
 
 def mfma_f8(src0: np.ndarray, src1: np.ndarray, c: np.ndarray) -> np.ndarray:

@@ -359,6 +359,46 @@ __global__ __launch_bounds__(256) void lds_load_probe(const unsigned char* __res
   sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = (float)buf[threadIdx.x * 4];
 }
 
+// LDS read probe: the mainloops' fragment reads alone.  A 512-thread workgroup (two waves per
+// SIMD, as in the two-wave instances) holds 96 KB of LDS, so one runs per CU.  Each wave reads
+// its own 12 KB with ds_read_b128 (16 bytes per lane, lanes on consecutive 16-byte chunks, so
+// no bank conflicts), eight reads of 1 KB per round at a base that moves with the round, and
+// folds the words into two registers with byte dot products (two VALU operations per read,
+// half of what the SIMDs issue at 256 bytes per clock per CU).  Wave 0 records the shader-clock counter (s_memtime) and the
+// constant-rate counter (s_memrealtime) around the loop, barriers on both sides.
+__global__ __launch_bounds__(512) void lds_read_probe(uint32_t* __restrict__ sink, uint64_t* __restrict__ clocks,
+                                                      int iters) {
+  __shared__ __attribute__((aligned(1024))) uint32_t buf[24576];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  for (int i = tid; i < 24576; i += 512) buf[i] = probe_hash((uint32_t)i + blockIdx.x * 24576u);
+  __syncthreads();
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  uint32_t a0 = 0, a1 = 0;
+  // byte offsets: wave * 12288 + lane * 16 + (it % 4) * 1024 + r * 1024 <= wave * 12288 + 12272
+  const unsigned char* wbase = (const unsigned char*)buf + wave * 12288 + lane * 16;
+  for (int it = 0; it < iters; ++it) {
+    asm volatile("" ::: "memory");    // every round reads LDS anew (no reuse across rounds)
+    const unsigned char* q = wbase + (it & 3) * 1024;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const u32x4_t v = *(const u32x4_t*)(q + r * 1024);
+      a0 = __builtin_amdgcn_udot4(v[0], v[1], a0, false);
+      a1 = __builtin_amdgcn_udot4(v[2], v[3], a1, false);
+    }
+  }
+  __syncthreads();
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+  sink[(int64_t)blockIdx.x * 512 + tid] = a0 ^ a1;
+  if (tid == 0) {
+    clocks[2 * (int64_t)blockIdx.x] = t1 - t0;
+    clocks[2 * (int64_t)blockIdx.x + 1] = r1 - r0;
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void copy_kernel(const u32x4_t* __restrict__ src, u32x4_t* __restrict__ dst,
                                                         int64_t nv) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -487,6 +527,13 @@ int ge_probe_lds_load(const void* src, int src_kb, float* sink, int workgroups, 
   if (!src || !sink || src_kb < 8 || src_kb > (1 << 20) || workgroups <= 0 || iters < 0) return 1;
   hipLaunchKernelGGL(lds_load_probe, dim3((unsigned)workgroups), dim3(256), 0, (hipStream_t)stream,
                      static_cast<const unsigned char*>(src), src_kb, sink, iters);
+  return launched();
+}
+
+int ge_probe_lds_read(uint32_t* sink, uint64_t* clocks, int workgroups, int iters, void* stream) {
+  if (!sink || !clocks || workgroups <= 0 || iters < 0) return 1;
+  hipLaunchKernelGGL(lds_read_probe, dim3((unsigned)workgroups), dim3(512), 0, (hipStream_t)stream, sink, clocks,
+                     iters);
   return launched();
 }
 

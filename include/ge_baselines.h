@@ -103,6 +103,14 @@ int ge_probe_mfma_f8(const uint8_t* src0, const uint8_t* src1, const float* c, f
  * `sink` receives workgroups * 256 floats.  Bytes moved per launch: workgroups * iters * 32768. */
 int ge_probe_lds_load(const void* src, int src_kb, float* sink, int workgroups, int iters, void* stream);
 
+/* LDS read probe, the fused kernels' fragment reads alone: `workgroups` workgroups of 8 waves
+ * (two per SIMD) holding 96 KiB of LDS each, so one per CU; each wave reads its own 12 KiB with
+ * 16-byte-per-lane reads free of bank conflicts, `iters` rounds of eight 1 KiB reads.  `sink`
+ * receives workgroups * 512 words (the folded data); `clocks` receives per workgroup two words:
+ * the shader-clock cycles (s_memtime) and the constant-rate counter ticks (s_memrealtime) of
+ * wave 0 around the loop.  Bytes read per workgroup: iters * 65536. */
+int ge_probe_lds_read(uint32_t* sink, uint64_t* clocks, int workgroups, int iters, void* stream);
+
 /* Streaming copy of `bytes` (a multiple of 16, 16-byte aligned pointers): reads and writes each
  * byte once. */
 int ge_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);

@@ -72,7 +72,7 @@ def test_device_code_hash_reads_the_fatbin_section():
 def test_baselines_library_exports_every_declared_symbol():
     from gemm_epilogue_transformer_tiled_amd import baselines
     names = _declared_symbols(r"ge_(?:unfused|probe)_\w+")
-    assert len(names) == 16
+    assert len(names) == 17
     lib = ctypes.CDLL(baselines.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -92,6 +92,8 @@ def test_baselines_reject_invalid_arguments_without_launching():
     assert lib.ge_probe_mfma_variant(None, 1, 1, 0, None) == 1
     sink = ctypes.c_float()
     assert lib.ge_probe_mfma_variant(ctypes.byref(sink), 1, 1, 3, None) == 1   # unknown form
+    assert lib.ge_probe_lds_read(None, None, 1, 1, None) == 1
+    assert lib.ge_probe_lds_read(ctypes.byref(sink), ctypes.byref(sink), 0, 1, None) == 1   # no workgroups
     assert lib.ge_unfused_scale(None, None, 0, 1.0, None) == 0      # empty: nothing to do
 
 

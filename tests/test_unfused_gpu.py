@@ -120,5 +120,9 @@ def test_probes_report_plausible_peaks():
     assert 200.0 < m8["tflops"] < 5200.0, m8
     ll = bl.probe_lds_load(src_kb=1024, workgroups=256, iters=64)
     assert 500.0 < ll["gbs"] < 200000.0, ll
+    lr = bl.probe_lds_read(workgroups=256, iters=1024)
+    assert 1000.0 < lr["gbs"] < 1000000.0, lr
+    assert 0.5 < lr["implied_clock_ghz"] < 3.5, lr            # s_memtime counts shader clocks
+    assert 16.0 < lr["bytes_per_clk_cu"] <= 1024.0, lr
     c = bl.probe_copy(mib=64)
     assert 100.0 < c["gbs"] < 9000.0, c
