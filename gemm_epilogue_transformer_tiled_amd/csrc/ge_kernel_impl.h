@@ -40,7 +40,8 @@
 //     stages and slots, but the waves form two groups of four that alternate a memory phase
 //     (this step's fragment reads, later steps' loads, waits) and a matrix phase (MFMAs only,
 //     at raised priority), one phase apart, so one wave per SIMD keeps the matrix core busy
-//     while the other waits on memory; the row statistic comes from the staged A slots.
+//     while the other waits on memory; the row statistic comes from the staged A slots, and
+//     a tile that starts after another tile of its tile row has published it reads it instead.
 //     With bf16 operands they multiply with v_mfma_f32_16x16x32_bf16 (one instruction per
 //     16x16 block and 32-deep step: half the accumulator traffic per flop of 32x32x16).
 #include <type_traits>
