@@ -784,8 +784,9 @@ void fused_gemm_epilogue(Params p) {
     // ---- reference build: one two-step slot at a time, nothing overlapped ----
     // Load the slot's A and B (B [K][N]: both steps' stages), wait for every load, barrier;
     // read and multiply steps k and k+1 with the pipelined build's fragments, MFMAs and order
-    // (and, on the two-wave tiles, square the slot's rows for the row statistic as their odd
-    // steps do); wait for the reads, barrier, so no stage is refilled while a wave still reads it.
+    // (and, on the two-wave tiles, square the slot's rows for the row statistic once per slot,
+    // as their even steps do); wait for the reads, barrier, so no stage is refilled while a
+    // wave still reads it.
     [[maybe_unused]] const int grp = wave >> 2;
     [[maybe_unused]] float ss1 = 0.0f;
     [[maybe_unused]] const uint32_t sq_row = (uint32_t)((wave & 3) * 64 + lane) * T::A_ROWB;
@@ -844,12 +845,14 @@ void fused_gemm_epilogue(Params p) {
     // Both groups run this sequence with one barrier between phases; group 1 starts one phase
     // behind group 0, so in every phase one wave of each SIMD issues MFMAs while the other
     // issues loads and fragment reads.  Group 0 reads step j in phase 2j, group 1 in 2j+1.
-    //   memory phase of step j: start the direct loads of B step j+3 (its stage held step j-1,
-    //     read by both groups before the previous barrier) and, for even j, of the A slot of
-    //     steps j+2 and j+3 (it held steps j-2 and j-1) -- with B given [N][K], B is staged in
-    //     two-step slots like A and loaded with it; read every fragment of step j; wait for
-    //     them and for this wave's loads of step j+1 (group 0 reads that step two phases
-    //     later, and every wave passes the barrier in between).
+    //   memory phase of step j: start the direct loads of later steps -- for even j the A
+    //     slot of steps j+2 and j+3 (it held steps j-2 and j-1), for odd j the B stages of
+    //     steps j+2 and j+3 (they held steps j-2 and j-1, read by both groups before the
+    //     previous barrier), so every memory phase moves 32 KB per workgroup; with B given
+    //     [N][K], B is staged in two-step slots like A and loaded with it on even steps --
+    //     read every fragment of step j; wait for them and for this wave's loads of step j+1
+    //     (group 0 reads that step two phases later, and every wave passes the barrier in
+    //     between).
     //   matrix phase of step j: the step's MFMAs only, at raised wave priority, so the
     //     partner wave's memory work fills the issue slots the MFMAs leave.
     static_assert(MF16 || F8IN, "two-wave instances: 16x16x32 bf16 or fp8 operands");
@@ -870,8 +873,8 @@ void fused_gemm_epilogue(Params p) {
       brs = rs_pp(b_base, b_ext32, kbb, bpk);
       if constexpr (T::PAIR) b2rs = rs_pp(b2_base, b_ext32, kbb, bpk);
     };
-    // Row statistic: in the memory phase of each odd step j every lane squares half of one
-    // row of the A slot of steps j-1 and j (its last use): slot row (wave % 4) * 64 + lane,
+    // Row statistic: in the memory phase of each even step j every lane squares half of one
+    // row of the A slot of steps j and j+1 (its first use): slot row (wave % 4) * 64 + lane,
     // physical chunks sq_c ^ i (i < 4), where sq_c's bit 2 is the wave group, so the two
     // groups cover the row's eight chunks between them (the sum does not depend on which
     // K a chunk holds).  sq_c = (l + l / 8) % 8, l = lane % 16, gives the 8 (16) lanes one
@@ -906,10 +909,11 @@ void fused_gemm_epilogue(Params p) {
     auto mem_phase = [&](auto s_c, int j, auto stat_c) {
       constexpr int S = decltype(s_c)::value;
       constexpr bool EVEN = S % 2 == 0;
-      constexpr bool SQ = ROWSTAT && !EVEN && decltype(stat_c)::value;   // this step squares its slot
+      constexpr bool SQ = ROWSTAT && EVEN && decltype(stat_c)::value;    // this step squares its slot
       using Cur = std::integral_constant<int, S>;
       using FillA = std::integral_constant<int, S + 2>;
       using FillB = std::integral_constant<int, S + 3>;
+      using FillB2 = std::integral_constant<int, S + 2>;
       // The loads of later steps fill other stages, so they may go before or after this step's
       // fragment reads.  Reads first (the phase waits for them; the loads' issue then overlaps
       // their LDS latency) measured +1 to +4.5 % on B [K][N] and fp8 operands, -1 % on bf16
@@ -921,9 +925,16 @@ void fused_gemm_epilogue(Params p) {
             issue_a((j + 2) * BKE, aslot(FillA{}));
             issue_b(bstage(FillA{}), (j + 2) * BKE);
           }
+        } else if constexpr (EVEN) {
+          issue_a((j + 2) * BKE, aslot(FillA{}));
         } else {
+          // B [K][N]: two one-step stages on odd steps, so that each memory phase carries the
+          // same 32 KB (the A slot alone on even steps); with one B stage per step and the A
+          // slot on top, the even phases held 48 KB and outlasted the matrix phases
+          set_rs_pp((j + 2) * BKE, (j + 2) * BKE);
+          issue_b(bstage(FillB2{}), (j + 2) * BKE);
+          set_rs_pp((j + 2) * BKE, (j + 3) * BKE);
           issue_b(bstage(FillB{}), (j + 3) * BKE);
-          if constexpr (EVEN) issue_a((j + 2) * BKE, aslot(FillA{}));
         }
       };
       constexpr bool READS_FIRST = !BNK || F8IN;
@@ -944,11 +955,12 @@ void fused_gemm_epilogue(Params p) {
         __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the loads
         issue_loads();
       }
-      // loads younger than those of step j+1: even j -- B of steps j+2, j+3 and the A slot
-      // of j+2, j+3; odd j -- B of step j+3 (the A slot of j+1 came with B of step j+2).
-      // [N][K]: even j -- the A and B slots of j+2, j+3; odd j -- none.
+      // loads younger than those of step j+1: even j -- B of step j+2 (issued with B of
+      // step j+1 on step j-1) and the A slot of j+2, j+3; odd j -- B of steps j+2, j+3 (the
+      // A slot of j+1 came on step j-1, after B of step j+1).  [N][K]: even j -- the A and B
+      // slots of j+2, j+3; odd j -- none.
       constexpr int YOUNGER = BNK ? (EVEN ? T::A_LOADS + BL : 0)
-                                  : (EVEN ? 2 * T::B_LOADS + T::A_LOADS : T::B_LOADS);
+                                  : (EVEN ? T::B_LOADS + T::A_LOADS : 2 * T::B_LOADS);
       __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(YOUNGER));
       if constexpr (SQ) {
 #pragma unroll
