@@ -66,9 +66,9 @@ ABNORMAL_RC = {-6, -9, -11, -15, 124, 134, 137, 139}
 # kernel at each workload; the factors scale the counters to the bytes of a plain 1 GiB device
 # copy.  Valid only for the device code they were taken on (sha256 prefix of the library's
 # .hip_fatbin section, below): any change to any kernel instance changes it.
-MEASURED_TRAFFIC_CODE = "3043a12469fcc574"
-MEASURED_TRAFFIC = {"c1": 1066177, "c2": 101056388, "c3": 2411661605, "c4": 537772793, "c5": 1709636878,
-                    "f1": 2392073093, "f2": 1714601333, "f3": 877333773}
+MEASURED_TRAFFIC_CODE = "04daa6e50266fff0"
+MEASURED_TRAFFIC = {"c1": 1066177, "c2": 101051631, "c3": 2402031871, "c4": 537792963, "c5": 1695033449,
+                    "f1": 2391858012, "f2": 1852936119, "f3": 877316544}
 
 
 def kernel_code_hash(lib_path=None):
