@@ -848,7 +848,7 @@ void fused_gemm_epilogue(Params p) {
     //   memory phase of step j: start the direct loads of later steps -- for even j the A
     //     slot of steps j+2 and j+3 (it held steps j-2 and j-1), for odd j the B stages of
     //     steps j+2 and j+3 (they held steps j-2 and j-1, read by both groups before the
-    //     previous barrier), so every memory phase moves 32 KB per workgroup; with B given
+    //     previous barrier), so every step moves 32 KB per workgroup; with B given
     //     [N][K], B is staged in two-step slots like A and loaded with it on even steps --
     //     read every fragment of step j; wait for them and for this wave's loads of step j+1
     //     (group 0 reads that step two phases later, and every wave passes the barrier in
@@ -928,9 +928,9 @@ void fused_gemm_epilogue(Params p) {
         } else if constexpr (EVEN) {
           issue_a((j + 2) * BKE, aslot(FillA{}));
         } else {
-          // B [K][N]: two one-step stages on odd steps, so that each memory phase carries the
-          // same 32 KB (the A slot alone on even steps); with one B stage per step and the A
-          // slot on top, the even phases held 48 KB and outlasted the matrix phases
+          // B [K][N]: two one-step stages on odd steps, so that every step moves the same
+          // 32 KB (the A slot alone on even steps); one B stage per step with the A slot on
+          // top of it on even steps (48 KB, then 16 KB) measured 3-5 % slower
           set_rs_pp((j + 2) * BKE, (j + 2) * BKE);
           issue_b(bstage(FillB2{}), (j + 2) * BKE);
           set_rs_pp((j + 2) * BKE, (j + 3) * BKE);
